@@ -1,0 +1,197 @@
+/*
+ * mmq.h -- C ABI of libmmq: q8-plane producers and q4_K / q6_K integer-dot
+ * matmuls for gfx950 (MI355X).
+ *
+ * The operations follow three pages of the "minfer" CUDA optimisation log:
+ *   [r52] "55 · r52 — skip-write mode 2: skipping the f32 intermediate write-out"
+ *   [r60] "64 · r60 — the coronation: flipping the verified gate set to default-on"
+ *   [d37] "72 · D3-7 — attn_v-q6K MMVQ routing (2b) + rms wide-block / positions memo (2c)"
+ *
+ * Vocabulary.
+ *   q8 plane   -- the block-32 quantisation of an f32 activation matrix
+ *                 [n][d]: for every 32 consecutive values of a row, one f32
+ *                 scale D = amax/127, 32 int8 codes q = clamp(rint(y/D),
+ *                 -127, 127) and one int32 sum S = sum(q) [r52 2.2, 3.2].
+ *                 Planes are owned by the context; rows are padded to a
+ *                 multiple of MMQ_PLANE_ROWS and padded rows are all zero
+ *                 [r52 3.2, the padded-tail zero-fill].
+ *   plane key  -- the f32 buffer a plane was quantised from (or, for a
+ *                 skip-write producer, the buffer it would have written);
+ *                 consumers look planes up by (pointer, n, d) [r52 3.1, d37 A2].
+ *   dead key   -- a skip-write producer's output buffer: it was never
+ *                 written, so quantising it again would read garbage; any
+ *                 request that would do so is refused [r52 3.1-3.2].
+ *
+ * Conventions for every call.
+ *   * Pointers named x, w, y, gate, up, a, out are DEVICE pointers on the
+ *     context's device (f32, row-major, contiguous, 16-byte aligned).
+ *     raw_host in mmq_register_weight is a HOST pointer.
+ *   * stream is a hipStream_t (NULL = the legacy default stream).  All device
+ *     work is enqueued on it in call order; calls never synchronise except
+ *     mmq_register_weight.  One context serves one stream: plane slots are
+ *     reused in enqueue order, so concurrent streams on one context race.
+ *   * Return value: MMQ_OK or a negative MMQ_E_* status.  Every argument,
+ *     shape, type and cache check runs before any launch, so a failing call
+ *     enqueues nothing; mmq_last_error() describes the failure.  The
+ *     library never aborts the process.
+ *   * Not thread-safe per context; distinct contexts may be used from
+ *     distinct threads.
+ */
+#ifndef MMQ_H
+#define MMQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------- */
+#define MMQ_OK            0
+#define MMQ_E_ARG        -1   /* null or misaligned pointer, bad flag       */
+#define MMQ_E_SHAPE      -2   /* d % 256 != 0, n < 1, shape mismatch        */
+#define MMQ_E_TYPE       -3   /* weight type does not fit the call          */
+#define MMQ_E_OOM        -4   /* device allocation failed or cap exceeded   */
+#define MMQ_E_DEAD_WRITE -5   /* request would quantise a dead key          */
+#define MMQ_E_HIP        -6   /* HIP runtime or launch error                */
+#define MMQ_E_DEVICE     -7   /* no usable gfx950 device / dry-run context  */
+
+/* ---- weight types (values follow the GGUF type ids) ------------------ */
+#define MMQ_Q4_K 12           /* 144-byte superblocks of 256 weights         */
+#define MMQ_Q6_K 14           /* 210-byte superblocks of 256 weights         */
+
+/* ---- context flags --------------------------------------------------- */
+#define MMQ_CTX_SYNC_CHECK 1u /* synchronise + check errors after each launch */
+#define MMQ_CTX_DRYRUN     2u /* host bookkeeping only: validation, cache and
+                                 statistics run, no device memory is touched
+                                 and nothing is launched (host-logic tests)  */
+
+/* ---- registration uses ------------------------------------------------ */
+#define MMQ_USE_GEMM 1u       /* prefill matmul (any n)                      */
+#define MMQ_USE_GEMV 2u       /* one-token GEMV (q6_K only)                  */
+
+#define MMQ_PLANE_ROWS 32     /* plane rows are padded to this multiple     */
+
+typedef struct mmq_ctx mmq_ctx;
+typedef struct mmq_weight mmq_weight;
+
+typedef struct mmq_stats_t {
+    int64_t launches_quant_rms;
+    int64_t launches_quant_swiglu;
+    int64_t launches_quant_f32;     /* standalone quantise, incl. cache misses */
+    int64_t launches_gemm_q4k;
+    int64_t launches_gemm_q6k;
+    int64_t launches_mmvq_q6k;
+    int64_t cache_hits;
+    int64_t cache_misses;
+    int64_t cache_refusals;         /* MMQ_E_DEAD_WRITE returns               */
+    int64_t cache_entries;          /* live table entries now                 */
+    int64_t plane_bytes;            /* device bytes held by plane slots       */
+    int64_t weight_bytes;           /* device bytes held by registered weights */
+} mmq_stats_t;
+
+/* ---- context ----------------------------------------------------------- */
+
+/* Create a context on HIP device `device` (must be gfx950; the device
+ * becomes current on the calling thread).  flags: MMQ_CTX_*.  With
+ * MMQ_CTX_DRYRUN no device is opened and `device` is ignored.
+ * Errors: MMQ_E_ARG (out == NULL, unknown flag), MMQ_E_DEVICE. */
+int mmq_create(int device, unsigned flags, mmq_ctx** out);
+
+/* Free every plane slot and the context.  Registered weights stay valid
+ * until mmq_weight_free.  NULL is ignored.  Synchronises the device. */
+void mmq_destroy(mmq_ctx* ctx);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* mmq_last_error(void);
+
+/* Cap on the total bytes of plane slots (default: no cap).  A producer or
+ * miss quantise that would grow past it returns MMQ_E_OOM. */
+int mmq_set_scratch_cap(mmq_ctx* ctx, int64_t bytes);
+
+/* Rows of a plane for n tokens: n rounded up to MMQ_PLANE_ROWS. */
+int64_t mmq_plane_rows(int64_t n);
+
+/* ---- registration [r60 3.1: weights are registered before the first
+ * forward; the engine keeps registration-time planes of every q4_K/q6_K
+ * weight] ---------------------------------------------------------------- */
+
+/* Copy `rows` x `cols` weights of type `type` (raw superblocks, row-major
+ * [rows][cols/256], 144 or 210 bytes each) from host memory and repack them
+ * into device tiles for the consumers named in `uses` (MMQ_USE_*; 0 means
+ * every consumer the type supports).  cols % 256 == 0.  raw_host may be
+ * freed on return.  Synchronises the device.
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE (unknown type, GEMV use on
+ * q4_K), MMQ_E_OOM, MMQ_E_HIP. */
+int mmq_register_weight(mmq_ctx* ctx, int type, int64_t rows, int64_t cols,
+                        const void* raw_host, unsigned uses, mmq_weight** out);
+
+/* Release a weight's device tiles (NULL ignored; synchronises the device). */
+void mmq_weight_free(mmq_weight* w);
+
+/* Device bytes held by a registered weight. */
+int64_t mmq_weight_bytes(const mmq_weight* w);
+
+/* ---- producers [r52 2.2, 3.2; d37 Excerpt C] ----------------------------
+ * Each quantises its f32 result in registers into a plane and records the
+ * plane under key y.  write_y != 0 also stores y [n][d] (the entry is live);
+ * write_y == 0 never touches y (the entry is dead: y is only the key).
+ * Preconditions: d % 256 == 0, n >= 1; x/gate/up/y 16-byte aligned.
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_OOM, MMQ_E_HIP. */
+
+/* RMSNorm: y[t][i] = (x[t][i] * s_t) * w[i], s_t = 1/sqrt(mean_i x[t][i]^2 + eps). */
+int mmq_quant_rms(mmq_ctx* ctx, const float* x, const float* w, float* y,
+                  int64_t n, int64_t d, float eps, int write_y, void* stream);
+
+/* SwiGLU: y = (g / (1 + exp(-g))) * u elementwise over [n][d]. */
+int mmq_quant_swiglu(mmq_ctx* ctx, const float* gate, const float* up, float* y,
+                     int64_t n, int64_t d, int write_y, void* stream);
+
+/* Standalone quantise of an existing f32 buffer x [n][d]; records key x
+ * (live).  Refuses with MMQ_E_DEAD_WRITE if x overlaps a dead key. */
+int mmq_quant_f32(mmq_ctx* ctx, const float* x, int64_t n, int64_t d, void* stream);
+
+/* ---- consumers [r60 3.2: int8 matmul over the plane, k32 chunks; q6_K
+ * with a rescale per 16-element half; d37 Excerpts A, A2] ------------------
+ * A consumer looks up the plane of `a` (key (a, n, cols)).  On a miss it
+ * quantises a standalone (as mmq_quant_f32) and records it, unless `a`
+ * overlaps a dead key, in which case it returns MMQ_E_DEAD_WRITE.
+ * out[t][o] = sum_k D[t][k/32] q[t][k] * w[o][k] for t < n, o < rows,
+ * row-major [n][rows] f32, caller-owned; w is the dequantised weight.
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE, MMQ_E_DEAD_WRITE, MMQ_E_OOM,
+ * MMQ_E_HIP. */
+int mmq_gemm_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,
+                 float* out, void* stream);
+int mmq_gemm_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,
+                 float* out, void* stream);
+
+/* One-token q6_K GEMV (n == 1): out[o] = sum_k D[k/32] q[k] * w[o][k]. */
+int mmvq_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
+             void* stream);
+
+/* ---- window boundary, hooks, statistics ---------------------------------- */
+
+/* Drop every cache entry and dead key: the end of an execution window
+ * [d37 Excerpt D, synchronize() clears the cache].  Plane slots are kept
+ * for reuse. */
+void mmq_cache_clear(mmq_ctx* ctx);
+
+/* Drop the entry and dead marks of `key` (for a buffer about to be reused
+ * with new contents inside a window).  MMQ_OK even if absent. */
+int mmq_cache_invalidate(mmq_ctx* ctx, const void* key);
+
+/* Copy the plane recorded under (key, n, d) into caller device buffers in
+ * the canonical row-major layout: q int8 [r][d], dq f32 [r][d/32],
+ * s int32 [r][d/32], with r = n, or mmq_plane_rows(n) if include_pad.
+ * Errors: MMQ_E_ARG (no such plane), MMQ_E_HIP, MMQ_E_DEVICE (dry run). */
+int mmq_plane_export(mmq_ctx* ctx, const void* key, int64_t n, int64_t d,
+                     int include_pad, int8_t* q, float* dq, int32_t* s,
+                     void* stream);
+
+/* Fill *st with counters since creation. */
+int mmq_stats(mmq_ctx* ctx, mmq_stats_t* st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMQ_H */

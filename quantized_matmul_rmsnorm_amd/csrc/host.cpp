@@ -1,0 +1,586 @@
+// host.cpp -- the C ABI of libmmq: context, plane cache, registration and
+// dispatch.  Declarations and the contract of every entry point: include/mmq.h.
+//
+// Plane cache ("55 · r52 ...", sections 3.1-3.2; "72 · D3-7 ...", Excerpts A2,
+// C and D).  Producers record the plane they wrote under the f32 buffer they
+// produced (or, with write_y = 0, the buffer they were promised but never
+// wrote); consumers look the plane up by (pointer, n, d) and on a miss
+// quantise the buffer themselves and record it.  A skip-write producer marks
+// its output range dead: any later request that would quantise bytes of a
+// dead range refuses loudly (status MMQ_E_DEAD_WRITE plus one stderr line)
+// instead of reading memory that was never written.  mmq_cache_clear is the
+// execution-window boundary: it drops every entry and every dead range.
+//
+// The table has kSlots entries, each owning one grow-only device plane slot;
+// when all are in use the least recently used entry is evicted and its slot
+// reused.  All launches go to the caller's stream in call order, so a slot is
+// only rewritten after every earlier kernel that read it (same stream).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mmq.h"
+#include "mmq_internal.h"
+
+using namespace mmq;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+constexpr int kSlots = 8;
+
+struct Entry {
+    bool used = false;
+    const void* key = nullptr;
+    int64_t n = 0, d = 0;
+    bool dead = false;
+    uint64_t last = 0;
+};
+
+struct Slot {
+    void* mem = nullptr;
+    int64_t cap = 0;
+};
+
+struct DeadRange {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+int64_t plane_bytes_for(int64_t n, int64_t d, int64_t* off_D, int64_t* off_S) {
+    const int64_t rows = round_up(n, kPlaneRows);
+    const int64_t nb = d / kBlock;
+    const int64_t oD = round_up(rows * d, 256);
+    const int64_t oS = oD + round_up(rows * nb * 4, 256);
+    if (off_D) *off_D = oD;
+    if (off_S) *off_S = oS;
+    return oS + round_up(rows * nb * 4, 256);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct mmq_ctx {
+    int device = -1;
+    unsigned flags = 0;
+    bool dry = false;
+    int64_t cap = -1;
+    Entry entries[kSlots];
+    Slot slots[kSlots];
+    std::vector<DeadRange> dead;
+    uint64_t tick = 0;
+    int64_t plane_bytes = 0;
+    int64_t weight_bytes = 0;
+    mmq_stats_t st{};
+};
+
+struct mmq_weight {
+    mmq_ctx* ctx = nullptr;
+    bool dry = false;
+    WeightDev w;
+};
+
+namespace {
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(MMQ_E_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+int after_launch(mmq_ctx* c, hipError_t e, hipStream_t s, const char* what) {
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (c->flags & MMQ_CTX_SYNC_CHECK) {
+        e = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, what);
+    }
+    return MMQ_OK;
+}
+
+int use_device(mmq_ctx* c) {
+    if (c->dry) return MMQ_OK;
+    hipError_t e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    return MMQ_OK;
+}
+
+bool overlaps_dead(const mmq_ctx* c, const void* p, int64_t bytes) {
+    const uintptr_t lo = (uintptr_t)p, hi = lo + (uintptr_t)bytes;
+    for (const DeadRange& r : c->dead)
+        if (lo < r.hi && r.lo < hi) return true;
+    return false;
+}
+
+int refuse_dead(mmq_ctx* c, const char* who, const void* p) {
+    c->st.cache_refusals++;
+    fprintf(stderr,
+            "libmmq: %s refused: buffer %p was promised unread by a skip-write producer "
+            "(write_y=0) and never written; quantising it would read garbage\n",
+            who, p);
+    return fail(MMQ_E_DEAD_WRITE, "%s: buffer %p overlaps a dead (never written) producer output",
+                who, p);
+}
+
+int find_entry(const mmq_ctx* c, const void* key, int64_t n, int64_t d) {
+    for (int i = 0; i < kSlots; ++i) {
+        const Entry& e = c->entries[i];
+        if (e.used && e.key == key && e.n == n && e.d == d) return i;
+    }
+    return -1;
+}
+
+// Drop entries whose key range overlaps [p, p + bytes): their planes describe
+// contents that a producer is about to replace.
+void drop_overlapping(mmq_ctx* c, const void* p, int64_t bytes) {
+    const uintptr_t lo = (uintptr_t)p, hi = lo + (uintptr_t)bytes;
+    for (Entry& e : c->entries) {
+        if (!e.used) continue;
+        const uintptr_t elo = (uintptr_t)e.key, ehi = elo + (uintptr_t)(e.n * e.d * 4);
+        if (lo < ehi && elo < hi) e.used = false;
+    }
+}
+
+// Pick an entry for (key, n, d), growing its slot if needed.  The entry is
+// not marked used until the caller commits it.
+int acquire_slot(mmq_ctx* c, const void* key, int64_t n, int64_t d, int* out_idx) {
+    int idx = find_entry(c, key, n, d);
+    if (idx < 0) {
+        for (int i = 0; i < kSlots && idx < 0; ++i)
+            if (!c->entries[i].used) idx = i;
+        if (idx < 0) {
+            idx = 0;
+            for (int i = 1; i < kSlots; ++i)
+                if (c->entries[i].last < c->entries[idx].last) idx = i;
+        }
+    }
+    const int64_t need = plane_bytes_for(n, d, nullptr, nullptr);
+    Slot& s = c->slots[idx];
+    if (s.cap < need) {
+        const int64_t total = c->plane_bytes - s.cap + need;
+        if (c->cap >= 0 && total > c->cap)
+            return fail(MMQ_E_OOM, "plane scratch cap %lld bytes exceeded (need %lld in total)",
+                        (long long)c->cap, (long long)total);
+        if (!c->dry) {
+            if (s.mem) {
+                hipError_t e = hipFree(s.mem);
+                if (e != hipSuccess) return hip_fail(e, "hipFree(plane slot)");
+                s.mem = nullptr;
+            }
+            void* m = nullptr;
+            hipError_t e = hipMalloc(&m, (size_t)need);
+            if (e != hipSuccess) {
+                c->plane_bytes -= s.cap;
+                s.cap = 0;
+                (void)hipGetLastError();
+                return fail(MMQ_E_OOM, "hipMalloc of a %lld-byte plane slot failed", (long long)need);
+            }
+            s.mem = m;
+        }
+        c->plane_bytes += need - s.cap;
+        s.cap = need;
+    }
+    *out_idx = idx;
+    return MMQ_OK;
+}
+
+void commit_entry(mmq_ctx* c, int idx, const void* key, int64_t n, int64_t d, bool dead) {
+    Entry& e = c->entries[idx];
+    e.used = true;
+    e.key = key;
+    e.n = n;
+    e.d = d;
+    e.dead = dead;
+    e.last = ++c->tick;
+}
+
+PlaneView view_of(const mmq_ctx* c, int idx) {
+    const Entry& e = c->entries[idx];
+    int64_t oD, oS;
+    plane_bytes_for(e.n, e.d, &oD, &oS);
+    char* base = (char*)c->slots[idx].mem;
+    PlaneView v;
+    v.q = (int8_t*)base;
+    v.D = (float*)(base + oD);
+    v.S = (int32_t*)(base + oS);
+    v.rows = round_up(e.n, kPlaneRows);
+    v.d = e.d;
+    return v;
+}
+
+int check_nd(const char* who, int64_t n, int64_t d) {
+    if (n < 1) return fail(MMQ_E_SHAPE, "%s: n=%lld must be >= 1", who, (long long)n);
+    if (d < kSuper || d % kSuper != 0)
+        return fail(MMQ_E_SHAPE, "%s: d=%lld must be a positive multiple of 256", who,
+                    (long long)d);
+    if (round_up(n, kPlaneRows) > (int64_t)1 << 30 || d > (int64_t)1 << 28 ||
+        round_up(n, kPlaneRows) * d > ((int64_t)1 << 40))
+        return fail(MMQ_E_SHAPE, "%s: n=%lld d=%lld too large", who, (long long)n, (long long)d);
+    return MMQ_OK;
+}
+
+// Shared body of the three producers.
+int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, const float* b,
+            float* y, int64_t n, int64_t d, float eps, int write_y, void* stream) {
+    if (!c) return fail(MMQ_E_ARG, "%s: null context", who);
+    int rc = check_nd(who, n, d);
+    if (rc) return rc;
+    if (!a || !aligned16(a) || (kind != kProdF32 && (!b || !aligned16(b))) ||
+        (kind != kProdF32 && (!y || !aligned16(y))))
+        return fail(MMQ_E_ARG, "%s: null or non-16-byte-aligned pointer", who);
+    const int64_t bytes = n * d * 4;
+    const void* key = kind == kProdF32 ? (const void*)a : (const void*)y;
+    if (kind == kProdF32 && overlaps_dead(c, a, bytes)) return refuse_dead(c, who, a);
+    if ((rc = use_device(c))) return rc;
+    int idx;
+    // The producer replaces whatever was cached for bytes it (re)defines.
+    if (kind != kProdF32) {
+        drop_overlapping(c, y, bytes);
+        if (write_y) {
+            // a real write makes previously dead bytes inside y valid again
+            c->dead.erase(std::remove_if(c->dead.begin(), c->dead.end(),
+                                         [&](const DeadRange& r) {
+                                             return r.lo >= (uintptr_t)y &&
+                                                    r.hi <= (uintptr_t)y + (uintptr_t)bytes;
+                                         }),
+                          c->dead.end());
+        }
+    } else {
+        drop_overlapping(c, a, bytes);
+    }
+    if ((rc = acquire_slot(c, key, n, d, &idx))) return rc;
+    const bool dead = kind != kProdF32 && !write_y;
+    commit_entry(c, idx, key, n, d, dead);
+    if (dead) c->dead.push_back({(uintptr_t)y, (uintptr_t)y + (uintptr_t)bytes});
+    if (kind == kProdRms) c->st.launches_quant_rms++;
+    else if (kind == kProdSwiglu) c->st.launches_quant_swiglu++;
+    else c->st.launches_quant_f32++;
+    if (c->dry) return MMQ_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const PlaneView pl = view_of(c, idx);
+    hipError_t e = launch_producer(kind, a, b, y, n, d, eps, write_y != 0, pl, s);
+    return after_launch(c, e, s, who);
+}
+
+// Consumer side: the plane of (a, n, d), quantising it on a miss.
+int plane_for(mmq_ctx* c, const char* who, const float* a, int64_t n, int64_t d, void* stream,
+              PlaneView* out) {
+    int idx = find_entry(c, a, n, d);
+    if (idx >= 0) {
+        c->st.cache_hits++;
+        c->entries[idx].last = ++c->tick;
+        *out = c->dry ? PlaneView{} : view_of(c, idx);
+        return MMQ_OK;
+    }
+    if (overlaps_dead(c, a, n * d * 4)) return refuse_dead(c, who, a);
+    c->st.cache_misses++;
+    int rc = produce(c, kProdF32, who, a, nullptr, nullptr, n, d, 0.0f, 0, stream);
+    if (rc) return rc;
+    idx = find_entry(c, a, n, d);
+    *out = c->dry ? PlaneView{} : view_of(c, idx);
+    return MMQ_OK;
+}
+
+int consume_check(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,
+                  int type, unsigned use, const char* who) {
+    if (!c) return fail(MMQ_E_ARG, "%s: null context", who);
+    if (!w || w->ctx != c) return fail(MMQ_E_ARG, "%s: weight is null or from another context", who);
+    if (w->w.type != type)
+        return fail(MMQ_E_TYPE, "%s: weight has type %d, this call needs %d", who, w->w.type, type);
+    if (!(w->w.uses & use))
+        return fail(MMQ_E_TYPE, "%s: weight was not registered for this consumer (uses=%u)", who,
+                    w->w.uses);
+    if (!a || !out || !aligned16(a) || !aligned16(out))
+        return fail(MMQ_E_ARG, "%s: null or non-16-byte-aligned pointer", who);
+    return check_nd(who, n, w->w.cols);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mmq_last_error(void) { return g_err.c_str(); }
+
+int64_t mmq_plane_rows(int64_t n) { return n < 1 ? 0 : round_up(n, kPlaneRows); }
+
+int mmq_create(int device, unsigned flags, mmq_ctx** out) {
+    if (!out) return fail(MMQ_E_ARG, "mmq_create: out is null");
+    *out = nullptr;
+    if (flags & ~(MMQ_CTX_SYNC_CHECK | MMQ_CTX_DRYRUN))
+        return fail(MMQ_E_ARG, "mmq_create: unknown flags 0x%x", flags);
+    mmq_ctx* c = new mmq_ctx();
+    c->flags = flags;
+    c->dry = (flags & MMQ_CTX_DRYRUN) != 0;
+    if (!c->dry) {
+        int count = 0;
+        if (hipGetDeviceCount(&count) != hipSuccess || count <= 0 || device < 0 ||
+            device >= count) {
+            (void)hipGetLastError();
+            delete c;
+            return fail(MMQ_E_DEVICE, "mmq_create: no HIP device %d (found %d)", device, count);
+        }
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+            delete c;
+            return fail(MMQ_E_DEVICE, "mmq_create: cannot query device %d", device);
+        }
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            delete c;
+            return fail(MMQ_E_DEVICE, "mmq_create: device %d is %s, this library is built for gfx950",
+                        device, prop.gcnArchName);
+        }
+        if (hipSetDevice(device) != hipSuccess) {
+            delete c;
+            return fail(MMQ_E_DEVICE, "mmq_create: hipSetDevice(%d) failed", device);
+        }
+        c->device = device;
+    }
+    *out = c;
+    return MMQ_OK;
+}
+
+void mmq_destroy(mmq_ctx* c) {
+    if (!c) return;
+    if (!c->dry) {
+        (void)hipSetDevice(c->device);
+        (void)hipDeviceSynchronize();
+        for (Slot& s : c->slots)
+            if (s.mem) (void)hipFree(s.mem);
+    }
+    delete c;
+}
+
+int mmq_set_scratch_cap(mmq_ctx* c, int64_t bytes) {
+    if (!c) return fail(MMQ_E_ARG, "mmq_set_scratch_cap: null context");
+    c->cap = bytes < 0 ? -1 : bytes;
+    return MMQ_OK;
+}
+
+int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const void* raw_host,
+                        unsigned uses, mmq_weight** out) {
+    const char* who = "mmq_register_weight";
+    if (!c || !raw_host || !out) return fail(MMQ_E_ARG, "%s: null argument", who);
+    *out = nullptr;
+    if (type != MMQ_Q4_K && type != MMQ_Q6_K)
+        return fail(MMQ_E_TYPE, "%s: unsupported weight type %d", who, type);
+    if (rows < 1 || cols < kSuper || cols % kSuper != 0 || rows > ((int64_t)1 << 30) ||
+        cols > ((int64_t)1 << 24))
+        return fail(MMQ_E_SHAPE, "%s: rows=%lld cols=%lld (cols must be a multiple of 256)", who,
+                    (long long)rows, (long long)cols);
+    if (uses & ~(MMQ_USE_GEMM | MMQ_USE_GEMV))
+        return fail(MMQ_E_ARG, "%s: unknown uses 0x%x", who, uses);
+    if (uses == 0) uses = type == MMQ_Q4_K ? MMQ_USE_GEMM : (MMQ_USE_GEMM | MMQ_USE_GEMV);
+    if (type == MMQ_Q4_K && (uses & MMQ_USE_GEMV))
+        return fail(MMQ_E_TYPE, "%s: the one-token GEMV is provided for q6_K only", who);
+
+    mmq_weight* h = new mmq_weight();
+    h->ctx = c;
+    h->dry = c->dry;
+    WeightDev& w = h->w;
+    w.type = type;
+    w.rows = rows;
+    w.cols = cols;
+    w.rows_pad = round_up(rows, kTileO);
+    w.uses = uses;
+    const int64_t nsb = cols / kSuper, nb = cols / kBlock, og = w.rows_pad / 32;
+    const int64_t bpb = type == MMQ_Q4_K ? 144 : 210;
+    const int64_t raw_bytes = rows * nsb * bpb;
+    const int npart = type == MMQ_Q4_K ? 1 : 2;
+    const int64_t wa_b = w.rows_pad * cols * npart * 2;
+    const int64_t dmr_b = og * nsb * (type == MMQ_Q4_K ? 64 : 32) * 4;
+    const int64_t mf_b = type == MMQ_Q4_K ? og * nsb * 512 * 2 : 0;
+    const int64_t ql_b = rows * nb * 16, qh_b = rows * nb * 8, sc_b = rows * nb * 2,
+                  dv_b = rows * nsb * 4;
+    int64_t total = 0;
+    if (uses & MMQ_USE_GEMM) total += wa_b + dmr_b + mf_b;
+    if (uses & MMQ_USE_GEMV) total += ql_b + qh_b + sc_b + dv_b;
+    w.bytes = total;
+    if (c->dry) {
+        c->weight_bytes += total;
+        *out = h;
+        return MMQ_OK;
+    }
+    int rc = use_device(c);
+    if (rc) { delete h; return rc; }
+
+    std::vector<void*> allocs;
+    auto cleanup = [&]() {
+        for (void* p : allocs) (void)hipFree(p);
+        delete h;
+    };
+    auto dalloc = [&](int64_t bytes, void** p) -> bool {
+        if (hipMalloc(p, (size_t)bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        allocs.push_back(*p);
+        return true;
+    };
+    void* raw_dev = nullptr;
+    if (!dalloc(raw_bytes, &raw_dev)) { cleanup(); return fail(MMQ_E_OOM, "%s: staging alloc failed", who); }
+    hipError_t e = hipMemcpy(raw_dev, raw_host, (size_t)raw_bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: copy"); }
+    if (uses & MMQ_USE_GEMM) {
+        void *p1 = nullptr, *p2 = nullptr, *p3 = nullptr;
+        if (!dalloc(wa_b, &p1) || !dalloc(dmr_b, &p2) || (mf_b && !dalloc(mf_b, &p3))) {
+            cleanup();
+            return fail(MMQ_E_OOM, "%s: %lld bytes of matmul tiles", who, (long long)(wa_b + dmr_b + mf_b));
+        }
+        w.wa = (_Float16*)p1; w.dmr = (float*)p2; w.mfrag = (_Float16*)p3;
+        hipMemset(p1, 0, (size_t)wa_b);
+        hipMemset(p2, 0, (size_t)dmr_b);
+        if (p3) hipMemset(p3, 0, (size_t)mf_b);
+        e = launch_repack_gemm((const uint8_t*)raw_dev, w, nullptr);
+        if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: repack"); }
+    }
+    if (uses & MMQ_USE_GEMV) {
+        void *p1 = nullptr, *p2 = nullptr, *p3 = nullptr, *p4 = nullptr;
+        if (!dalloc(ql_b, &p1) || !dalloc(qh_b, &p2) || !dalloc(sc_b, &p3) || !dalloc(dv_b, &p4)) {
+            cleanup();
+            return fail(MMQ_E_OOM, "%s: GEMV tiles", who);
+        }
+        w.gv_ql = (uint4*)p1; w.gv_qh = (uint2*)p2; w.gv_sc = (int16_t*)p3; w.gv_d = (float*)p4;
+        e = launch_repack_gemv((const uint8_t*)raw_dev, w, nullptr);
+        if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: repack"); }
+    }
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: sync"); }
+    (void)hipFree(raw_dev);
+    allocs.erase(allocs.begin());
+    c->weight_bytes += total;
+    *out = h;
+    return MMQ_OK;
+}
+
+void mmq_weight_free(mmq_weight* h) {
+    if (!h) return;
+    if (!h->dry) {
+        (void)hipSetDevice(h->ctx->device);
+        (void)hipDeviceSynchronize();
+        void* ps[] = {h->w.wa, h->w.dmr, h->w.mfrag, h->w.gv_ql, h->w.gv_qh, h->w.gv_sc, h->w.gv_d};
+        for (void* p : ps)
+            if (p) (void)hipFree(p);
+    }
+    h->ctx->weight_bytes -= h->w.bytes;
+    delete h;
+}
+
+int64_t mmq_weight_bytes(const mmq_weight* h) { return h ? h->w.bytes : 0; }
+
+int mmq_quant_rms(mmq_ctx* c, const float* x, const float* w, float* y, int64_t n, int64_t d,
+                  float eps, int write_y, void* stream) {
+    return produce(c, kProdRms, "mmq_quant_rms", x, w, y, n, d, eps, write_y, stream);
+}
+
+int mmq_quant_swiglu(mmq_ctx* c, const float* gate, const float* up, float* y, int64_t n,
+                     int64_t d, int write_y, void* stream) {
+    return produce(c, kProdSwiglu, "mmq_quant_swiglu", gate, up, y, n, d, 0.0f, write_y, stream);
+}
+
+int mmq_quant_f32(mmq_ctx* c, const float* x, int64_t n, int64_t d, void* stream) {
+    return produce(c, kProdF32, "mmq_quant_f32", x, nullptr, nullptr, n, d, 0.0f, 0, stream);
+}
+
+static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,
+                       void* stream, int type, const char* who) {
+    int rc = consume_check(c, w, a, n, out, type, MMQ_USE_GEMM, who);
+    if (rc) return rc;
+    if ((rc = use_device(c))) return rc;
+    PlaneView pl;
+    if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;
+    if (type == MMQ_Q4_K) c->st.launches_gemm_q4k++;
+    else c->st.launches_gemm_q6k++;
+    if (c->dry) return MMQ_OK;
+    hipStream_t s = (hipStream_t)stream;
+    return after_launch(c, launch_gemm(w->w, pl, n, out, s), s, who);
+}
+
+int mmq_gemm_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,
+                 void* stream) {
+    return gemm_common(c, w, a, n, out, stream, MMQ_Q4_K, "mmq_gemm_q4k");
+}
+
+int mmq_gemm_q6k(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,
+                 void* stream) {
+    return gemm_common(c, w, a, n, out, stream, MMQ_Q6_K, "mmq_gemm_q6k");
+}
+
+int mmvq_q6k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* stream) {
+    const char* who = "mmvq_q6k";
+    int rc = consume_check(c, w, a, 1, out, MMQ_Q6_K, MMQ_USE_GEMV, who);
+    if (rc) return rc;
+    if ((rc = use_device(c))) return rc;
+    PlaneView pl;
+    if ((rc = plane_for(c, who, a, 1, w->w.cols, stream, &pl))) return rc;
+    c->st.launches_mmvq_q6k++;
+    if (c->dry) return MMQ_OK;
+    hipStream_t s = (hipStream_t)stream;
+    return after_launch(c, launch_mmvq_q6k(w->w, pl, out, s), s, who);
+}
+
+void mmq_cache_clear(mmq_ctx* c) {
+    if (!c) return;
+    for (Entry& e : c->entries) e.used = false;
+    c->dead.clear();
+}
+
+int mmq_cache_invalidate(mmq_ctx* c, const void* key) {
+    if (!c) return fail(MMQ_E_ARG, "mmq_cache_invalidate: null context");
+    for (Entry& e : c->entries)
+        if (e.used && e.key == key) e.used = false;
+    c->dead.erase(std::remove_if(c->dead.begin(), c->dead.end(),
+                                 [&](const DeadRange& r) { return r.lo == (uintptr_t)key; }),
+                  c->dead.end());
+    return MMQ_OK;
+}
+
+int mmq_plane_export(mmq_ctx* c, const void* key, int64_t n, int64_t d, int include_pad,
+                     int8_t* q, float* dq, int32_t* s, void* stream) {
+    const char* who = "mmq_plane_export";
+    if (!c || !q || !dq || !s) return fail(MMQ_E_ARG, "%s: null argument", who);
+    const int idx = find_entry(c, key, n, d);
+    if (idx < 0) return fail(MMQ_E_ARG, "%s: no plane recorded for (%p, %lld, %lld)", who, key,
+                             (long long)n, (long long)d);
+    if (c->dry) return fail(MMQ_E_DEVICE, "%s: dry-run context holds no planes", who);
+    int rc = use_device(c);
+    if (rc) return rc;
+    const PlaneView pl = view_of(c, idx);
+    const int64_t rows = include_pad ? pl.rows : n;
+    const int64_t nb = d / kBlock;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(q, pl.q, (size_t)(rows * d), hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(dq, pl.D, (size_t)(rows * nb * 4), hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(s, pl.S, (size_t)(rows * nb * 4), hipMemcpyDeviceToDevice, st);
+    return after_launch(c, e, st, who);
+}
+
+int mmq_stats(mmq_ctx* c, mmq_stats_t* st) {
+    if (!c || !st) return fail(MMQ_E_ARG, "mmq_stats: null argument");
+    *st = c->st;
+    int64_t live = 0;
+    for (const Entry& e : c->entries) live += e.used ? 1 : 0;
+    st->cache_entries = live;
+    st->plane_bytes = c->plane_bytes;
+    st->weight_bytes = c->weight_bytes;
+    return MMQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// mmq_internal.h -- launcher interface between the host library (host.cpp)
+// and the gfx950 kernels (quant.hip, repack.hip, gemm.hip, mmvq.hip).
+// Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmq {
+
+// Plane of n tokens x d values: rows padded to kPlaneRows, three arrays in one
+// allocation: q int8 [rows][d], D f32 [rows][d/32], S int32 [rows][d/32].
+constexpr int kPlaneRows = 32;
+constexpr int kBlock = 32;     // activation block (one f32 scale, one int sum)
+constexpr int kSuper = 256;    // K-quant superblock
+
+struct PlaneView {
+    int8_t* q;
+    float* D;
+    int32_t* S;
+    int64_t rows;   // padded row count
+    int64_t d;
+};
+
+// Matmul tiles: weights are padded to kTileO output rows (zero weights).
+constexpr int kTileO = 128;
+
+// Registered weight, device side.  Layouts are written by repack.hip and read
+// by gemm.hip / mmvq.hip; they are described there.
+struct WeightDev {
+    int type = 0;             // 12 = q4_K, 14 = q6_K
+    int64_t rows = 0, cols = 0, rows_pad = 0;
+    unsigned uses = 0;
+    // prefill matmul tiles
+    _Float16* wa = nullptr;   // f16 integer-valued A fragments
+    float* dmr = nullptr;     // per (row group, superblock) scales, fragment order
+    _Float16* mfrag = nullptr;// q4_K only: 6-bit mins as f16, fragment order
+    // one-token GEMV (q6_K)
+    uint4* gv_ql = nullptr;   // [rows][cols/32] low nibbles
+    uint2* gv_qh = nullptr;   // [rows][cols/32] high bit pairs
+    int16_t* gv_sc = nullptr; // [rows][cols/32] two int8 sub-scales
+    float* gv_d = nullptr;    // [rows][cols/256]
+    int64_t bytes = 0;
+};
+
+// ---- producers (quant.hip) ----
+enum ProducerKind { kProdRms = 0, kProdSwiglu = 1, kProdF32 = 2 };
+hipError_t launch_producer(ProducerKind kind, const float* a, const float* b, float* y,
+                           int64_t n, int64_t d, float eps, bool write_y,
+                           const PlaneView& pl, hipStream_t s);
+
+// ---- registration repack (repack.hip): raw superblocks already on device ----
+hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s);
+hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s);
+
+// ---- consumers ----
+hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
+                       hipStream_t s);
+hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
+                           hipStream_t s);
+
+}  // namespace mmq

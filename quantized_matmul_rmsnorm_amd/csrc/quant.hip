@@ -1,0 +1,224 @@
+// quant.hip -- fused producers that quantise f32 activations in registers into
+// a q8 plane (gfx950, wave64).
+//
+// Method: "55 · r52 — skip-write mode 2" (sections 2.2 and 3.2) and the decode
+// RMSNorm of "72 · D3-7 ..." (Excerpt C).  Per row of d values (d % 256 == 0):
+//   RMSNorm : y = (x * s) * w,  s = 1 / sqrt(sum(x^2) / d + eps)
+//   SwiGLU  : y = (g / (1 + exp(-g))) * u
+//   F32     : y = x                      (standalone quantise)
+// then per 32-block: amax = max|y|, D = amax / 127, q = clamp(rint(y / D),
+// -127, 127), S = sum(q); an all-zero block has D = 0, q = 0, S = 0.
+//
+// Geometry.  One wave per row.  The row is swept in rounds of 256 values: in
+// round r lane l owns the float4 at 256*r + 4*l, so each wave access is one
+// contiguous 1 KiB (the pages' rule that a full-width coalesced access must
+// never be broken), and the 8 consecutive lanes 8g..8g+7 hold exactly one
+// 32-block.  amax and the code sum are reduced inside those 8 lanes with DPP
+// (quad_perm xor-1, xor-2, then row_half_mirror).  Max and integer sums are
+// exact in any order, so the plane does not depend on the lane grouping; the
+// f32 y values themselves are computed by the same expressions whether or not
+// y is stored, so write_y = 0, write_y = 1 and a standalone quantise of the
+// stored y give byte-identical planes.
+//
+// RMSNorm accumulates sum(x^2) in f64 (products of f32 values are exact in
+// f64) and rounds the scale once from f64, which makes s independent of the
+// summation order to within one f64 rounding.  For d <= 256*MAXR the row's x
+// stays in registers between the two passes; longer rows are re-read.
+//
+// Rows n .. rows-1 of the plane (the padding to a multiple of 32 rows) are
+// written as zeros, so a plane's content never depends on what its slot held
+// before.
+#include "mmq_internal.h"
+
+namespace mmq {
+namespace {
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7-i in each 8
+
+__device__ __forceinline__ float max8(float v) {
+    v = fmaxf(v, __int_as_float(dpp<kQuadXor1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<kQuadXor2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<kHalfMirror>(__float_as_int(v))));
+    return v;
+}
+
+__device__ __forceinline__ int sum8(int v) {
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kHalfMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ int code(float v, float dsc) {
+    float r = rintf(v / dsc);                // IEEE quotient, round half to even
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// Quantise the 4 values of this lane; lanes 8g..8g+7 form one 32-block.
+// Writes the 4 codes as one dword and, from the group's first lane, D and S.
+__device__ __forceinline__ void quant4(float4 v, int lane, uint32_t* qdst, float* Ddst,
+                                       int32_t* Sdst) {
+    float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    am = max8(am);
+    const float dsc = am / 127.0f;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (am > 0.0f) {
+        q0 = code(v.x, dsc); q1 = code(v.y, dsc); q2 = code(v.z, dsc); q3 = code(v.w, dsc);
+    }
+    *qdst = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
+            ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
+    const int s = sum8((q0 + q1) + (q2 + q3));
+    if ((lane & 7) == 0) {
+        *Ddst = dsc;
+        *Sdst = s;
+    }
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float den = 1.0f + expf(-g);
+    return (g / den) * u;
+}
+
+template <int KIND, bool WRITE_Y, int MAXR>
+__global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
+                                                  const float* __restrict__ b,
+                                                  float* __restrict__ y, int n, int d,
+                                                  float eps, int8_t* __restrict__ q,
+                                                  float* __restrict__ D,
+                                                  int32_t* __restrict__ S, int rows) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const int nb = d / kBlock;
+    const int rounds = d / kSuper;
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (int64_t)row * d);
+    float* Dr = D + (int64_t)row * nb;
+    int32_t* Sr = S + (int64_t)row * nb;
+    const int g = lane >> 3;
+
+    if (row >= n) {  // padded tail rows: deterministic zeros
+        for (int r = 0; r < rounds; ++r) {
+            q4[64 * r + lane] = 0u;
+            if ((lane & 7) == 0) {
+                Dr[8 * r + g] = 0.0f;
+                Sr[8 * r + g] = 0;
+            }
+        }
+        return;
+    }
+
+    const float4* a4 = reinterpret_cast<const float4*>(a + (int64_t)row * d);
+    const float4* b4 = reinterpret_cast<const float4*>(
+        KIND == kProdRms ? b : (b ? b + (int64_t)row * d : nullptr));
+    float4* y4 = reinterpret_cast<float4*>(y + (int64_t)row * d);
+
+    float scale = 0.0f;
+    float4 xr[MAXR > 0 ? MAXR : 1];
+    if constexpr (KIND == kProdRms) {
+        double ss = 0.0;
+        if constexpr (MAXR > 0) {
+#pragma unroll
+            for (int r = 0; r < MAXR; ++r)
+                if (r < rounds) xr[r] = a4[64 * r + lane];
+#pragma unroll
+            for (int r = 0; r < MAXR; ++r)
+                if (r < rounds) {
+                    const float4 v = xr[r];
+                    ss += (double)v.x * (double)v.x;
+                    ss += (double)v.y * (double)v.y;
+                    ss += (double)v.z * (double)v.z;
+                    ss += (double)v.w * (double)v.w;
+                }
+        } else {
+            for (int r = 0; r < rounds; ++r) {
+                const float4 v = a4[64 * r + lane];
+                ss += (double)v.x * (double)v.x;
+                ss += (double)v.y * (double)v.y;
+                ss += (double)v.z * (double)v.z;
+                ss += (double)v.w * (double)v.w;
+            }
+        }
+        ss = wave_sum_f64(ss);
+        scale = (float)(1.0 / sqrt(ss / (double)d + (double)eps));
+    }
+
+    auto one_round = [&](int r, float4 xin) {
+        float4 v;
+        if constexpr (KIND == kProdRms) {
+            const float4 w = b4[64 * r + lane];
+            v.x = (xin.x * scale) * w.x;
+            v.y = (xin.y * scale) * w.y;
+            v.z = (xin.z * scale) * w.z;
+            v.w = (xin.w * scale) * w.w;
+        } else if constexpr (KIND == kProdSwiglu) {
+            const float4 u = b4[64 * r + lane];
+            v.x = silu_mul(xin.x, u.x);
+            v.y = silu_mul(xin.y, u.y);
+            v.z = silu_mul(xin.z, u.z);
+            v.w = silu_mul(xin.w, u.w);
+        } else {
+            v = xin;
+        }
+        if constexpr (WRITE_Y) y4[64 * r + lane] = v;
+        quant4(v, lane, q4 + 64 * r + lane, Dr + 8 * r + g, Sr + 8 * r + g);
+    };
+
+    if constexpr (MAXR > 0) {
+#pragma unroll
+        for (int r = 0; r < MAXR; ++r)
+            if (r < rounds) one_round(r, xr[r]);
+    } else {
+        for (int r = 0; r < rounds; ++r) one_round(r, a4[64 * r + lane]);
+    }
+}
+
+template <int KIND, bool WY>
+hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, int64_t d,
+                         float eps, const PlaneView& pl, hipStream_t s) {
+    const int rounds = (int)(d / kSuper);
+    dim3 grid((unsigned)((pl.rows + 3) / 4)), block(256);
+    if (KIND == kProdRms && rounds <= 16) {
+        hipLaunchKernelGGL((k_producer<KIND, WY, 16>), grid, block, 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
+    } else if (KIND == kProdRms && rounds <= 32) {
+        hipLaunchKernelGGL((k_producer<KIND, WY, 32>), grid, block, 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
+    } else {
+        hipLaunchKernelGGL((k_producer<KIND, WY, 0>), grid, block, 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_producer(ProducerKind kind, const float* a, const float* b, float* y,
+                           int64_t n, int64_t d, float eps, bool write_y,
+                           const PlaneView& pl, hipStream_t s) {
+    switch (kind) {
+        case kProdRms:
+            return write_y ? dispatch_maxr<kProdRms, true>(a, b, y, n, d, eps, pl, s)
+                           : dispatch_maxr<kProdRms, false>(a, b, y, n, d, eps, pl, s);
+        case kProdSwiglu:
+            return write_y ? dispatch_maxr<kProdSwiglu, true>(a, b, y, n, d, eps, pl, s)
+                           : dispatch_maxr<kProdSwiglu, false>(a, b, y, n, d, eps, pl, s);
+        default:
+            return dispatch_maxr<kProdF32, false>(a, nullptr, nullptr, n, d, eps, pl, s);
+    }
+}
+
+}  // namespace mmq

@@ -1,0 +1,208 @@
+// repack.hip -- registration-time repack of raw q4_K / q6_K superblocks into the
+// device tiles the matmul and GEMV kernels read.
+//
+// The pages register every q4_K / q6_K weight once, before the first forward,
+// and keep registration-time planes of them ("64 · r60 ...", section 3.1; the
+// W_exp / W_dsc planes named in section 1).  Here a weight is copied to the
+// device raw and this kernel rewrites it; it runs once per weight, outside any
+// timed loop.
+//
+// Superblock formats (public GGUF K-quants, 256 weights each):
+//   q4_K, 144 B: f16 d | f16 dmin | 12 B packed 6-bit (scale, min) x 8 | 128 B
+//                4-bit quants; w = d*sc_j*q - dmin*m_j, j = sub-block of 32.
+//   q6_K, 210 B: ql[128] | qh[64] | int8 scales[16] | f16 d;
+//                w = d*sc[e/16]*(q - 32), q in [0, 63].
+//
+// Prefill tiles (read by gemm.hip).  Rows are padded to a multiple of 128
+// with zero weights; og = row / 32, ol = row % 32; for k: k16 = k / 16,
+// lane = ol + 32*((k % 16) / 8), e = k % 8 -- the A-operand fragment of
+// v_mfma_f32_32x32x16_f16 (lane holds row lane%32, 8 consecutive k of the
+// half lane/32), so a wave reads one fragment as 1 KiB contiguous.
+//   q4_K: wa[og][k16][lane][e] = f16(sc_j * q)        (exact: <= 63*15 = 945)
+//         dmr[og][sb][{d,dmin}][half][r] f32, r/half as the MFMA output row
+//             of ol: ol = 8*(r/4) + 4*half + r%4
+//         mfrag[og][sb][lane][j] = f16(m_j) for both lane halves (exact)
+//   q6_K: v = sc * (q - 32) in [-4096, 4096] needs 13 bits, more than f16
+//         holds exactly, so it is split v = hi + lo with lo = v & 1 and hi
+//         even (exact in f16 up to 4096):
+//         wa[og][k16][part][lane][e] = f16(part ? lo : hi)
+//         dmr[og][sb][half][r] = d
+// One-token GEMV tiles (q6_K, read by mmvq.hip), per row o and 32-block b
+// (weights w_0..w_31):
+//   ql[o][b]  uint4: dword u holds w_8u..w_8u+7; byte i = low4(w_8u+i) |
+//                    low4(w_8u+i+4) << 4
+//   qh[o][b]  uint2: dword u holds w_16u..w_16u+15; byte i = hi2(w_i') |
+//                    hi2(w_i'+4) << 2 | hi2(w_i'+8) << 4 | hi2(w_i'+12) << 6,
+//                    i' = 16u + i
+//   sc[o][b]  int16: low byte = sub-scale of w_0..15, high byte = of w_16..31
+//   d[o][sb]  f32
+#include "mmq_internal.h"
+
+namespace mmq {
+namespace {
+
+__device__ __forceinline__ float f16f(const uint8_t* p) {
+    const uint16_t bits = (uint16_t)(p[0] | (p[1] << 8));
+    return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+__device__ __forceinline__ void q4k_decode(const uint8_t* blk, float& d, float& dmin,
+                                           int sc[8], int mn[8]) {
+    d = f16f(blk);
+    dmin = f16f(blk + 2);
+    const uint8_t* s = blk + 4;
+    for (int j = 0; j < 4; ++j) {
+        sc[j] = s[j] & 63;
+        mn[j] = s[j + 4] & 63;
+        sc[j + 4] = (s[j + 8] & 15) | ((s[j] >> 6) << 4);
+        mn[j + 4] = (s[j + 8] >> 4) | ((s[j + 4] >> 6) << 4);
+    }
+}
+
+__device__ __forceinline__ int q4k_quant(const uint8_t* blk, int e) {
+    const uint8_t byte = blk[16 + 32 * (e / 64) + (e % 32)];
+    return (e % 64) < 32 ? (byte & 15) : (byte >> 4);
+}
+
+__device__ __forceinline__ int q6k_quant(const uint8_t* blk, int e) {
+    const int h = e / 128, r = e % 128, s = r / 32, l = r % 32;
+    const uint8_t lb = blk[64 * h + l + 32 * (s & 1)];
+    const int lo = s < 2 ? (lb & 15) : (lb >> 4);
+    const int hi = (blk[128 + 32 * h + l] >> (2 * s)) & 3;
+    return lo | (hi << 4);
+}
+
+__device__ __forceinline__ void frag_pos(int64_t o, int64_t k, int64_t& og, int& lane, int& e,
+                                         int64_t& k16) {
+    og = o / 32;
+    const int ol = (int)(o % 32);
+    k16 = k / 16;
+    lane = ol + 32 * (int)((k % 16) / 8);
+    e = (int)(k % 8);
+}
+
+__device__ __forceinline__ int out_reg(int ol, int& half) {
+    half = (ol % 8) / 4;
+    return 4 * (ol / 8) + (ol % 4);
+}
+
+// One thread per (row, superblock) of the real rows.
+__global__ void k_repack_q4k_gemm(const uint8_t* __restrict__ raw, int64_t rows, int64_t cols,
+                                  _Float16* __restrict__ wa, float* __restrict__ dmr,
+                                  _Float16* __restrict__ mfrag) {
+    const int64_t nsb = cols / kSuper;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nsb) return;
+    const int64_t o = idx / nsb, sb = idx % nsb;
+    const uint8_t* blk = raw + idx * 144;
+    float d, dmin;
+    int sc[8], mn[8];
+    q4k_decode(blk, d, dmin, sc, mn);
+    const int64_t K16 = cols / 16;
+    for (int e = 0; e < kSuper; ++e) {
+        int64_t og, k16; int lane, el;
+        frag_pos(o, sb * kSuper + e, og, lane, el, k16);
+        wa[((og * K16 + k16) * 64 + lane) * 8 + el] = (_Float16)(float)(sc[e / 32] * q4k_quant(blk, e));
+    }
+    const int64_t og = o / 32;
+    const int ol = (int)(o % 32);
+    int half;
+    const int r = out_reg(ol, half);
+    float* dm = dmr + (og * nsb + sb) * 64;
+    dm[half * 16 + r] = d;
+    dm[32 + half * 16 + r] = dmin;
+    _Float16* mf = mfrag + (og * nsb + sb) * 512;
+    for (int j = 0; j < 8; ++j) {
+        mf[ol * 8 + j] = (_Float16)(float)mn[j];
+        mf[(ol + 32) * 8 + j] = (_Float16)(float)mn[j];
+    }
+}
+
+__global__ void k_repack_q6k_gemm(const uint8_t* __restrict__ raw, int64_t rows, int64_t cols,
+                                  _Float16* __restrict__ wa, float* __restrict__ dmr) {
+    const int64_t nsb = cols / kSuper;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nsb) return;
+    const int64_t o = idx / nsb, sb = idx % nsb;
+    const uint8_t* blk = raw + idx * 210;
+    const float d = f16f(blk + 208);
+    const int8_t* scales = reinterpret_cast<const int8_t*>(blk + 192);
+    const int64_t K16 = cols / 16;
+    for (int e = 0; e < kSuper; ++e) {
+        const int v = (int)scales[e / 16] * (q6k_quant(blk, e) - 32);
+        const int lo = v & 1;
+        const int hi = v - lo;
+        int64_t og, k16; int lane, el;
+        frag_pos(o, sb * kSuper + e, og, lane, el, k16);
+        const int64_t base = (og * K16 + k16) * 2;
+        wa[((base + 0) * 64 + lane) * 8 + el] = (_Float16)(float)hi;
+        wa[((base + 1) * 64 + lane) * 8 + el] = (_Float16)(float)lo;
+    }
+    const int64_t og = o / 32;
+    int half;
+    const int r = out_reg((int)(o % 32), half);
+    dmr[(og * nsb + sb) * 32 + half * 16 + r] = d;
+}
+
+__global__ void k_repack_q6k_gemv(const uint8_t* __restrict__ raw, int64_t rows, int64_t cols,
+                                  uint4* __restrict__ ql, uint2* __restrict__ qh,
+                                  int16_t* __restrict__ scv, float* __restrict__ dv) {
+    const int64_t nsb = cols / kSuper;
+    const int64_t nb = cols / kBlock;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nsb) return;
+    const int64_t o = idx / nsb, sb = idx % nsb;
+    const uint8_t* blk = raw + idx * 210;
+    const int8_t* scales = reinterpret_cast<const int8_t*>(blk + 192);
+    dv[o * nsb + sb] = f16f(blk + 208);
+    for (int j = 0; j < 8; ++j) {
+        int q[32];
+        for (int i = 0; i < 32; ++i) q[i] = q6k_quant(blk, 32 * j + i);
+        uint32_t L[4], H[2];
+        for (int u = 0; u < 4; ++u) {
+            uint32_t v = 0;
+            for (int i = 0; i < 4; ++i)
+                v |= (uint32_t)((q[8 * u + i] & 15) | ((q[8 * u + i + 4] & 15) << 4)) << (8 * i);
+            L[u] = v;
+        }
+        for (int u = 0; u < 2; ++u) {
+            uint32_t v = 0;
+            for (int i = 0; i < 4; ++i) {
+                const int b0 = 16 * u + i;
+                const uint32_t byte = (uint32_t)((q[b0] >> 4) | ((q[b0 + 4] >> 4) << 2) |
+                                                 ((q[b0 + 8] >> 4) << 4) | ((q[b0 + 12] >> 4) << 6));
+                v |= byte << (8 * i);
+            }
+            H[u] = v;
+        }
+        const int64_t b = sb * 8 + j;
+        ql[o * nb + b] = make_uint4(L[0], L[1], L[2], L[3]);
+        qh[o * nb + b] = make_uint2(H[0], H[1]);
+        scv[o * nb + b] = (int16_t)(((uint16_t)(uint8_t)scales[2 * j]) |
+                                    ((uint16_t)(uint8_t)scales[2 * j + 1] << 8));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s) {
+    const int64_t total = w.rows * (w.cols / kSuper);
+    const dim3 block(128), grid((unsigned)((total + 127) / 128));
+    if (w.type == 12)
+        hipLaunchKernelGGL(k_repack_q4k_gemm, grid, block, 0, s, raw_dev, w.rows, w.cols, w.wa,
+                           w.dmr, w.mfrag);
+    else
+        hipLaunchKernelGGL(k_repack_q6k_gemm, grid, block, 0, s, raw_dev, w.rows, w.cols, w.wa,
+                           w.dmr);
+    return hipGetLastError();
+}
+
+hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s) {
+    const int64_t total = w.rows * (w.cols / kSuper);
+    const dim3 block(128), grid((unsigned)((total + 127) / 128));
+    hipLaunchKernelGGL(k_repack_q6k_gemv, grid, block, 0, s, raw_dev, w.rows, w.cols, w.gv_ql,
+                       w.gv_qh, w.gv_sc, w.gv_d);
+    return hipGetLastError();
+}
+
+}  // namespace mmq

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs come from synth.py (seeded); expected values come only from oracle/.
+Planes are compared on the canonical export; matmuls against the oracle run on
+the GPU's exported plane (which isolates the matmul from producer rounding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_matmul_rmsnorm_amd as mmq
+import synth
+from tests.gpu_util import (assert_fused_close, assert_gemm_close, assert_plane_equal,
+                            dev_tensor, export_plane)
+
+pytestmark = pytest.mark.gpu
+EPS = synth.EPS
+WT = {"q4_K": 12, "q6_K": 14}
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = mmq.mmq_create(0, 0)
+    yield c
+    mmq.mmq_destroy(c)
+
+
+def _act(tag, n, d, spread=True):
+    rng = synth.rng_for("test", n * 100003 + d, tag)
+    y = synth.activations(rng, n, d)
+    if spread:  # rows and blocks of very different magnitude, a few all-zero blocks
+        y *= rng.uniform(0.05, 20.0, (n, 1)).astype(np.float32)
+        y.reshape(n, -1, 32)[:, ::7, :] *= np.float32(1e-3)
+        if n * d >= 64:
+            y.reshape(-1, 32)[::13] = 0.0
+    return np.ascontiguousarray(y, np.float32)
+
+
+# ------------------------------------------------------------------ producers
+@pytest.mark.parametrize("n,d", [(1, 256), (37, 512), (64, 3584), (3, 5120), (5, 18944),
+                                 (3314, 3584)])
+def test_quant_f32_bit_exact(ctx, n, d):
+    y = _act("qf32", n, d)
+    x = dev_tensor(y)
+    mmq.mmq_quant_f32(ctx, x, n, d)
+    assert_plane_equal(export_plane(ctx, x, n, d), oracle.quantize(y), f"quant_f32 {n}x{d}")
+
+
+def test_quant_f32_special_values(ctx):
+    n, d = 4, 256
+    y = np.zeros((n, d), np.float32)
+    y[0, :32] = 1e-40                     # subnormal block
+    y[0, 32:64] = np.linspace(-3e-39, 3e-39, 32)
+    y[1, :32] = 3e38                      # near the top of the range
+    y[1, 40] = -1e-30                     # lone tiny value
+    y[2, ::2] = 2.5                       # ties around the code grid
+    y[2, 1::2] = 127.0
+    y[3] = np.float32(7.0) / np.float32(3.0)
+    x = dev_tensor(y)
+    mmq.mmq_quant_f32(ctx, x, n, d)
+    assert_plane_equal(export_plane(ctx, x, n, d), oracle.quantize(y), "special values")
+
+
+@pytest.mark.parametrize("n,d", [(37, 512), (128, 3584), (1, 5120), (3314, 3584)])
+def test_quant_rms_fused_and_cross_mode(ctx, n, d):
+    rng = synth.rng_for("test", n, f"rms{d}")
+    xh = synth.activations(rng, n, d)
+    wh = synth.rms_weight(rng, d)
+    y_ref = oracle.rmsnorm(xh, wh, EPS)
+    ref = oracle.quantize(y_ref)
+    x, w = dev_tensor(xh), dev_tensor(wh)
+    y1 = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    y0 = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    mmq.mmq_quant_rms(ctx, x, w, y1, n, d, EPS, 1)
+    p1 = export_plane(ctx, y1, n, d)
+    mmq.mmq_quant_rms(ctx, x, w, y0, n, d, EPS, 0)
+    p0 = export_plane(ctx, y0, n, d)
+    y_gpu = y1.cpu().numpy()
+    mmq.mmq_quant_f32(ctx, y1, n, d)          # standalone quantise of the written y
+    pf = export_plane(ctx, y1, n, d)
+    assert_plane_equal(p0, p1, "write_y=0 vs 1")
+    assert_plane_equal(pf, p1, "standalone vs fused")
+    assert_plane_equal(oracle.quantize(y_gpu), p1, "oracle quantiser on the GPU's y")
+    assert_fused_close(p1, ref, y_gpu, y_ref, f"rms {n}x{d}")
+    rel = np.abs(y_gpu.astype(np.float64) - y_ref) / np.maximum(np.abs(y_ref), 1e-30)
+    assert rel.max() < 4e-7
+
+
+@pytest.mark.parametrize("n,d", [(37, 512), (64, 18944), (1, 13824), (3314, 18944)])
+def test_quant_swiglu_fused_and_cross_mode(ctx, n, d):
+    rng = synth.rng_for("test", n, f"swiglu{d}")
+    gh = synth.activations(rng, n, d)
+    uh = synth.activations(rng, n, d)
+    y_ref = oracle.swiglu(gh, uh)
+    ref = oracle.quantize(y_ref)
+    g, u = dev_tensor(gh), dev_tensor(uh)
+    y1 = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    y0 = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    mmq.mmq_quant_swiglu(ctx, g, u, y1, n, d, 1)
+    p1 = export_plane(ctx, y1, n, d)
+    mmq.mmq_quant_swiglu(ctx, g, u, y0, n, d, 0)
+    p0 = export_plane(ctx, y0, n, d)
+    y_gpu = y1.cpu().numpy()
+    mmq.mmq_quant_f32(ctx, y1, n, d)
+    pf = export_plane(ctx, y1, n, d)
+    assert_plane_equal(p0, p1, "write_y=0 vs 1")
+    assert_plane_equal(pf, p1, "standalone vs fused")
+    assert_fused_close(p1, ref, y_gpu, y_ref, f"swiglu {n}x{d}")
+    rel = np.abs(y_gpu.astype(np.float64) - y_ref) / np.maximum(np.abs(y_ref), 1e-30)
+    assert np.quantile(rel, 0.999999) < 1e-6
+
+
+def test_padded_rows_zero_after_poisoned_slot(ctx):
+    """A slot that held a bigger plane is reused for a smaller one: the padded
+    rows must come back zero, not stale."""
+    d = 512
+    mmq.mmq_cache_clear(ctx)
+    big = dev_tensor(_act("poison", 64, d) + np.float32(5.0))
+    keys = [big]
+    mmq.mmq_quant_f32(ctx, big, 64, d)
+    # fill every slot with non-zero planes, then clear and write a 37-row plane
+    for i in range(8):
+        t = dev_tensor(_act(f"poison{i}", 64, d) + np.float32(3.0))
+        keys.append(t)
+        mmq.mmq_quant_f32(ctx, t, 64, d)
+    mmq.mmq_cache_clear(ctx)
+    xh = synth.activations(synth.rng_for("test", 0, "padrms"), 37, d)
+    wh = synth.rms_weight(synth.rng_for("test", 1, "padrms"), d)
+    y = torch.empty((37, d), dtype=torch.float32, device="cuda")
+    mmq.mmq_quant_rms(ctx, dev_tensor(xh), dev_tensor(wh), y, 37, d, EPS, 0)
+    q, D, S = export_plane(ctx, y, 37, d, include_pad=True)
+    assert q.shape[0] == 64
+    assert not q[37:].any() and not D[37:].any() and not S[37:].any()
+    assert q[:37].any()
+
+
+# ------------------------------------------------------------------ matmuls
+def _gemm_case(ctx, wtype, n, od, id_, tag):
+    rng = synth.rng_for("test", n * 7 + od, f"{tag}{wtype}{id_}")
+    raw = synth.weights(wtype, rng, od, id_)
+    ah = _act(tag, n, id_)
+    w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw, 1)
+    a = dev_tensor(ah)
+    out = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
+    fn = mmq.mmq_gemm_q4k if wtype == "q4_K" else mmq.mmq_gemm_q6k
+    fn(ctx, w, a, n, out)
+    torch.cuda.synchronize()
+    plane = export_plane(ctx, a, n, id_)
+    return w, raw, plane, out.cpu().numpy()
+
+
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("n,od,id_", [(1, 128, 256), (37, 256, 512), (200, 384, 1024),
+                                      (130, 1000, 768), (16, 32, 2304)])
+def test_gemm_parity(ctx, wtype, n, od, id_):
+    w, raw, (q, D, S), got = _gemm_case(ctx, wtype, n, od, id_, "gemm")
+    ref = oracle.gemm(wtype, q, D, S, raw, od, id_)
+    assert_gemm_close(got, ref, f"{wtype} n={n} od={od} id={id_}")
+    mmq.mmq_weight_free(w)
+
+
+@pytest.mark.parametrize("wtype,od,id_", [("q4_K", 18944, 3584), ("q6_K", 3584, 18944),
+                                          ("q4_K", 512, 3584), ("q6_K", 512, 3584)])
+def test_gemm_full_size_sampled(ctx, wtype, od, id_):
+    n = 3314
+    w, raw, (q, D, S), got = _gemm_case(ctx, wtype, n, od, id_, "full")
+    rng = np.random.default_rng(od + id_)
+    tok = np.unique(np.concatenate([[0, 1, 31, 32, 127, 128, 3199, 3200, 3313],
+                                    rng.integers(0, n, 7)]))
+    outs = np.unique(np.concatenate([[0, 31, 32, 127, 128, od - 1],
+                                     rng.integers(0, od, 250)]))
+    ref = oracle.gemm(wtype, q, D, S, raw, od, id_, tok=tok, outs=outs)
+    assert_gemm_close(got[np.ix_(tok, outs)], ref, f"{wtype} {od}x{id_} sampled")
+    assert np.isfinite(got).all()
+    mmq.mmq_weight_free(w)
+
+
+# ------------------------------------------------------------------ one-token GEMV
+@pytest.mark.parametrize("od,id_", [(1000, 5120), (64, 256), (300, 13824), (33, 20480),
+                                    (1024, 5120)])
+def test_mmvq_parity(ctx, od, id_):
+    rng = synth.rng_for("test", od, f"mmvq{id_}")
+    raw = synth.q6k_weights(rng, od, id_)
+    w = mmq.mmq_register_weight(ctx, 14, od, id_, raw, 2)
+    ah = _act("mmvq", 1, id_)
+    a = dev_tensor(ah)
+    out = torch.full((od,), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmvq_q6k(ctx, w, a, out)
+    q, D, S = export_plane(ctx, a, 1, id_)
+    ref = oracle.gemm("q6_K", q, D, S, raw, od, id_)[0]
+    assert_gemm_close(out.cpu().numpy(), ref, f"mmvq {od}x{id_}")
+    mmq.mmq_weight_free(w)
+
+
+def test_mmvq_decode_chain_full_size(ctx):
+    """14B decode: rms(5120) plane shared by attn_v and lm_head (hits), SwiGLU(13824)
+    plane feeding ffn_down; lm_head checked on sampled rows."""
+    c = mmq.mmq_create(0, 0)
+    try:
+        rng = synth.rng_for("decode14b", 0, "x")
+        xh = synth.activations(rng, 1, 5120)
+        wn = synth.rms_weight(synth.rng_for("decode14b", 0, "norm"), 5120)
+        gh = synth.activations(synth.rng_for("decode14b", 0, "gate"), 1, 13824)
+        uh = synth.activations(synth.rng_for("decode14b", 0, "up"), 1, 13824)
+        shapes = {"attn_v": (1024, 5120), "lm_head": (152064, 5120), "ffn_down": (5120, 13824)}
+        raws, ws = {}, {}
+        for k, (od, id_) in shapes.items():
+            raws[k] = synth.q6k_weights(synth.rng_for("decode14b", 0, k), od, id_)
+            ws[k] = mmq.mmq_register_weight(c, 14, od, id_, raws[k], 2)
+        y = torch.empty((1, 5120), dtype=torch.float32, device="cuda")
+        y2 = torch.empty((1, 13824), dtype=torch.float32, device="cuda")
+        outs = {k: torch.empty((od,), dtype=torch.float32, device="cuda") for k, (od, _) in shapes.items()}
+        mmq.mmq_quant_rms(c, dev_tensor(xh), dev_tensor(wn), y, 1, 5120, EPS, 0)
+        mmq.mmvq_q6k(c, ws["attn_v"], y, outs["attn_v"])
+        mmq.mmvq_q6k(c, ws["lm_head"], y, outs["lm_head"])
+        mmq.mmq_quant_swiglu(c, dev_tensor(gh), dev_tensor(uh), y2, 1, 13824, 0)
+        mmq.mmvq_q6k(c, ws["ffn_down"], y2, outs["ffn_down"])
+        st = mmq.mmq_stats(c)
+        assert st["cache_hits"] == 3 and st["cache_misses"] == 0 and st["launches_quant_f32"] == 0
+        p1 = export_plane(c, y, 1, 5120)
+        p2 = export_plane(c, y2, 1, 13824)
+        assert_fused_close(p1, oracle.quantize(oracle.rmsnorm(xh, wn, EPS)), what="decode rms")
+        for k, (od, id_) in shapes.items():
+            q, D, S = p1 if id_ == 5120 else p2
+            rows = None if od <= 8192 else np.unique(np.concatenate(
+                [[0, od - 1], np.random.default_rng(5).integers(0, od, 2000)]))
+            ref = oracle.gemm("q6_K", q, D, S, raws[k], od, id_, outs=rows)[0]
+            got = outs[k].cpu().numpy()
+            assert_gemm_close(got if rows is None else got[rows], ref, k)
+        for wt in ws.values():
+            mmq.mmq_weight_free(wt)
+    finally:
+        mmq.mmq_destroy(c)
+
+
+# ------------------------------------------------------------------ cache semantics on the device
+def test_attention_projection_cache_counts():
+    """rms plane shared by q, k, v (three hits); o misses and quantises its
+    input once; outputs match the oracle on the shared plane."""
+    c = mmq.mmq_create(0, 0)
+    try:
+        n, d = 300, 3584
+        xh = synth.activations(synth.rng_for("attn", 0, "x"), n, d)
+        wn = synth.rms_weight(synth.rng_for("attn", 0, "norm"), d)
+        ah = synth.activations(synth.rng_for("attn", 0, "attn_out"), n, d)
+        specs = {"q": ("q4_K", 3584), "k": ("q4_K", 512), "v": ("q6_K", 512), "o": ("q4_K", 3584)}
+        raws = {k: synth.weights(t, synth.rng_for("attn", 0, k), od, d) for k, (t, od) in specs.items()}
+        ws = {k: mmq.mmq_register_weight(c, WT[t], od, d, raws[k], 1) for k, (t, od) in specs.items()}
+        y = torch.empty((n, d), dtype=torch.float32, device="cuda")
+        a = dev_tensor(ah)
+        outs = {k: torch.empty((n, od), dtype=torch.float32, device="cuda") for k, (t, od) in specs.items()}
+        mmq.mmq_quant_rms(c, dev_tensor(xh), dev_tensor(wn), y, n, d, EPS, 0)
+        for k in ("q", "k", "v"):
+            fn = mmq.mmq_gemm_q4k if specs[k][0] == "q4_K" else mmq.mmq_gemm_q6k
+            fn(c, ws[k], y, n, outs[k])
+        mmq.mmq_gemm_q4k(c, ws["o"], a, n, outs["o"])
+        st = mmq.mmq_stats(c)
+        assert (st["cache_hits"], st["cache_misses"], st["launches_quant_rms"],
+                st["launches_quant_f32"]) == (3, 1, 1, 1)
+        py = export_plane(c, y, n, d)
+        pa = export_plane(c, a, n, d)
+        for k, (t, od) in specs.items():
+            q, D, S = pa if k == "o" else py
+            ref = oracle.gemm(t, q, D, S, raws[k], od, d, tok=np.arange(0, n, 7))
+            assert_gemm_close(outs[k].cpu().numpy()[::7], ref, k)
+        # the o input plane is exactly the oracle's quantisation of it
+        assert_plane_equal(pa, oracle.quantize(ah), "o input")
+        for wt in ws.values():
+            mmq.mmq_weight_free(wt)
+    finally:
+        mmq.mmq_destroy(c)
+
+
+def test_dead_write_refusal_launches_nothing():
+    c = mmq.mmq_create(0, 0)
+    try:
+        n, d = 40, 512
+        raw = synth.q4k_weights(synth.rng_for("dead", 0, "w"), 128, d)
+        w = mmq.mmq_register_weight(c, 12, 128, d, raw, 1)
+        x = dev_tensor(synth.activations(synth.rng_for("dead", 0, "x"), n, d))
+        wn = dev_tensor(synth.rms_weight(synth.rng_for("dead", 0, "n"), d))
+        y = torch.empty((n, d), dtype=torch.float32, device="cuda")
+        out = torch.empty((n, 128), dtype=torch.float32, device="cuda")
+        mmq.mmq_quant_rms(c, x, wn, y, n, d, EPS, 0)
+        before = mmq.mmq_stats(c)
+        with pytest.raises(mmq.MmqError) as e1:
+            mmq.mmq_quant_f32(c, y, n, d)
+        with pytest.raises(mmq.MmqError) as e2:
+            mmq.mmq_gemm_q4k(c, w, y, n - 1, out)      # different n: a miss on a dead buffer
+        assert e1.value.status == mmq.MMQ_E_DEAD_WRITE == e2.value.status
+        after = mmq.mmq_stats(c)
+        assert after["cache_refusals"] == before["cache_refusals"] + 2
+        for k in ("launches_quant_f32", "launches_gemm_q4k", "launches_quant_rms"):
+            assert after[k] == before[k]
+        mmq.mmq_gemm_q4k(c, w, y, n, out)             # the recorded plane still serves
+        mmq.mmq_cache_clear(c)                        # window boundary: y is no longer dead
+        y.zero_()
+        mmq.mmq_quant_f32(c, y, n, d)
+        mmq.mmq_weight_free(w)
+    finally:
+        mmq.mmq_destroy(c)
