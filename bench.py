@@ -1,0 +1,334 @@
+"""Benchmark: the 7B prefill matmul chain (one step = all 28 layers) on one MI355X.
+
+One step runs, for each of 28 layers at 3314 tokens (hidden 3584, ffn 18944):
+  RMSNorm -> q8 plane (skip-write) -> q (q4_K 3584x3584), k (q4_K 512x3584),
+  v (q6_K 512x3584), all three reading the one cached plane;
+  standalone quantise of the attention output -> o (q4_K 3584x3584);
+  RMSNorm -> plane (skip-write) -> gate, up (q4_K 18944x3584);
+  SwiGLU(gate, up) -> plane (skip-write) -> down (q6_K 3584x18944);
+then one cache clear (the execution-window boundary).  Every layer has its own
+seeded synthetic weights and N(0,1) inputs, resident in HBM before timing.
+
+Printed (one JSON line): MMQ chain TOPS (value), tok/s-equivalent, per-kernel-
+class times from HIP events over the timed region, the roofline of the
+dominant kernel (the q4_K matmul), the one-token q6_K GEMV bandwidth at the
+14B decode shapes (weights rotated so they stream from HBM, not the 256 MB
+last-level cache), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HIDDEN, FFN, KV, TOKENS, LAYERS = 3584, 18944, 512, 3314, 28
+PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 MFMA
+PEAK_F16_TOPS = 2500.0           # MI355X dense f16 MFMA (the instruction the matmul issues)
+PEAK_HBM_GBS = 8000.0
+
+# (name, weight type, od, id, input) per layer, in chain order
+LAYER_GEMMS = [("q", "q4_K", HIDDEN, HIDDEN, "attn_norm"), ("k", "q4_K", KV, HIDDEN, "attn_norm"),
+               ("v", "q6_K", KV, HIDDEN, "attn_norm"), ("o", "q4_K", HIDDEN, HIDDEN, "attn_out"),
+               ("gate", "q4_K", FFN, HIDDEN, "ffn_norm"), ("up", "q4_K", FFN, HIDDEN, "ffn_norm"),
+               ("down", "q6_K", HIDDEN, FFN, "swiglu")]
+
+
+def chain_ops(tokens=TOKENS, layers=LAYERS):
+    return 2 * tokens * layers * sum(od * id_ for _, _, od, id_, _ in LAYER_GEMMS)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--layers", type=int, default=LAYERS, help=argparse.SUPPRESS)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Chain:
+    def __init__(self, mmq, torch, synth, layers):
+        self.mmq, self.torch = mmq, torch
+        self.ctx = mmq.mmq_create(0, 0)
+        self.layers = []
+        dev = "cuda"
+        for l in range(layers):
+            L = {}
+            for name, wt, od, id_, _ in LAYER_GEMMS:
+                raw = synth.weights(wt, synth.rng_for("chain7b", l, name), od, id_)
+                code = mmq.MMQ_Q4_K if wt == "q4_K" else mmq.MMQ_Q6_K
+                L[name] = mmq.mmq_register_weight(self.ctx, code, od, id_, raw, mmq.MMQ_USE_GEMM)
+                del raw
+            for t in ("x_attn", "attn_out", "x_ffn"):
+                L[t] = torch.from_numpy(synth.activations(synth.rng_for("chain7b", l, t), TOKENS,
+                                                          HIDDEN)).to(dev)
+            for t in ("norm_attn", "norm_ffn"):
+                L[t] = torch.from_numpy(synth.rms_weight(synth.rng_for("chain7b", l, t), HIDDEN)).to(dev)
+            self.layers.append(L)
+            if l % 7 == 6:
+                log(f"registered layer {l + 1}/{layers}")
+        e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+        # producer output buffers: allocated (they are the plane keys) but never written
+        self.y_attn, self.y_ffn, self.y_sw = e(TOKENS, HIDDEN), e(TOKENS, HIDDEN), e(TOKENS, FFN)
+        self.out = {name: e(TOKENS, od) for name, _, od, _, _ in LAYER_GEMMS}
+        self.events = None
+
+    def _ev(self, cls):
+        if self.events is None:
+            return None
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
+        self.events.setdefault(cls, []).append((a, b))
+        return b
+
+    def _run(self, cls, fn, *args):
+        end = self._ev(cls)
+        fn(*args)
+        if end is not None:
+            end.record()
+
+    def step(self):
+        m, c, n = self.mmq, self.ctx, TOKENS
+        for L in self.layers:
+            self._run("quant_rms", m.mmq_quant_rms, c, L["x_attn"], L["norm_attn"], self.y_attn, n,
+                      HIDDEN, 1e-6, 0)
+            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["q"], self.y_attn, n, self.out["q"])
+            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["k"], self.y_attn, n, self.out["k"])
+            self._run("gemm_q6k", m.mmq_gemm_q6k, c, L["v"], self.y_attn, n, self.out["v"])
+            self._run("quant_f32", m.mmq_quant_f32, c, L["attn_out"], n, HIDDEN)
+            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["o"], L["attn_out"], n, self.out["o"])
+            self._run("quant_rms", m.mmq_quant_rms, c, L["x_ffn"], L["norm_ffn"], self.y_ffn, n,
+                      HIDDEN, 1e-6, 0)
+            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["gate"], self.y_ffn, n, self.out["gate"])
+            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["up"], self.y_ffn, n, self.out["up"])
+            self._run("quant_swiglu", m.mmq_quant_swiglu, c, self.out["gate"], self.out["up"],
+                      self.y_sw, n, FFN, 0)
+            self._run("gemm_q6k", m.mmq_gemm_q6k, c, L["down"], self.y_sw, n, self.out["down"])
+        m.mmq_cache_clear(c)
+
+    def class_times_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) for k, v in self.events.items()}, \
+               {k: len(v) for k, v in self.events.items()}
+
+
+def decode_gemv(mmq, torch, synth):
+    """One-token q6_K GEMV at the 14B decode shapes, weights streamed cold."""
+    ctx = mmq.mmq_create(0, 0)
+    shapes = {"attn_v": (1024, 5120, 64), "ffn_down": (5120, 13824, 8), "lm_head": (152064, 5120, 2)}
+    res = {}
+    try:
+        y5 = torch.empty((1, 5120), dtype=torch.float32, device="cuda")
+        y13 = torch.empty((1, 13824), dtype=torch.float32, device="cuda")
+        x = torch.from_numpy(synth.activations(synth.rng_for("decode14b", 0, "x"), 1, 5120)).cuda()
+        wn = torch.from_numpy(synth.rms_weight(synth.rng_for("decode14b", 0, "norm"), 5120)).cuda()
+        g = torch.from_numpy(synth.activations(synth.rng_for("decode14b", 0, "gate"), 1, 13824)).cuda()
+        u = torch.from_numpy(synth.activations(synth.rng_for("decode14b", 0, "up"), 1, 13824)).cuda()
+        tot_b, tot_t = 0.0, 0.0
+        for name, (od, id_, copies) in shapes.items():
+            raw = synth.q6k_weights(synth.rng_for("decode14b", 0, name), od, id_)
+            ws = [mmq.mmq_register_weight(ctx, mmq.MMQ_Q6_K, od, id_, raw, mmq.MMQ_USE_GEMV)
+                  for _ in range(copies)]
+            del raw
+            out = torch.empty((od,), dtype=torch.float32, device="cuda")
+            key = y5 if id_ == 5120 else y13
+            if id_ == 5120:
+                mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)
+            else:
+                mmq.mmq_quant_swiglu(ctx, g, u, y13, 1, 13824, 0)
+            reps = max(2 * copies, 16)
+            for i in range(copies):
+                mmq.mmvq_q6k(ctx, ws[i], key, out)
+            torch.cuda.synchronize()
+            evs = []
+            for i in range(reps):
+                a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+                a.record(); mmq.mmvq_q6k(ctx, ws[i % copies], key, out); b.record()
+                evs.append((a, b))
+            torch.cuda.synchronize()
+            t_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / reps
+            nbytes = od * id_ / 256 * 210 + id_ * 1.25 + od * 4
+            res[name] = {"od": od, "id": id_, "us": round(t_us, 3),
+                         "GB_s": round(nbytes / (t_us * 1e-6) / 1e9, 1)}
+            tot_b += nbytes; tot_t += t_us
+            for w in ws:
+                mmq.mmq_weight_free(w)
+        # decode producers (rms 5120, swiglu 13824) at n = 1
+        for name, fn in (("rms_5120", lambda: mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)),
+                         ("swiglu_13824", lambda: mmq.mmq_quant_swiglu(ctx, g, u, y13, 1, 13824, 0))):
+            fn(); torch.cuda.synchronize()
+            evs = []
+            for _ in range(50):
+                a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+                a.record(); fn(); b.record(); evs.append((a, b))
+            torch.cuda.synchronize()
+            res[name] = {"us": round(1e3 * sum(a.elapsed_time(b) for a, b in evs) / 50, 3)}
+        res["aggregate_GB_s"] = round(tot_b / (tot_t * 1e-6) / 1e9, 1)
+        res["aggregate_frac_hbm"] = round(res["aggregate_GB_s"] / PEAK_HBM_GBS, 4)
+    finally:
+        mmq.mmq_destroy(ctx)
+    return res
+
+
+def cpu_baseline(seconds: float):
+    """The CPU oracle (as it is) on a bounded sample of one layer of the chain:
+    producers and all seven matmuls for a growing number of tokens, run until
+    about `seconds` of CPU time; reported in the chain's unit (TOPS)."""
+    import oracle
+    import synth
+    t_used = 0.0
+    ops = 0
+    tok_done = 0
+    raws = {name: synth.weights(wt, synth.rng_for("chain7b", 0, name), od, id_)
+            for name, wt, od, id_, _ in LAYER_GEMMS}
+    x = synth.activations(synth.rng_for("chain7b", 0, "x_attn"), TOKENS, HIDDEN)
+    a = synth.activations(synth.rng_for("chain7b", 0, "attn_out"), TOKENS, HIDDEN)
+    h = synth.activations(synth.rng_for("chain7b", 0, "x_ffn"), TOKENS, HIDDEN)
+    n1 = synth.rms_weight(synth.rng_for("chain7b", 0, "norm_attn"), HIDDEN)
+    n2 = synth.rms_weight(synth.rng_for("chain7b", 0, "norm_ffn"), HIDDEN)
+    chunk = 4
+    while t_used < seconds and tok_done + chunk <= TOKENS:
+        sl = slice(tok_done, tok_done + chunk)
+        t0 = time.perf_counter()
+        pa = oracle.quantize(oracle.rmsnorm(x[sl], n1, 1e-6))
+        po = oracle.quantize(a[sl])
+        pf = oracle.quantize(oracle.rmsnorm(h[sl], n2, 1e-6))
+        outs = {}
+        for name, wt, od, id_, src in LAYER_GEMMS:
+            if src == "swiglu":
+                continue
+            q, D, S = {"attn_norm": pa, "attn_out": po, "ffn_norm": pf}[src]
+            outs[name] = oracle.gemm(wt, q, D, S, raws[name], od, id_)
+        ps = oracle.quantize(oracle.swiglu(outs["gate"], outs["up"]))
+        oracle.gemm("q6_K", *ps, raws["down"], HIDDEN, FFN)
+        t_used += time.perf_counter() - t0
+        tok_done += chunk
+    ops = 2 * tok_done * sum(od * id_ for _, _, od, id_, _ in LAYER_GEMMS)
+    return {"value": round(ops / t_used / 1e12, 6), "unit": "TOPS", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"layer 0 of the chain (both RMSNorm producers, the standalone quantise, "
+                      f"SwiGLU and all 7 matmuls) for {tok_done} of {TOKENS} tokens, "
+                      f"{t_used:.1f} s; the work is linear in tokens",
+            "cpu_model": _cpu_model(), "seconds": round(t_used, 2)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path is data-parallel over tokens and needs no "
+              f"collective; --gpus {args.gpus} is not supported (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    from quantized_matmul_rmsnorm_amd import build as _b
+    if not os.path.exists(_b.LIB):
+        _b.build()
+    import quantized_matmul_rmsnorm_amd as mmq
+    import synth
+
+    t_setup = time.perf_counter()
+    chain = Chain(mmq, torch, synth, args.layers)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s")
+    for _ in range(args.warmup):
+        chain.step()
+    torch.cuda.synchronize()
+    st0 = mmq.mmq_stats(chain.ctx)
+    chain.events = {}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        chain.step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    cls_ms, cls_n = chain.class_times_ms()
+    st1 = mmq.mmq_stats(chain.ctx)
+    ops = chain_ops(TOKENS, args.layers)
+    tops = ops / (ms_step * 1e-3) / 1e12
+    log(f"{ms_step:.2f} ms/step ({wall / args.steps * 1e3:.2f} ms wall), {tops:.1f} TOPS")
+
+    q4_ops_launch = 2 * TOKENS * sum(od * id_ for _, wt, od, id_, _ in LAYER_GEMMS if wt == "q4_K") / 5
+    q4_avg_us = 1e3 * cls_ms["gemm_q4k"] / cls_n["gemm_q4k"]
+    achieved = q4_ops_launch / (q4_avg_us * 1e-6) / 1e12
+    q6_ops_launch = 2 * TOKENS * sum(od * id_ for _, wt, od, id_, _ in LAYER_GEMMS if wt == "q6_K") / 2
+    q6_avg_us = 1e3 * cls_ms["gemm_q6k"] / cls_n["gemm_q6k"]
+
+    kernels = {}
+    for k in cls_ms:
+        kernels[k] = {"launches": cls_n[k], "avg_us": round(1e3 * cls_ms[k] / cls_n[k], 2),
+                      "share": round(cls_ms[k] / (ms_step * args.steps), 4)}
+    # producers are HBM-bound: algorithmic bytes per launch
+    rms_b = TOKENS * HIDDEN * (4 + 1.25) + HIDDEN * 4
+    sw_b = TOKENS * FFN * (8 + 1.25)
+    qf_b = TOKENS * HIDDEN * (4 + 1.25)
+    for k, b in (("quant_rms", rms_b), ("quant_swiglu", sw_b), ("quant_f32", qf_b)):
+        kernels[k]["GB_s"] = round(b / (kernels[k]["avg_us"] * 1e-6) / 1e9, 1)
+    kernels["gemm_q4k"]["TOPS"] = round(achieved, 1)
+    kernels["gemm_q6k"]["TOPS"] = round(q6_ops_launch / (q6_avg_us * 1e-6) / 1e12, 1)
+
+    decode = None if args.no_decode else decode_gemv(mmq, torch, synth)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+
+    rec = {
+        "metric": "MMQ chain TOPS + tok/s-equiv at 7B pp3314; q6_K decode GEMV GB/s",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "7B prefill matmul chain: 28 layers x (RMSNorm->q8 plane->q,k,v; "
+                               "quantise->o; RMSNorm->gate,up; SwiGLU->down), skip-write planes",
+                   "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN, "kv": KV, "layers": args.layers,
+                   "weights": "q4_K (q,k,o,gate,up), q6_K (v,down)"},
+        "tok_s_equiv": round(TOKENS / (ms_step * 1e-3), 1),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": None, "kernel": "k_gemm<q4_K>",
+                     "ops_per_launch": q4_ops_launch, "avg_launch_us": round(q4_avg_us, 2),
+                     "frac_of_f16_mfma_peak": round(achieved / PEAK_F16_TOPS, 4)},
+        "kernels": kernels,
+        "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
+        "decode_gemv": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -138,6 +138,21 @@ int refuse_dead(mmq_ctx* c, const char* who, const void* p) {
                 who, p);
 }
 
+// Remove [p, p + bytes) from every dead range (ranges are split if needed).
+void revive(mmq_ctx* c, const void* p, int64_t bytes) {
+    const uintptr_t lo = (uintptr_t)p, hi = lo + (uintptr_t)bytes;
+    std::vector<DeadRange> keep;
+    for (const DeadRange& r : c->dead) {
+        if (hi <= r.lo || r.hi <= lo) {
+            keep.push_back(r);
+            continue;
+        }
+        if (r.lo < lo) keep.push_back({r.lo, lo});
+        if (hi < r.hi) keep.push_back({hi, r.hi});
+    }
+    c->dead.swap(keep);
+}
+
 int find_entry(const mmq_ctx* c, const void* key, int64_t n, int64_t d) {
     for (int i = 0; i < kSlots; ++i) {
         const Entry& e = c->entries[i];
@@ -252,15 +267,7 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
     // The producer replaces whatever was cached for bytes it (re)defines.
     if (kind != kProdF32) {
         drop_overlapping(c, y, bytes);
-        if (write_y) {
-            // a real write makes previously dead bytes inside y valid again
-            c->dead.erase(std::remove_if(c->dead.begin(), c->dead.end(),
-                                         [&](const DeadRange& r) {
-                                             return r.lo >= (uintptr_t)y &&
-                                                    r.hi <= (uintptr_t)y + (uintptr_t)bytes;
-                                         }),
-                          c->dead.end());
-        }
+        if (write_y) revive(c, y, bytes);  // a real write makes these bytes valid again
     } else {
         drop_overlapping(c, a, bytes);
     }

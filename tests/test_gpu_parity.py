@@ -20,10 +20,18 @@ WT = {"q4_K": 12, "q6_K": 14}
 
 
 @pytest.fixture(scope="module")
-def ctx():
+def _module_ctx():
     c = mmq.mmq_create(0, 0)
     yield c
     mmq.mmq_destroy(c)
+
+
+@pytest.fixture
+def ctx(_module_ctx):
+    # each test is its own execution window: buffers freed by an earlier test
+    # may come back at the same addresses
+    mmq.mmq_cache_clear(_module_ctx)
+    return _module_ctx
 
 
 def _act(tag, n, d, spread=True):
