@@ -1,0 +1,208 @@
+"""CPU tests of the C ABI: every declared symbol is exported, and the host logic
+(argument/shape/type validation, plane cache, dead-key refusal, statistics,
+scratch cap) behaves as include/mmq.h states.  Uses MMQ_CTX_DRYRUN contexts:
+bookkeeping runs, nothing touches a device (pointers are plain integers).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import quantized_matmul_rmsnorm_amd as mmq
+from quantized_matmul_rmsnorm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mmq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mmq\w+|mmvq\w+)\s*\(", text)))
+
+
+def test_header_declares_the_exported_list():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    dyn = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in dyn, name
+        assert getattr(ctypes.CDLL(_lib.LIB_PATH), name) is not None
+
+
+def test_no_device_is_reported():
+    with pytest.raises(mmq.MmqError) as e:
+        mmq.mmq_create(999, 0)
+    assert e.value.status == mmq.MMQ_E_DEVICE
+    with pytest.raises(mmq.MmqError) as e:
+        mmq.mmq_create(0, 0x100)
+    assert e.value.status == mmq.MMQ_E_ARG
+
+
+@pytest.fixture
+def ctx():
+    c = mmq.mmq_create(0, mmq.MMQ_CTX_DRYRUN)
+    yield c
+    mmq.mmq_destroy(c)
+
+
+def _w(ctx, wtype=mmq.MMQ_Q4_K, rows=512, cols=256, uses=0):
+    bpb = 144 if wtype == mmq.MMQ_Q4_K else 210
+    raw = np.zeros(rows * cols // 256 * bpb, np.uint8)
+    return mmq.mmq_register_weight(ctx, wtype, rows, cols, raw, uses)
+
+
+def _status(fn, *a):
+    try:
+        fn(*a)
+    except mmq.MmqError as e:
+        return e.status
+    return mmq.MMQ_OK
+
+
+def test_plane_rows():
+    assert [mmq.mmq_plane_rows(n) for n in (0, 1, 31, 32, 33, 3314)] == [0, 32, 32, 32, 64, 3328]
+
+
+def test_shape_and_argument_validation(ctx):
+    X, W, Y = 0x10000, 0x20000, 0x30000
+    assert _status(mmq.mmq_quant_rms, ctx, X, W, Y, 4, 300, 1e-6, 0) == mmq.MMQ_E_SHAPE
+    assert _status(mmq.mmq_quant_rms, ctx, X, W, Y, 0, 256, 1e-6, 0) == mmq.MMQ_E_SHAPE
+    assert _status(mmq.mmq_quant_rms, ctx, X + 4, W, Y, 4, 256, 1e-6, 0) == mmq.MMQ_E_ARG
+    assert _status(mmq.mmq_quant_swiglu, ctx, X, 0, Y, 4, 256, 0) == mmq.MMQ_E_ARG
+    assert _status(mmq.mmq_quant_f32, ctx, 0, 4, 256) == mmq.MMQ_E_ARG
+    st = mmq.mmq_stats(ctx)
+    assert st["launches_quant_rms"] == st["launches_quant_swiglu"] == st["launches_quant_f32"] == 0
+
+
+def test_registration_validation(ctx):
+    raw = np.zeros(144 * 4, np.uint8)
+    assert _status(mmq.mmq_register_weight, ctx, 13, 4, 256, raw) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 300, raw) == mmq.MMQ_E_SHAPE
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 0, 256, raw) == mmq.MMQ_E_SHAPE
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw,
+                   mmq.MMQ_USE_GEMV) == mmq.MMQ_E_TYPE
+    w4 = _w(ctx, mmq.MMQ_Q4_K, 512, 256)
+    w6 = _w(ctx, mmq.MMQ_Q6_K, 1000, 512)
+    # q4_K: f16 tiles (2 B/weight) + scales + mins; q6_K adds the GEMV layout
+    assert mmq.mmq_weight_bytes(w4) == 512 * 256 * 2 + 16 * 1 * 64 * 4 + 16 * 1 * 512 * 2
+    rows_pad = 1024
+    gemm6 = rows_pad * 512 * 4 + (rows_pad // 32) * 2 * 32 * 4
+    gemv6 = 1000 * 16 * (16 + 8 + 2) + 1000 * 2 * 4
+    assert mmq.mmq_weight_bytes(w6) == gemm6 + gemv6
+    assert mmq.mmq_stats(ctx)["weight_bytes"] == mmq.mmq_weight_bytes(w4) + mmq.mmq_weight_bytes(w6)
+    mmq.mmq_weight_free(w4)
+    assert mmq.mmq_stats(ctx)["weight_bytes"] == mmq.mmq_weight_bytes(w6)
+    mmq.mmq_weight_free(w6)
+
+
+def test_consumer_type_checks(ctx):
+    w4 = _w(ctx, mmq.MMQ_Q4_K, 512, 256)
+    w6g = _w(ctx, mmq.MMQ_Q6_K, 64, 256, mmq.MMQ_USE_GEMM)
+    A, O = 0x100000, 0x200000
+    assert _status(mmq.mmq_gemm_q6k, ctx, w4, A, 8, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmq_gemm_q4k, ctx, w6g, A, 8, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmvq_q6k, ctx, w6g, A, O) == mmq.MMQ_E_TYPE     # not registered for GEMV
+    assert _status(mmq.mmq_gemm_q4k, ctx, w4, A, 0, O) == mmq.MMQ_E_SHAPE
+    other = mmq.mmq_create(0, mmq.MMQ_CTX_DRYRUN)
+    try:
+        assert _status(mmq.mmq_gemm_q4k, other, w4, A, 8, O) == mmq.MMQ_E_ARG
+    finally:
+        mmq.mmq_destroy(other)
+
+
+def test_attention_chain_counts(ctx):
+    """rms plane shared by q, k, v (3 hits); o's input misses once, then hits."""
+    wq, wk = _w(ctx, mmq.MMQ_Q4_K, 512, 256), _w(ctx, mmq.MMQ_Q4_K, 128, 256)
+    wv = _w(ctx, mmq.MMQ_Q6_K, 128, 256)
+    X, W, Y, ATT, OUT = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    mmq.mmq_quant_rms(ctx, X, W, Y, 40, 256, 1e-6, 0)
+    mmq.mmq_gemm_q4k(ctx, wq, Y, 40, OUT)
+    mmq.mmq_gemm_q4k(ctx, wk, Y, 40, OUT)
+    mmq.mmq_gemm_q6k(ctx, wv, Y, 40, OUT)
+    mmq.mmq_gemm_q4k(ctx, wq, ATT, 40, OUT)
+    mmq.mmq_gemm_q4k(ctx, wq, ATT, 40, OUT)
+    st = mmq.mmq_stats(ctx)
+    assert (st["cache_hits"], st["cache_misses"], st["launches_quant_rms"],
+            st["launches_quant_f32"], st["launches_gemm_q4k"], st["launches_gemm_q6k"]) == (4, 1, 1, 1, 4, 1)
+    assert st["cache_entries"] == 2
+    mmq.mmq_cache_clear(ctx)
+    assert mmq.mmq_stats(ctx)["cache_entries"] == 0
+
+
+def test_dead_write_refusal_and_revival(ctx, capfd):
+    w = _w(ctx, mmq.MMQ_Q4_K, 128, 256)
+    Y = 0x1000000
+    n, d = 100, 256
+    mmq.mmq_quant_swiglu(ctx, 0x10000, 0x20000, Y, n, d, 0)          # dead [Y, Y + 102400)
+    before = mmq.mmq_stats(ctx)
+    assert _status(mmq.mmq_quant_f32, ctx, Y, n, d) == mmq.MMQ_E_DEAD_WRITE
+    assert _status(mmq.mmq_quant_f32, ctx, Y + 4096, 10, d) == mmq.MMQ_E_DEAD_WRITE
+    assert _status(mmq.mmq_gemm_q4k, ctx, w, Y, n - 1, 0x9000000) == mmq.MMQ_E_DEAD_WRITE
+    mmq.mmq_gemm_q4k(ctx, w, Y, n, 0x9000000)                          # the recorded plane serves
+    after = mmq.mmq_stats(ctx)
+    assert after["cache_refusals"] - before["cache_refusals"] == 3
+    assert after["launches_quant_f32"] == before["launches_quant_f32"]
+    assert after["launches_gemm_q4k"] == before["launches_gemm_q4k"] + 1
+    assert "refused" in capfd.readouterr().err
+    # a real write into the middle revives exactly those bytes
+    mid = Y + 40 * d * 4
+    mmq.mmq_quant_rms(ctx, 0x10000, 0x20000, mid, 10, d, 1e-6, 1)
+    assert _status(mmq.mmq_quant_f32, ctx, mid, 10, d) == mmq.MMQ_OK
+    assert _status(mmq.mmq_quant_f32, ctx, mid - 1024, 1, d) == mmq.MMQ_E_DEAD_WRITE
+    assert _status(mmq.mmq_quant_f32, ctx, mid + 10 * d * 4, 1, d) == mmq.MMQ_E_DEAD_WRITE
+    # invalidate drops the dead range that starts at the key; clear drops all
+    mmq.mmq_cache_invalidate(ctx, Y)
+    assert _status(mmq.mmq_quant_f32, ctx, Y, 1, d) == mmq.MMQ_OK
+    mmq.mmq_quant_swiglu(ctx, 0x10000, 0x20000, Y, n, d, 0)
+    mmq.mmq_cache_clear(ctx)
+    assert _status(mmq.mmq_quant_f32, ctx, Y, n, d) == mmq.MMQ_OK
+
+
+def test_lru_eviction_keeps_recent_entries(ctx):
+    w = _w(ctx, mmq.MMQ_Q4_K, 128, 256)
+    keys = [0x1000000 * (i + 1) for i in range(10)]
+    for k in keys:
+        mmq.mmq_quant_f32(ctx, k, 8, 256)
+    assert mmq.mmq_stats(ctx)["cache_entries"] == 8
+    h0 = mmq.mmq_stats(ctx)["cache_hits"]
+    mmq.mmq_gemm_q4k(ctx, w, keys[-1], 8, 0x9000000)    # recent: hit
+    assert mmq.mmq_stats(ctx)["cache_hits"] == h0 + 1
+    m0 = mmq.mmq_stats(ctx)["cache_misses"]
+    mmq.mmq_gemm_q4k(ctx, w, keys[0], 8, 0x9000000)     # evicted: miss, re-quantised
+    assert mmq.mmq_stats(ctx)["cache_misses"] == m0 + 1
+
+
+def test_producer_replaces_stale_overlapping_entries(ctx):
+    w = _w(ctx, mmq.MMQ_Q4_K, 128, 256)
+    Y = 0x1000000
+    mmq.mmq_quant_rms(ctx, 0x10000, 0x20000, Y, 64, 256, 1e-6, 1)
+    mmq.mmq_quant_f32(ctx, Y + 256 * 4, 8, 256)          # plane of a sub-range of y
+    mmq.mmq_quant_rms(ctx, 0x10000, 0x20000, Y, 64, 256, 1e-6, 1)   # y rewritten
+    m0 = mmq.mmq_stats(ctx)["cache_misses"]
+    mmq.mmq_gemm_q4k(ctx, w, Y + 256 * 4, 8, 0x9000000)  # stale sub-range plane was dropped
+    assert mmq.mmq_stats(ctx)["cache_misses"] == m0 + 1
+
+
+def test_scratch_cap(ctx):
+    mmq.mmq_set_scratch_cap(ctx, 64 * 1024)
+    assert _status(mmq.mmq_quant_f32, ctx, 0x100000, 32, 512) == mmq.MMQ_OK     # ~21 KB
+    assert _status(mmq.mmq_quant_f32, ctx, 0x200000, 1024, 512) == mmq.MMQ_E_OOM
+    st = mmq.mmq_stats(ctx)
+    assert st["plane_bytes"] <= 64 * 1024 and st["launches_quant_f32"] == 1
+    mmq.mmq_set_scratch_cap(ctx, -1)
+    assert _status(mmq.mmq_quant_f32, ctx, 0x200000, 1024, 512) == mmq.MMQ_OK
+
+
+def test_export_needs_a_plane_and_a_device(ctx):
+    assert _status(mmq.mmq_plane_export, ctx, 0x100000, 8, 256, 0, 0x1, 0x2, 0x3) == mmq.MMQ_E_ARG
+    mmq.mmq_quant_f32(ctx, 0x100000, 8, 256)
+    rc = _lib.lib.mmq_plane_export(ctx, 0x100000, 8, 256, 0, 0x1000, 0x2000, 0x3000, None)
+    assert rc == mmq.MMQ_E_DEVICE
