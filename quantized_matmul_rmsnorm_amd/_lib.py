@@ -64,6 +64,15 @@ class mmq_stats_t(ctypes.Structure):
 
 
 def _load():
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7 (same
+    # SONAME as the system one libmmq.so links against).  Loading torch first
+    # makes libmmq bind to torch's runtime, so tensors torch allocates and the
+    # kernels libmmq launches live in one runtime; the reverse order leaves
+    # torch on a runtime it was not built for ("No HIP GPUs are available").
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libmmq.so is not built ({LIB_PATH}); run "
                           "quantized_matmul_rmsnorm_amd.build.build() -- there is no fallback")

@@ -24,13 +24,17 @@
 // the q4_K min term sum_j (D*S)[t][j] * m_j is one extra MFMA per superblock
 // with m_j exact in f16 and D*S split into two f16 parts (22 significant bits).
 //
-// Tiling.  Workgroup of 8 waves computes 128 outputs x 128 tokens; wave w owns
-// output group w%4 (32 rows) and token groups 2*(w/4), 2*(w/4)+1 (2 x 32
-// tokens).  Per 32-block the workgroup stages the weight fragments (copied,
-// already in fragment order) and the 128 x 32 activation codes (converted
-// int8 -> f16 once) in LDS; the next block's global loads are issued before the
-// current block's MFMAs.  Plane rows beyond the plane's padded row count read
-// as zero; outputs are stored only for t < n and o < rows.
+// Tiling.  A workgroup of 8 waves computes 128 outputs x 128 tokens; wave w
+// owns output group w%4 (32 rows) and token groups 2*(w/4), 2*(w/4)+1.  Each
+// wave streams its own weight fragments (stored in MFMA fragment order at
+// registration) straight from L2 into a small register ring a few blocks
+// ahead; the activation codes of the tile are staged per 4-block chunk
+// through two LDS buffers, converted int8 -> f16 once per workgroup, and each
+// block's B fragments are read from LDS one block ahead.  All global reads use
+// raw buffer loads with 32-bit offsets; plane rows past the plane's padded
+// row count fall outside the buffer and read as zero.  Outputs are stored
+// only for t < n and o < rows.  Workgroups are mapped so that each XCD works
+// on a contiguous group of output x token tiles (shared L2).
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -82,22 +86,49 @@ __device__ __forceinline__ void tile_of(int n_ttiles, int n_otiles, int& t_tile,
     t_tile = r / go;
 }
 
-template <bool Q4K, int CH>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(
-    const half8* __restrict__ wa, const float* __restrict__ dmr,
-    const half8* __restrict__ mfrag, const int8_t* __restrict__ Q,
-    const float* __restrict__ Dp, const int32_t* __restrict__ Sp, int n, int plane_rows,
-    int id, int od, int n_ttiles, int n_otiles, float* __restrict__ out) {
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (sizeof(T) == 16)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    else if constexpr (sizeof(T) == 8)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+struct GemmArgs {
+    const half8* wa;      // weight fragments
+    const float* dmr;     // per (row group, superblock) scales
+    const half8* mfrag;   // q4_K mins
+    const int8_t* q;      // plane codes [plane_rows][id]
+    const float* D;       // plane scales [plane_rows][id/32]
+    const int32_t* S;     // plane sums  [plane_rows][id/32]
+    float* out;           // [n][od]
+    uint32_t wa_bytes, dmr_bytes, mfrag_bytes, q_bytes, ds_bytes;
+    int n, plane_rows, id, od, n_ttiles, n_otiles;
+};
+
+// The matmul kernel.  RA: depth of the weight-fragment register ring (the
+// prefetch distance is RA-1 blocks).
+template <bool Q4K>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     constexpr int NPART = Q4K ? 1 : 2;
-    constexpr int BPAD = 4;    // half8 of padding per B slot: keeps the 4 slots on distinct banks
-    constexpr int DPAD = 16;   // floats of padding per D slot
-    // Two LDS buffers of CH staged 32-blocks each (double buffering).
-    __shared__ half8 sA[2][CH][4][2][NPART][64];   // [buf][block][o group][k16][part][lane]
-    __shared__ half8 sB[2][CH][4 * 2 * 64 + BPAD]; // [buf][block][(t group, k16, lane)]
+    constexpr int CH = 4;                   // 32-blocks per staged activation chunk
+    constexpr int SBCH = 8 / CH;
+    constexpr int NDM = Q4K ? 2 : 1;
+    constexpr int RA = Q4K ? 4 : 2;         // weight-fragment ring depth (divides 8)
+    constexpr int PD = RA - 1;              // prefetch distance in blocks
+    constexpr int BPAD = 4, DPAD = 16;
+    __shared__ half8 sB[2][CH][4 * 2 * 64 + BPAD];
     __shared__ float sD[2][CH][128 + DPAD];
-    // q4_K: D*S of the current and the next superblock: [sb&1][t group][lane][block j],
-    // hi part in lanes < 32, lo part in lanes >= 32
     __shared__ __attribute__((aligned(16))) _Float16 sP[Q4K ? 2 : 1][4][64][8];
+    __shared__ __attribute__((aligned(16))) float sDM[2][4][NDM * 32];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -106,172 +137,154 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(
     const int th = wave >> 2;
 
     int t_tile, o_tile;
-    tile_of(n_ttiles, n_otiles, t_tile, o_tile);
-    const int64_t t0 = (int64_t)t_tile * 128;
-    const int64_t og0 = (int64_t)o_tile * 4;
-
+    tile_of(g.n_ttiles, g.n_otiles, t_tile, o_tile);
+    const int t0 = t_tile * 128;
+    const int og0 = o_tile * 4;
+    const int id = g.id;
     const int nb = id / kBlock;
     const int nsb = id / kSuper;
-    const int64_t K16 = id / 16;
-    const int nch = nb / CH;
+    const int K16 = id / 16;
 
-    // ---- staging assignment ----
-    // A: per block q4_K has 8 fragments (4 groups x 2 k16), q6_K 16 (x 2 parts);
-    //    thread tid copies fragment tid/64 (+ 8 for the second part) of each block.
-    const int fa = tid >> 6;
-    // B, D, S: CH == 4: thread -> token row tid/4, block tid%4 of the chunk (one
-    // 32-byte block); CH == 2: thread -> row tid/4, block (tid/2)%2, 16-byte half tid%2.
-    const int tb = tid >> 2;
-    const int jb = CH == 4 ? (tid & 3) : ((tid >> 1) & 1);
-    const int hb = CH == 4 ? -1 : (tid & 1);
-    const int64_t rowb = t0 + tb;
-    const bool rowb_ok = rowb < plane_rows;
-    const uint4* qrow = reinterpret_cast<const uint4*>(Q + rowb * (int64_t)id);
+    const auto rA = rsrc(g.wa, g.wa_bytes);
+    const auto rQ = rsrc(g.q, g.q_bytes);
+    const auto rD = rsrc(g.D, g.ds_bytes);
+    const auto rS = rsrc(g.S, g.ds_bytes);
+    const auto rM = rsrc(g.dmr, g.dmr_bytes);
+    const auto rF = rsrc(g.mfrag, g.mfrag_bytes);
 
-    half8 ra[CH][NPART];
-    uint4 rb0, rb1;
-    float rd;
-    int32_t rs;
-
-    auto load_chunk = [&](int c) {
+    // this wave's weight fragments: block b, k16, part at voffA + b * 2*NPART KiB
+    const uint32_t voffA = ((uint32_t)(og0 + ogl) * (uint32_t)K16 * NPART) * 1024u + (uint32_t)lane * 16u;
+    half8 ring[RA][2][NPART];
+    auto load_a = [&](int b, int slot) {
 #pragma unroll
-        for (int jj = 0; jj < CH; ++jj) {
-            const int b = c * CH + jj;
+        for (int k16 = 0; k16 < 2; ++k16)
 #pragma unroll
-            for (int p = 0; p < NPART; ++p) {
-                int64_t src;
-                if (Q4K) {
-                    const int g = fa >> 1, k16 = fa & 1;
-                    src = ((og0 + g) * K16 + 2 * b + k16) * 64 + lane;
-                } else {
-                    const int f = fa + 8 * p;           // 0..15 = g*4 + k16*2 + part
-                    const int g = f >> 2, k16 = (f >> 1) & 1, part = f & 1;
-                    src = (((og0 + g) * K16 + 2 * b + k16) * 2 + part) * 64 + lane;
-                }
-                ra[jj][p] = wa[src];
-            }
-        }
-        const int b = c * CH + jb;
-        if (rowb_ok) {
-            if (CH == 4) {
-                rb0 = qrow[2 * b];
-                rb1 = qrow[2 * b + 1];
-            } else {
-                rb0 = qrow[2 * b + hb];
-            }
-            rd = Dp[rowb * nb + b];
-            rs = Q4K ? Sp[rowb * nb + b] : 0;
-        } else {
-            rb0 = rb1 = make_uint4(0u, 0u, 0u, 0u);
-            rd = 0.0f;
-            rs = 0;
-        }
+            for (int p = 0; p < NPART; ++p)
+                ring[slot][k16][p] = bload<half8>(rA, voffA + (uint32_t)((k16 * NPART + p) * 1024),
+                                                  (uint32_t)b * (2u * NPART * 1024u));
     };
 
+    const int tb = tid >> 2;
+    const int jb = tid & 3;
+    const int rowb = t0 + tb;
+    const uint32_t rowq = rowb < g.plane_rows ? (uint32_t)rowb * (uint32_t)id : 0x80000000u;
+    const uint32_t rowd = rowb < g.plane_rows ? (uint32_t)(rowb * nb + jb) * 4u : 0x80000000u;
+    const int dm_g = tid / (NDM * 32), dm_i = tid % (NDM * 32);
+    const bool dm_thread = tid < 4 * NDM * 32;
+
+    uint4 rb0, rb1;
+    float rd, rdm = 0.0f;
+    int32_t rs;
+    auto load_chunk = [&](int c) {
+        const uint32_t sq = (uint32_t)(c * CH) * 32u;
+        rb0 = bload<uint4>(rQ, rowq + (uint32_t)jb * 32u, sq);
+        rb1 = bload<uint4>(rQ, rowq + (uint32_t)jb * 32u + 16u, sq);
+        rd = bload<float>(rD, rowd, (uint32_t)(c * CH) * 4u);
+        rs = Q4K ? bload<int32_t>(rS, rowd, (uint32_t)(c * CH) * 4u) : 0;
+        if ((c % SBCH) == 0 && dm_thread) {
+            const int sb = c / SBCH;
+            rdm = bload<float>(rM, (uint32_t)(((og0 + dm_g) * nsb + sb) * (NDM * 32 * 4) + dm_i * 4), 0u);
+        }
+    };
     auto store_chunk = [&](int c, int buf) {
-#pragma unroll
-        for (int jj = 0; jj < CH; ++jj) {
-#pragma unroll
-            for (int p = 0; p < NPART; ++p) {
-                if (Q4K) {
-                    sA[buf][jj][fa >> 1][fa & 1][0][lane] = ra[jj][p];
-                } else {
-                    const int f = fa + 8 * p;
-                    sA[buf][jj][f >> 2][(f >> 1) & 1][f & 1][lane] = ra[jj][p];
-                }
-            }
-        }
-        // codes of (row tb, block jb): 16 codes per k16, 8 per lane half
         const int tg = tb >> 5, tl = tb & 31;
-        half8* sb = &sB[buf][jb][tg * 128];
-        if (CH == 4) {
-            sb[tl] = i8x8_to_f16(rb0.x, rb0.y);
-            sb[tl + 32] = i8x8_to_f16(rb0.z, rb0.w);
-            sb[64 + tl] = i8x8_to_f16(rb1.x, rb1.y);
-            sb[64 + tl + 32] = i8x8_to_f16(rb1.z, rb1.w);
-        } else {
-            sb[64 * hb + tl] = i8x8_to_f16(rb0.x, rb0.y);
-            sb[64 * hb + tl + 32] = i8x8_to_f16(rb0.z, rb0.w);
+        half8* sbp = &sB[buf][jb][tg * 128];
+        sbp[tl] = i8x8_to_f16(rb0.x, rb0.y);
+        sbp[tl + 32] = i8x8_to_f16(rb0.z, rb0.w);
+        sbp[64 + tl] = i8x8_to_f16(rb1.x, rb1.y);
+        sbp[64 + tl + 32] = i8x8_to_f16(rb1.z, rb1.w);
+        const int b = c * CH + jb;
+        sD[buf][jb][tb] = rd;
+        if (Q4K) {
+            const float P = rd * (float)rs;
+            const _Float16 hi = (_Float16)P;
+            const _Float16 lo = (_Float16)(P - (float)hi);
+            sP[(b >> 3) & 1][tg][tl][b & 7] = hi;
+            sP[(b >> 3) & 1][tg][tl + 32][b & 7] = lo;
         }
-        if (CH == 4 || hb == 0) {
-            sD[buf][jb][tb] = rd;
-            if (Q4K) {
-                const float P = rd * (float)rs;
-                const _Float16 hi = (_Float16)P;
-                const _Float16 lo = (_Float16)(P - (float)hi);
-                const int b = c * CH + jb;
-                sP[(b >> 3) & 1][tg][tl][b & 7] = hi;
-                sP[(b >> 3) & 1][tg][tl + 32][b & 7] = lo;
-            }
-        }
+        if ((c % SBCH) == 0 && dm_thread) sDM[(c / SBCH) & 1][dm_g][dm_i] = rdm;
     };
 
     f32x16 acc[2], res[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { acc[i][r] = 0.0f; res[i][r] = 0.0f; }
-    }
+        for (int r = 0; r < 16; ++r) res[i][r] = 0.0f;
 
+    const int nch = nb / CH;
+#pragma unroll
+    for (int b = 0; b < PD; ++b)
+        if (b < nb) load_a(b, b);
     load_chunk(0);
     store_chunk(0, 0);
     if (nch > 1) load_chunk(1);
     __syncthreads();
 
-    for (int c = 0; c < nch; ++c) {
-        const int buf = c & 1;
-        // stage chunk c+1 into the other buffer (its previous contents, chunk c-1,
-        // were consumed before the barrier that ended the last iteration)
-        if (c + 1 < nch) {
-            store_chunk(c + 1, buf ^ 1);
-            if (c + 2 < nch) load_chunk(c + 2);
-        }
-
-        // Software pipeline inside the chunk: the MFMAs of block jj are issued
-        // before the epilogue FMAs of block jj-1, so the matrix core and the
-        // VALU work on different blocks at the same time.
-        f32x16 X[2][2];
-        auto mfma_block = [&](int jj, f32x16* Xo) {
+    for (int sb = 0; sb < nsb; ++sb) {
 #pragma unroll
-            for (int k16 = 0; k16 < 2; ++k16) {
-                half8 a[NPART];
+        for (int cc = 0; cc < SBCH; ++cc) {
+            const int c = sb * SBCH + cc;
+            const int buf = cc & 1;
+            if (c + 1 < nch) {
+                store_chunk(c + 1, buf ^ 1);
+                if (c + 2 < nch) load_chunk(c + 2);
+            }
+            f32x16 X[2][2];
+            half8 bfr[2][2][2];   // B fragments [ring][t group][k16], one block ahead
+            auto read_b = [&](int jj, half8 (*dst)[2]) {
 #pragma unroll
-                for (int p = 0; p < NPART; ++p) a[p] = sA[buf][jj][ogl][k16][p][lane];
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int k16 = 0; k16 < 2; ++k16)
+                        dst[i][k16] = sB[buf][jj][((2 * th + i) * 2 + k16) * 64 + lane];
+            };
+            auto mfma_block = [&](int slot, half8 (*bf)[2], f32x16* Xo) {
+#pragma unroll
+                for (int k16 = 0; k16 < 2; ++k16) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        if (k16 == 0) {
+                            const f32x16 zero = {};
+                            Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][0][0], bf[i][0], zero, 0, 0, 0);
+                        } else {
+                            Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][1][0], bf[i][1], Xo[i], 0, 0, 0);
+                        }
+                        if (!Q4K)
+                            Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][k16][NPART - 1], bf[i][k16], Xo[i], 0, 0, 0);
+                    }
+                }
+            };
+            auto epilogue_block = [&](int jj, const f32x16* Xi) {
+                const int j = cc * CH + jj;
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const half8 bf = sB[buf][jj][((2 * th + i) * 2 + k16) * 64 + lane];
-                    if (k16 == 0) {
-                        const f32x16 zero = {};
-                        Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], bf, zero, 0, 0, 0);
+                    const float da = sD[buf][jj][(2 * th + i) * 32 + (lane & 31)];
+                    if (j == 0) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[i][r] = da * Xi[i][r];
                     } else {
-                        Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], bf, Xo[i], 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(da, Xi[i][r], acc[i][r]);
                     }
-                    if (!Q4K)
-                        Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[NPART - 1], bf, Xo[i], 0, 0, 0);
                 }
-            }
-        };
-        auto epilogue_block = [&](int jj, const f32x16* Xi) {
-            const int b = c * CH + jj;
+            };
+            read_b(0, bfr[0]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float da = sD[buf][jj][(2 * th + i) * 32 + (lane & 31)];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(da, Xi[i][r], acc[i][r]);
+            for (int jj = 0; jj < CH; ++jj) {
+                const int j = cc * CH + jj;            // block within the superblock
+                const int b = sb * 8 + j;
+                load_a(min(b + PD, nb - 1), (j + PD) % RA);   // clamped: no branch, always in bounds
+                if (jj + 1 < CH) read_b(jj + 1, bfr[(jj + 1) & 1]);
+                mfma_block(j % RA, bfr[jj & 1], X[jj & 1]);
+                if (jj > 0) epilogue_block(jj - 1, X[(jj - 1) & 1]);
             }
-            if ((b & 7) == 7) {  // superblock boundary
-                const int sb = b >> 3;
-                const int64_t og = og0 + ogl;
+            epilogue_block(CH - 1, X[(CH - 1) & 1]);
+
+            if (cc == SBCH - 1) {
                 const int half = lane >> 5;
+                const float* dmv = &sDM[sb & 1][ogl][half * 16];
                 if (Q4K) {
-                    const float* dm = dmr + (og * nsb + sb) * 64;
-                    float dv[16], mv[16];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        dv[r] = dm[half * 16 + r];
-                        mv[r] = dm[32 + half * 16 + r];
-                    }
-                    const half8 mf = mfrag[(og * nsb + sb) * 64 + lane];
+                    const half8 mf = bload<half8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const half8 pf = *reinterpret_cast<const half8*>(&sP[sb & 1][2 * th + i][lane][0]);
@@ -279,41 +292,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(
                         const f32x16 mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf, pf, zero, 0, 0, 0);
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            float v = fmaf(dv[r], acc[i][r], res[i][r]);
-                            res[i][r] = fmaf(-mv[r], mn[r], v);
-                            acc[i][r] = 0.0f;
+                            const float v = fmaf(dmv[r], acc[i][r], res[i][r]);
+                            res[i][r] = fmaf(-dmv[32 + r], mn[r], v);
                         }
                     }
                 } else {
-                    const float* dm = dmr + (og * nsb + sb) * 32 + half * 16;
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            res[i][r] = fmaf(dm[r], acc[i][r], res[i][r]);
-                            acc[i][r] = 0.0f;
-                        }
+                        for (int r = 0; r < 16; ++r) res[i][r] = fmaf(dmv[r], acc[i][r], res[i][r]);
                 }
             }
-        };
-#pragma unroll
-        for (int jj = 0; jj < CH; ++jj) {
-            mfma_block(jj, X[jj & 1]);
-            if (jj > 0) epilogue_block(jj - 1, X[(jj - 1) & 1]);
+            __syncthreads();
         }
-        epilogue_block(CH - 1, X[(CH - 1) & 1]);
-        __syncthreads();
     }
 
-    // ---- store: lane holds token t, rows o = 8*(r/4) + 4*(lane/32) + r%4 ----
+    const int od = g.od;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t t = t0 + (2 * th + i) * 32 + (lane & 31);
-        if (t >= n) continue;
-        float* orow = out + t * (int64_t)od;
+        if (t >= g.n) continue;
+        float* orow = g.out + t * (int64_t)od;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t o = (og0 + ogl) * 32 + 8 * q + 4 * (lane >> 5);
+            const int64_t o = (int64_t)(og0 + ogl) * 32 + 8 * q + 4 * (lane >> 5);
             if (o + 3 < od && (od & 3) == 0) {
                 *reinterpret_cast<float4*>(orow + o) =
                     make_float4(res[i][4 * q], res[i][4 * q + 1], res[i][4 * q + 2], res[i][4 * q + 3]);
@@ -330,17 +332,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(
 
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
                        hipStream_t s) {
-    const int n_ttiles = (int)((n + 127) / 128);
-    const int n_otiles = (int)(w.rows_pad / kTileO);
-    const dim3 grid((unsigned)(n_ttiles * n_otiles)), block(kThreads);
-    if (w.type == 12)
-        hipLaunchKernelGGL((k_gemm<true, 4>), grid, block, 0, s, (const half8*)w.wa, w.dmr,
-                           (const half8*)w.mfrag, pl.q, pl.D, pl.S, (int)n, (int)pl.rows,
-                           (int)w.cols, (int)w.rows, n_ttiles, n_otiles, out);
-    else
-        hipLaunchKernelGGL((k_gemm<false, 2>), grid, block, 0, s, (const half8*)w.wa, w.dmr,
-                           (const half8*)nullptr, pl.q, pl.D, pl.S, (int)n, (int)pl.rows,
-                           (int)w.cols, (int)w.rows, n_ttiles, n_otiles, out);
+    GemmArgs a;
+    a.wa = (const half8*)w.wa;
+    a.dmr = w.dmr;
+    a.mfrag = (const half8*)w.mfrag;
+    a.q = pl.q;
+    a.D = pl.D;
+    a.S = pl.S;
+    a.out = out;
+    const int npart = w.type == 12 ? 1 : 2;
+    const int64_t nsb = w.cols / kSuper, og = w.rows_pad / 32;
+    a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * npart * 2);
+    a.dmr_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 64 : 32) * 4);
+    a.mfrag_bytes = w.type == 12 ? (uint32_t)(og * nsb * 512 * 2) : 0u;
+    a.q_bytes = (uint32_t)(pl.rows * pl.d);
+    a.ds_bytes = (uint32_t)(pl.rows * (pl.d / kBlock) * 4);
+    a.n = (int)n;
+    a.plane_rows = (int)pl.rows;
+    a.id = (int)w.cols;
+    a.od = (int)w.rows;
+    a.n_ttiles = (int)((n + 127) / 128);
+    if (w.type == 12) {
+        a.n_otiles = (int)(w.rows_pad / 128);
+        const dim3 grid((unsigned)(a.n_ttiles * a.n_otiles)), block(kThreads);
+        hipLaunchKernelGGL((k_gemm_da<true>), grid, block, 0, s, a);
+    } else {
+        a.n_otiles = (int)(w.rows_pad / 128);
+        const dim3 grid((unsigned)(a.n_ttiles * a.n_otiles)), block(kThreads);
+        hipLaunchKernelGGL((k_gemm_da<false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

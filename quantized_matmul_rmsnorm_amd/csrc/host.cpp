@@ -414,6 +414,13 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     const int64_t mf_b = type == MMQ_Q4_K ? og * nsb * 512 * 2 : 0;
     const int64_t ql_b = rows * nb * 16, qh_b = rows * nb * 8, sc_b = rows * nb * 2,
                   dv_b = rows * nsb * 4;
+    // the matmul addresses its tiles with 32-bit buffer offsets
+    if ((uses & MMQ_USE_GEMM) && wa_b > (int64_t)0xFFFFFFFF) {
+        delete h;
+        return fail(MMQ_E_SHAPE, "%s: %lld x %lld needs %lld bytes of matmul tiles (limit 4 GiB); "
+                    "register it as several row blocks", who, (long long)rows, (long long)cols,
+                    (long long)wa_b);
+    }
     int64_t total = 0;
     if (uses & MMQ_USE_GEMM) total += wa_b + dmr_b + mf_b;
     if (uses & MMQ_USE_GEMV) total += ql_b + qh_b + sc_b + dv_b;
@@ -450,10 +457,10 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
             return fail(MMQ_E_OOM, "%s: %lld bytes of matmul tiles", who, (long long)(wa_b + dmr_b + mf_b));
         }
         w.wa = (_Float16*)p1; w.dmr = (float*)p2; w.mfrag = (_Float16*)p3;
-        hipMemset(p1, 0, (size_t)wa_b);
-        hipMemset(p2, 0, (size_t)dmr_b);
-        if (p3) hipMemset(p3, 0, (size_t)mf_b);
-        e = launch_repack_gemm((const uint8_t*)raw_dev, w, nullptr);
+        e = hipMemset(p1, 0, (size_t)wa_b);   // padded rows stay zero weights
+        if (e == hipSuccess) e = hipMemset(p2, 0, (size_t)dmr_b);
+        if (e == hipSuccess && p3) e = hipMemset(p3, 0, (size_t)mf_b);
+        if (e == hipSuccess) e = launch_repack_gemm((const uint8_t*)raw_dev, w, nullptr);
         if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: repack"); }
     }
     if (uses & MMQ_USE_GEMV) {
@@ -508,6 +515,10 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
                        void* stream, int type, const char* who) {
     int rc = consume_check(c, w, a, n, out, type, MMQ_USE_GEMM, who);
     if (rc) return rc;
+    // the matmul addresses the plane with 32-bit offsets
+    if (round_up(n, kPlaneRows) * w->w.cols >= ((int64_t)1 << 31))
+        return fail(MMQ_E_SHAPE, "%s: plane of %lld x %lld codes exceeds 2 GiB; split the tokens",
+                    who, (long long)n, (long long)w->w.cols);
     if ((rc = use_device(c))) return rc;
     PlaneView pl;
     if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;
