@@ -9,8 +9,9 @@
 // then per 32-block: amax = max|y|, D = amax / 127, q = clamp(rint(y / D),
 // -127, 127), S = sum(q); an all-zero block has D = 0, q = 0, S = 0.
 //
-// Geometry.  One wave per row.  The row is swept in rounds of 256 values: in
-// round r lane l owns the float4 at 256*r + 4*l, so each wave access is one
+// Geometry.  One workgroup of 4 waves per row; the row is swept in rounds of
+// 256 values, round r belonging to wave r % 4: in round r lane l owns the
+// float4 at 256*r + 4*l, so each wave access is one
 // contiguous 1 KiB (the pages' rule that a full-width coalesced access must
 // never be broken), and the 8 consecutive lanes 8g..8g+7 hold exactly one
 // 32-block.  amax and the code sum are reduced inside those 8 lanes with DPP
@@ -21,9 +22,11 @@
 // stored y give byte-identical planes.
 //
 // RMSNorm accumulates sum(x^2) in f64 (products of f32 values are exact in
-// f64) and rounds the scale once from f64, which makes s independent of the
-// summation order to within one f64 rounding.  For d <= 256*MAXR the row's x
-// stays in registers between the two passes; longer rows are re-read.
+// f64): per lane, then across the wave, then the four wave sums in a fixed
+// order through LDS; the scale is rounded once from f64, which makes it
+// independent of the summation order to within one f64 rounding.  While a
+// wave's share of the row fits (d <= 4*256*MAXR) its x stays in registers
+// between the two passes; longer rows are re-read.
 //
 // Rows n .. rows-1 of the plane (the padding to a multiple of 32 rows) are
 // written as zeros, so a plane's content never depends on what its slot held
@@ -62,8 +65,15 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
-__device__ __forceinline__ int code(float v, float dsc) {
-    float r = rintf(v / dsc);                // IEEE quotient, round half to even
+// q = clamp(rint(v / dsc), -127, 127) with the IEEE quotient.  Fast path:
+// a = v * rcp(dsc) is within a few ulp of v / dsc (|v / dsc| <= 127, so within
+// 2^-15 absolute); when a is farther than 2^-11 from a half-integer, rint(a)
+// equals rint of the correctly rounded quotient.  Otherwise (and for a
+// subnormal dsc) the quotient is computed exactly.
+__device__ __forceinline__ int code(float v, float dsc, float rcp) {
+    const float a = v * rcp;
+    float r = rintf(a);
+    if (!(fabsf(a - r) <= 0.5f - 0x1p-11f) || dsc < 0x1p-126f) r = rintf(v / dsc);
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (int)r;
 }
@@ -77,7 +87,9 @@ __device__ __forceinline__ void quant4(float4 v, int lane, uint32_t* qdst, float
     const float dsc = am / 127.0f;
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
     if (am > 0.0f) {
-        q0 = code(v.x, dsc); q1 = code(v.y, dsc); q2 = code(v.z, dsc); q3 = code(v.w, dsc);
+        const float rcp = __builtin_amdgcn_rcpf(dsc);
+        q0 = code(v.x, dsc, rcp); q1 = code(v.y, dsc, rcp);
+        q2 = code(v.z, dsc, rcp); q3 = code(v.w, dsc, rcp);
     }
     *qdst = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
             ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
@@ -93,6 +105,9 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return (g / den) * u;
 }
 
+// One workgroup (4 waves) per row; round r of the row belongs to wave r % 4.
+// MAXR > 0: a wave's rounds (at most MAXR) stay in registers between the
+// RMSNorm passes.
 template <int KIND, bool WRITE_Y, int MAXR>
 __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
                                                   const float* __restrict__ b,
@@ -100,25 +115,30 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
                                                   float eps, int8_t* __restrict__ q,
                                                   float* __restrict__ D,
                                                   int32_t* __restrict__ S, int rows) {
+    constexpr int W = 4;   // waves per row
+    constexpr int U = 8;   // rounds of one wave whose loads are in flight together
+    __shared__ double s_ss[W];
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;  // wave-uniform
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x;
     const int nb = d / kBlock;
     const int rounds = d / kSuper;
+    const int my = (rounds - wave + W - 1) / W;   // rounds of this wave: wave + W*k, k < my
     uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (int64_t)row * d);
     float* Dr = D + (int64_t)row * nb;
     int32_t* Sr = S + (int64_t)row * nb;
     const int g = lane >> 3;
 
     if (row >= n) {  // padded tail rows: deterministic zeros
-        for (int r = 0; r < rounds; ++r) {
+        for (int k = 0; k < my; ++k) {
+            const int r = wave + W * k;
             q4[64 * r + lane] = 0u;
             if ((lane & 7) == 0) {
                 Dr[8 * r + g] = 0.0f;
                 Sr[8 * r + g] = 0;
             }
         }
-        return;
+        return;  // the whole workgroup takes this branch
     }
 
     const float4* a4 = reinterpret_cast<const float4*>(a + (int64_t)row * d);
@@ -130,46 +150,49 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
     float4 xr[MAXR > 0 ? MAXR : 1];
     if constexpr (KIND == kProdRms) {
         double ss = 0.0;
+        auto acc4 = [&](const float4& v) {
+            ss += (double)v.x * (double)v.x;
+            ss += (double)v.y * (double)v.y;
+            ss += (double)v.z * (double)v.z;
+            ss += (double)v.w * (double)v.w;
+        };
         if constexpr (MAXR > 0) {
 #pragma unroll
-            for (int r = 0; r < MAXR; ++r)
-                if (r < rounds) xr[r] = a4[64 * r + lane];
+            for (int k = 0; k < MAXR; ++k)
+                if (k < my) xr[k] = a4[64 * (wave + W * k) + lane];
 #pragma unroll
-            for (int r = 0; r < MAXR; ++r)
-                if (r < rounds) {
-                    const float4 v = xr[r];
-                    ss += (double)v.x * (double)v.x;
-                    ss += (double)v.y * (double)v.y;
-                    ss += (double)v.z * (double)v.z;
-                    ss += (double)v.w * (double)v.w;
-                }
+            for (int k = 0; k < MAXR; ++k)
+                if (k < my) acc4(xr[k]);
         } else {
-            for (int r = 0; r < rounds; ++r) {
-                const float4 v = a4[64 * r + lane];
-                ss += (double)v.x * (double)v.x;
-                ss += (double)v.y * (double)v.y;
-                ss += (double)v.z * (double)v.z;
-                ss += (double)v.w * (double)v.w;
+            for (int k0 = 0; k0 < my; k0 += U) {
+                float4 t[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (k0 + u < my) t[u] = a4[64 * (wave + W * (k0 + u)) + lane];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (k0 + u < my) acc4(t[u]);
             }
         }
         ss = wave_sum_f64(ss);
-        scale = (float)(1.0 / sqrt(ss / (double)d + (double)eps));
+        if (lane == 0) s_ss[wave] = ss;
+        __syncthreads();
+        const double tot = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+        scale = (float)(1.0 / sqrt(tot / (double)d + (double)eps));
     }
 
-    auto one_round = [&](int r, float4 xin) {
+    auto finish = [&](int r, float4 xin, float4 bin) {
         float4 v;
         if constexpr (KIND == kProdRms) {
-            const float4 w = b4[64 * r + lane];
-            v.x = (xin.x * scale) * w.x;
-            v.y = (xin.y * scale) * w.y;
-            v.z = (xin.z * scale) * w.z;
-            v.w = (xin.w * scale) * w.w;
+            v.x = (xin.x * scale) * bin.x;
+            v.y = (xin.y * scale) * bin.y;
+            v.z = (xin.z * scale) * bin.z;
+            v.w = (xin.w * scale) * bin.w;
         } else if constexpr (KIND == kProdSwiglu) {
-            const float4 u = b4[64 * r + lane];
-            v.x = silu_mul(xin.x, u.x);
-            v.y = silu_mul(xin.y, u.y);
-            v.z = silu_mul(xin.z, u.z);
-            v.w = silu_mul(xin.w, u.w);
+            v.x = silu_mul(xin.x, bin.x);
+            v.y = silu_mul(xin.y, bin.y);
+            v.z = silu_mul(xin.z, bin.z);
+            v.w = silu_mul(xin.w, bin.w);
         } else {
             v = xin;
         }
@@ -179,23 +202,45 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
 
     if constexpr (MAXR > 0) {
 #pragma unroll
-        for (int r = 0; r < MAXR; ++r)
-            if (r < rounds) one_round(r, xr[r]);
+        for (int k0 = 0; k0 < MAXR; k0 += U) {
+            if (k0 < my) {
+                float4 tb[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (k0 + u < my) tb[u] = b4[64 * (wave + W * (k0 + u)) + lane];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (k0 + u < my) finish(wave + W * (k0 + u), xr[k0 + u], tb[u]);
+            }
+        }
     } else {
-        for (int r = 0; r < rounds; ++r) one_round(r, a4[64 * r + lane]);
+        for (int k0 = 0; k0 < my; k0 += U) {
+            float4 ta[U], tb[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = wave + W * (k0 + u);
+                if (k0 + u < my) {
+                    ta[u] = a4[64 * r + lane];
+                    if constexpr (KIND != kProdF32) tb[u] = b4[64 * r + lane];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (k0 + u < my) finish(wave + W * (k0 + u), ta[u], KIND != kProdF32 ? tb[u] : ta[u]);
+        }
     }
 }
 
 template <int KIND, bool WY>
 hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, int64_t d,
                          float eps, const PlaneView& pl, hipStream_t s) {
-    const int rounds = (int)(d / kSuper);
-    dim3 grid((unsigned)((pl.rows + 3) / 4)), block(256);
-    if (KIND == kProdRms && rounds <= 16) {
-        hipLaunchKernelGGL((k_producer<KIND, WY, 16>), grid, block, 0, s, a, b, y, (int)n,
+    const int per_wave = (int)((d / kSuper + 3) / 4);
+    dim3 grid((unsigned)pl.rows), block(256);
+    if (KIND == kProdRms && per_wave <= 8) {
+        hipLaunchKernelGGL((k_producer<KIND, WY, 8>), grid, block, 0, s, a, b, y, (int)n,
                            (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
-    } else if (KIND == kProdRms && rounds <= 32) {
-        hipLaunchKernelGGL((k_producer<KIND, WY, 32>), grid, block, 0, s, a, b, y, (int)n,
+    } else if (KIND == kProdRms && per_wave <= 16) {
+        hipLaunchKernelGGL((k_producer<KIND, WY, 16>), grid, block, 0, s, a, b, y, (int)n,
                            (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
     } else {
         hipLaunchKernelGGL((k_producer<KIND, WY, 0>), grid, block, 0, s, a, b, y, (int)n,
