@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    # one untimed device copy of this many MiB before the chain: the plain copy
+    # kernel of known size that scales the HBM byte counters of a --pmc run
+    p.add_argument("--copy-calibration", type=int, default=0, help=argparse.SUPPRESS)
     return p.parse_args()
 
 
@@ -123,8 +126,30 @@ class Chain:
                {k: len(v) for k, v in self.events.items()}
 
 
+def _graph_time_us(torch, fn, reps):
+    """Average time of one fn() launch: `reps` launches captured in one HIP
+    graph, the graph replayed three times between HIP events (launch gaps
+    inside a graph are included; host call overhead is not)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / (3 * reps)
+
+
 def decode_gemv(mmq, torch, synth):
-    """One-token q6_K GEMV at the 14B decode shapes, weights streamed cold."""
+    """One-token q6_K GEMV at the 14B decode shapes, weights streamed cold
+    (copies rotated so the set exceeds the 256 MB last-level cache), and the
+    n = 1 producers that feed them; each timed as a captured HIP graph."""
     ctx = mmq.mmq_create(0, 0)
     shapes = {"attn_v": (1024, 5120, 64), "ffn_down": (5120, 13824, 8), "lm_head": (152064, 5120, 2)}
     res = {}
@@ -147,17 +172,13 @@ def decode_gemv(mmq, torch, synth):
                 mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)
             else:
                 mmq.mmq_quant_swiglu(ctx, g, u, y13, 1, 13824, 0)
-            reps = max(2 * copies, 16)
-            for i in range(copies):
-                mmq.mmvq_q6k(ctx, ws[i], key, out)
+            mmq.mmvq_q6k(ctx, ws[0], key, out)
             torch.cuda.synchronize()
-            evs = []
-            for i in range(reps):
-                a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
-                a.record(); mmq.mmvq_q6k(ctx, ws[i % copies], key, out); b.record()
-                evs.append((a, b))
-            torch.cuda.synchronize()
-            t_us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / reps
+            ref = out.clone()
+            reps = max(2 * copies, 32)
+            t_us = _graph_time_us(torch, lambda i: mmq.mmvq_q6k(ctx, ws[i % copies], key, out), reps)
+            if not torch.equal(out, ref):       # every copy holds the same weights
+                raise RuntimeError(f"{name}: graph replay output differs from the eager launch")
             nbytes = od * id_ / 256 * 210 + id_ * 1.25 + od * 4
             res[name] = {"od": od, "id": id_, "us": round(t_us, 3),
                          "GB_s": round(nbytes / (t_us * 1e-6) / 1e9, 1)}
@@ -165,18 +186,13 @@ def decode_gemv(mmq, torch, synth):
             for w in ws:
                 mmq.mmq_weight_free(w)
         # decode producers (rms 5120, swiglu 13824) at n = 1
-        for name, fn in (("rms_5120", lambda: mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)),
-                         ("swiglu_13824", lambda: mmq.mmq_quant_swiglu(ctx, g, u, y13, 1, 13824, 0))):
-            fn(); torch.cuda.synchronize()
-            evs = []
-            for _ in range(50):
-                a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
-                a.record(); fn(); b.record(); evs.append((a, b))
-            torch.cuda.synchronize()
-            res[name] = {"us": round(1e3 * sum(a.elapsed_time(b) for a, b in evs) / 50, 3)}
+        for name, fn in (("rms_5120", lambda i: mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)),
+                         ("swiglu_13824", lambda i: mmq.mmq_quant_swiglu(ctx, g, u, y13, 1, 13824, 0))):
+            res[name] = {"us": round(_graph_time_us(torch, fn, 50), 3)}
         res["aggregate_GB_s"] = round(tot_b / (tot_t * 1e-6) / 1e9, 1)
         res["aggregate_frac_hbm"] = round(res["aggregate_GB_s"] / PEAK_HBM_GBS, 4)
     finally:
+        mmq.mmq_cache_clear(ctx)
         mmq.mmq_destroy(ctx)
     return res
 
@@ -223,6 +239,33 @@ def cpu_baseline(seconds: float):
             "cpu_model": _cpu_model(), "seconds": round(t_used, 2)}
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(ROOT, "quantized_matmul_rmsnorm_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_da_q4k_traffic_7b_chain.txt")
+
+
+def gemm_source_sha():
+    import hashlib
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per q4_K matmul launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE runs, each scaled by the copy calibration), or
+    None when the summary is missing or was taken from another gemm.hip."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("traffic_json:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("gemm_sha256") == gemm_source_sha():
+                        return rec
+    except (OSError, ValueError):
+        pass
+    return None
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -250,6 +293,16 @@ def main():
     import quantized_matmul_rmsnorm_amd as mmq
     import synth
 
+    if args.copy_calibration:
+        nel = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nel * 4} bytes read, {nel * 4} bytes written")
+        del src, dst
+
     t_setup = time.perf_counter()
     chain = Chain(mmq, torch, synth, args.layers)
     torch.cuda.synchronize()
@@ -264,12 +317,18 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
+    marks = [start]
     for _ in range(args.steps):
         chain.step()
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        marks.append(ev)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
+    per_step = sorted(a.elapsed_time(b) for a, b in zip(marks[:-1], marks[1:]))
+    ms_median = per_step[len(per_step) // 2]
     cls_ms, cls_n = chain.class_times_ms()
     st1 = mmq.mmq_stats(chain.ctx)
     ops = chain_ops(TOKENS, args.layers)
@@ -279,6 +338,11 @@ def main():
     q4_ops_launch = 2 * TOKENS * sum(od * id_ for _, wt, od, id_, _ in LAYER_GEMMS if wt == "q4_K") / 5
     q4_avg_us = 1e3 * cls_ms["gemm_q4k"] / cls_n["gemm_q4k"]
     achieved = q4_ops_launch / (q4_avg_us * 1e-6) / 1e12
+    q4_shapes = [(od, id_) for _, wt, od, id_, _ in LAYER_GEMMS if wt == "q4_K"]
+    # the method's own data, each byte once: q4_K superblocks (144 B / 256
+    # weights), the plane (1 + 4/32 + 4/32 B per value), f32 outputs
+    q4_alg_bytes = sum(od * id_ * 144 / 256 + TOKENS * id_ * 1.25 + TOKENS * od * 4
+                       for od, id_ in q4_shapes) / len(q4_shapes)
     q6_ops_launch = 2 * TOKENS * sum(od * id_ for _, wt, od, id_, _ in LAYER_GEMMS if wt == "q6_K") / 2
     q6_avg_us = 1e3 * cls_ms["gemm_q6k"] / cls_n["gemm_q6k"]
 
@@ -295,6 +359,7 @@ def main():
     kernels["gemm_q4k"]["TOPS"] = round(achieved, 1)
     kernels["gemm_q6k"]["TOPS"] = round(q6_ops_launch / (q6_avg_us * 1e-6) / 1e12, 1)
 
+    traffic = measured_traffic()
     decode = None if args.no_decode else decode_gemv(mmq, torch, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
@@ -316,11 +381,14 @@ def main():
                    "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN, "kv": KV, "layers": args.layers,
                    "weights": "q4_K (q,k,o,gate,up), q6_K (v,down)"},
         "tok_s_equiv": round(TOKENS / (ms_step * 1e-3), 1),
+        "median_ms_per_step": round(ms_median, 3),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": None, "kernel": "k_gemm<q4_K>",
-                     "ops_per_launch": q4_ops_launch, "avg_launch_us": round(q4_avg_us, 2),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "kernel": "k_gemm_da<true> (q4_K)",
+                     "ops_per_launch": q4_ops_launch,
+                     "algorithmic_bytes_per_launch": round(q4_alg_bytes), "avg_launch_us": round(q4_avg_us, 2),
                      "frac_of_f16_mfma_peak": round(achieved / PEAK_F16_TOPS, 4)},
         "kernels": kernels,
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
