@@ -32,7 +32,11 @@
 // through two LDS buffers, converted int8 -> f16 once per workgroup, and each
 // block's B fragments are read from LDS one block ahead.  All global reads use
 // raw buffer loads with 32-bit offsets; plane rows past the plane's padded
-// row count fall outside the buffer and read as zero.  Outputs are stored
+// row count fall outside the buffer and read as zero.  Staging and prefetch
+// indices are clamped instead of guarded, so a superblock's two chunks form
+// one basic block the scheduler can interleave; each wave raises its priority
+// while it issues a block's MFMAs, so the other wave on the SIMD runs its
+// rescale FMAs in the gaps.  Outputs are stored
 // only for t < n and o < rows.  Workgroups are mapped so that each XCD works
 // on a contiguous group of output x token tiles (shared L2).
 #include "mmq_internal.h"
@@ -127,8 +131,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     constexpr int BPAD = 4, DPAD = 16;
     __shared__ half8 sB[2][CH][4 * 2 * 64 + BPAD];
     __shared__ float sD[2][CH][128 + DPAD];
-    __shared__ __attribute__((aligned(16))) _Float16 sP[Q4K ? 2 : 1][4][64][8];
-    __shared__ __attribute__((aligned(16))) float sDM[2][4][NDM * 32];
+    __shared__ __attribute__((aligned(16))) _Float16 sP[Q4K ? 3 : 1][4][64][8];
+    __shared__ __attribute__((aligned(16))) float sDM[2][kThreads];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -169,24 +173,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     const int rowb = t0 + tb;
     const uint32_t rowq = rowb < g.plane_rows ? (uint32_t)rowb * (uint32_t)id : 0x80000000u;
     const uint32_t rowd = rowb < g.plane_rows ? (uint32_t)(rowb * nb + jb) * 4u : 0x80000000u;
-    const int dm_g = tid / (NDM * 32), dm_i = tid % (NDM * 32);
-    const bool dm_thread = tid < 4 * NDM * 32;
+    // superblock scales: thread tid stages entry tid % DMN (threads past DMN
+    // duplicate an entry into a spare half of sDM, so every thread stores)
+    constexpr int DMN = 4 * NDM * 32;
+    const int dm_e = tid % DMN;
+    const uint32_t dm_off = (uint32_t)(((og0 + dm_e / (NDM * 32)) * nsb) * (NDM * 32 * 4) +
+                                       (dm_e % (NDM * 32)) * 4);
 
     uint4 rb0, rb1;
     float rd, rdm = 0.0f;
     int32_t rs;
-    auto load_chunk = [&](int c) {
+    // Chunk c's codes, scales and sums (and, for a superblock's first chunk,
+    // the superblock scales) into registers.  c is clamped by the caller, so
+    // the loop body has no branch; a clamped repeat is never consumed.
+    auto load_chunk = [&](int c, bool first) {
         const uint32_t sq = (uint32_t)(c * CH) * 32u;
         rb0 = bload<uint4>(rQ, rowq + (uint32_t)jb * 32u, sq);
         rb1 = bload<uint4>(rQ, rowq + (uint32_t)jb * 32u + 16u, sq);
         rd = bload<float>(rD, rowd, (uint32_t)(c * CH) * 4u);
         rs = Q4K ? bload<int32_t>(rS, rowd, (uint32_t)(c * CH) * 4u) : 0;
-        if ((c % SBCH) == 0 && dm_thread) {
-            const int sb = c / SBCH;
-            rdm = bload<float>(rM, (uint32_t)(((og0 + dm_g) * nsb + sb) * (NDM * 32 * 4) + dm_i * 4), 0u);
-        }
+        if (first) rdm = bload<float>(rM, dm_off, (uint32_t)((c / SBCH) * (NDM * 32 * 4)));
     };
-    auto store_chunk = [&](int c, int buf) {
+    // real == false: a clamped repeat of the last chunk; its min-term operands
+    // go to a spare slot of sP (the codes land in the idle sB buffer).
+    auto store_chunk = [&](int c, int buf, bool first, bool real) {
         const int tg = tb >> 5, tl = tb & 31;
         half8* sbp = &sB[buf][jb][tg * 128];
         sbp[tl] = i8x8_to_f16(rb0.x, rb0.y);
@@ -199,10 +209,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
             const float P = rd * (float)rs;
             const _Float16 hi = (_Float16)P;
             const _Float16 lo = (_Float16)(P - (float)hi);
-            sP[(b >> 3) & 1][tg][tl][b & 7] = hi;
-            sP[(b >> 3) & 1][tg][tl + 32][b & 7] = lo;
+            const int slot = real ? ((b >> 3) & 1) : 2;
+            sP[slot][tg][tl][b & 7] = hi;
+            sP[slot][tg][tl + 32][b & 7] = lo;
         }
-        if ((c % SBCH) == 0 && dm_thread) sDM[(c / SBCH) & 1][dm_g][dm_i] = rdm;
+        if (first) sDM[(c / SBCH) & 1][tid] = rdm;
     };
 
     f32x16 acc[2], res[2];
@@ -211,13 +222,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) res[i][r] = 0.0f;
 
-    const int nch = nb / CH;
+    const int nch = nb / CH;     // even: id is a multiple of 256
 #pragma unroll
-    for (int b = 0; b < PD; ++b)
-        if (b < nb) load_a(b, b);
-    load_chunk(0);
-    store_chunk(0, 0);
-    if (nch > 1) load_chunk(1);
+    for (int b = 0; b < PD; ++b) load_a(b, b);   // nb >= 8 > PD
+    load_chunk(0, true);
+    store_chunk(0, 0, true, true);
+    load_chunk(1, false);
     __syncthreads();
 
     for (int sb = 0; sb < nsb; ++sb) {
@@ -225,10 +235,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
         for (int cc = 0; cc < SBCH; ++cc) {
             const int c = sb * SBCH + cc;
             const int buf = cc & 1;
-            if (c + 1 < nch) {
-                store_chunk(c + 1, buf ^ 1);
-                if (c + 2 < nch) load_chunk(c + 2);
-            }
+            // stage chunk c+1 (loaded one chunk ago), load chunk c+2
+            store_chunk(min(c + 1, nch - 1), buf ^ 1, (cc + 1) % SBCH == 0, c + 1 < nch);
+            load_chunk(min(c + 2, nch - 1), cc % SBCH == 0);
+            half8 mf;
+            if (Q4K && cc == SBCH - 1)
+                mf = bload<half8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
             f32x16 X[2][2];
             half8 bfr[2][2][2];   // B fragments [ring][t group][k16], one block ahead
             auto read_b = [&](int jj, half8 (*dst)[2]) {
@@ -254,11 +266,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
                     }
                 }
             };
+            float dav[CH][2];
+#pragma unroll
+            for (int jj = 0; jj < CH; ++jj)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) dav[jj][i] = sD[buf][jj][(2 * th + i) * 32 + (lane & 31)];
             auto epilogue_block = [&](int jj, const f32x16* Xi) {
                 const int j = cc * CH + jj;
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const float da = sD[buf][jj][(2 * th + i) * 32 + (lane & 31)];
+                    const float da = dav[jj][i];
                     if (j == 0) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[i][r] = da * Xi[i][r];
@@ -275,16 +292,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
                 const int b = sb * 8 + j;
                 load_a(min(b + PD, nb - 1), (j + PD) % RA);   // clamped: no branch, always in bounds
                 if (jj + 1 < CH) read_b(jj + 1, bfr[(jj + 1) & 1]);
+                __builtin_amdgcn_s_setprio(1);   // wave priority only (not a queue priority)
                 mfma_block(j % RA, bfr[jj & 1], X[jj & 1]);
+                __builtin_amdgcn_s_setprio(0);
                 if (jj > 0) epilogue_block(jj - 1, X[(jj - 1) & 1]);
             }
             epilogue_block(CH - 1, X[(CH - 1) & 1]);
 
             if (cc == SBCH - 1) {
                 const int half = lane >> 5;
-                const float* dmv = &sDM[sb & 1][ogl][half * 16];
+                const float* dmv = &sDM[sb & 1][ogl * (NDM * 32) + half * 16];
                 if (Q4K) {
-                    const half8 mf = bload<half8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const half8 pf = *reinterpret_cast<const half8*>(&sP[sb & 1][2 * th + i][lane][0]);
