@@ -78,13 +78,27 @@ __device__ __forceinline__ float block_term(const ActBlock& a, uint4 L, uint2 H,
     return (a.D * d) * (float)ic;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes: four DPP steps inside each row of 16 lanes
+// (quad xor-1, quad xor-2, half-row mirror, row mirror), then two lane swaps.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    v += dppf<0xB1>(v);
+    v += dppf<0x4E>(v);
+    v += dppf<0x141>(v);
+    v += dppf<0x140>(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
     return v;
 }
 
-// MAXR > 0: the lane's activation blocks stay in registers (nb <= 64 * MAXR).
+// MAXR > 0: the lane's activation blocks stay in registers (nb <= 64 * MAXR),
+// and the weights of the wave's next row are loaded block by block as soon as
+// the current row's registers for that block are consumed, so a row's loads
+// are in flight while the previous row is reduced.
 // MAXR == 0: blocks are re-read from the plane for every row (any length).
 template <int MAXR>
 __global__ __launch_bounds__(256) void k_mmvq_q6k(const uint4* __restrict__ ql,
@@ -101,25 +115,52 @@ __global__ __launch_bounds__(256) void k_mmvq_q6k(const uint4* __restrict__ ql,
     const int nsb = id / kSuper;
     const int rounds = (nb + 63) / 64;
 
-    ActBlock act[MAXR > 0 ? MAXR : 1];
     if constexpr (MAXR > 0) {
+        ActBlock act[MAXR];
+        uint4 L[MAXR];
+        uint2 H[MAXR];
+        int16_t S[MAXR];
+        float Dw[MAXR];
 #pragma unroll
         for (int r = 0; r < MAXR; ++r)
             if (r < rounds) act[r] = load_act(Q, Dp, 64 * r + lane, nb);
-    }
-
-    for (int o = wave; o < od; o += nwaves) {
-        const int64_t rb = (int64_t)o * nb;
-        float acc = 0.0f;
-        if constexpr (MAXR > 0) {
+        auto load_block = [&](int o, int r) {
+            const int b = 64 * r + lane;
+            const int64_t rb = (int64_t)o * nb;
+            {
+                typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                const u4v l4 = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ql) + rb + b);
+                const u2v h2 = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(qh) + rb + b);
+                L[r] = make_uint4(l4.x, l4.y, l4.z, l4.w);
+                H[r] = make_uint2(h2.x, h2.y);
+            }
+            S[r] = __builtin_nontemporal_load(&sc[rb + b]);
+            Dw[r] = __builtin_nontemporal_load(&dv[(int64_t)o * nsb + (b >> 3)]);
+        };
+        int o = wave;
+        if (o < od) {
+#pragma unroll
+            for (int r = 0; r < MAXR; ++r)
+                if (r < rounds && 64 * r + lane < nb) load_block(o, r);
+        }
+        for (; o < od; o += nwaves) {
+            const int on = o + nwaves;
+            float acc = 0.0f;
 #pragma unroll
             for (int r = 0; r < MAXR; ++r) {
-                const int b = 64 * r + lane;
-                if (r < rounds && b < nb)
-                    acc += block_term(act[r], ql[rb + b], qh[rb + b], sc[rb + b],
-                                      dv[(int64_t)o * nsb + (b >> 3)]);
+                if (r < rounds && 64 * r + lane < nb) {
+                    acc += block_term(act[r], L[r], H[r], S[r], Dw[r]);
+                    if (on < od) load_block(on, r);
+                }
             }
-        } else {
+            acc = wave_sum(acc);
+            if (lane == 0) out[o] = acc;
+        }
+    } else {
+        for (int o = wave; o < od; o += nwaves) {
+            const int64_t rb = (int64_t)o * nb;
+            float acc = 0.0f;
             for (int r = 0; r < rounds; ++r) {
                 const int b = 64 * r + lane;
                 if (b < nb) {
@@ -128,10 +169,30 @@ __global__ __launch_bounds__(256) void k_mmvq_q6k(const uint4* __restrict__ ql,
                                       dv[(int64_t)o * nsb + (b >> 3)]);
                 }
             }
+            acc = wave_sum(acc);
+            if (lane == 0) out[o] = acc;
         }
-        acc = wave_sum(acc);
-        if (lane == 0) out[o] = acc;
     }
+}
+
+// Workgroups of one launch: every row gets a wave when the rows fit in two
+// rounds of resident waves; larger matrices get exactly the resident waves
+// (each then walks rows grid-stride with its plane slice loaded once).
+template <int MAXR>
+int64_t mmvq_grid(int64_t rows) {
+    static int per_cu = -1, n_cu = 0;
+    if (per_cu < 0) {
+        int dev = 0, blk = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq_q6k<MAXR>, 256, 0) != hipSuccess)
+            blk = 1;
+        per_cu = blk > 0 ? blk : 1;
+        if (n_cu <= 0) n_cu = 256;
+    }
+    const int64_t resident = (int64_t)per_cu * n_cu;
+    const int64_t want = (rows + 3) / 4;
+    return want <= 2 * resident ? want : resident;
 }
 
 }  // namespace
@@ -139,20 +200,21 @@ __global__ __launch_bounds__(256) void k_mmvq_q6k(const uint4* __restrict__ ql,
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s) {
     const int64_t nb = w.cols / kBlock;
-    const int64_t waves_wanted = w.rows;
-    int64_t blocks = (waves_wanted + 3) / 4;
-    if (blocks > 2048) blocks = 2048;
-    const dim3 grid((unsigned)blocks), block(256);
     const int id = (int)w.cols, od = (int)w.rows;
-    if (nb <= 64 * 4)
+    const dim3 block(256);
+    if (nb <= 64 * 4) {
+        const dim3 grid((unsigned)mmvq_grid<4>(w.rows));
         hipLaunchKernelGGL(k_mmvq_q6k<4>, grid, block, 0, s, w.gv_ql, w.gv_qh, w.gv_sc, w.gv_d,
                            pl.q, pl.D, id, od, out);
-    else if (nb <= 64 * 8)
+    } else if (nb <= 64 * 8) {
+        const dim3 grid((unsigned)mmvq_grid<8>(w.rows));
         hipLaunchKernelGGL(k_mmvq_q6k<8>, grid, block, 0, s, w.gv_ql, w.gv_qh, w.gv_sc, w.gv_d,
                            pl.q, pl.D, id, od, out);
-    else
+    } else {
+        const dim3 grid((unsigned)mmvq_grid<0>(w.rows));
         hipLaunchKernelGGL(k_mmvq_q6k<0>, grid, block, 0, s, w.gv_ql, w.gv_qh, w.gv_sc, w.gv_d,
                            pl.q, pl.D, id, od, out);
+    }
     return hipGetLastError();
 }
 

@@ -9,8 +9,10 @@
 // then per 32-block: amax = max|y|, D = amax / 127, q = clamp(rint(y / D),
 // -127, 127), S = sum(q); an all-zero block has D = 0, q = 0, S = 0.
 //
-// Geometry.  One workgroup of 4 waves per row; the row is swept in rounds of
-// 256 values, round r belonging to wave r % 4: in round r lane l owns the
+// Geometry.  One workgroup of 4 waves per row (per row segment for SwiGLU and
+// the standalone quantise when there are too few rows to fill the chip, as at
+// one token); the row is swept in rounds of 256 values, round r belonging to
+// wave r % 4: in round r lane l owns the
 // float4 at 256*r + 4*l, so each wave access is one
 // contiguous 1 KiB (the pages' rule that a full-width coalesced access must
 // never be broken), and the 8 consecutive lanes 8g..8g+7 hold exactly one
@@ -31,6 +33,8 @@
 // Rows n .. rows-1 of the plane (the padding to a multiple of 32 rows) are
 // written as zeros, so a plane's content never depends on what its slot held
 // before.
+#include <algorithm>
+
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -114,19 +118,22 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
                                                   float* __restrict__ y, int n, int d,
                                                   float eps, int8_t* __restrict__ q,
                                                   float* __restrict__ D,
-                                                  int32_t* __restrict__ S, int rows) {
-    constexpr int W = 4;   // waves per row
+                                                  int32_t* __restrict__ S, int rows,
+                                                  int rps) {
+    constexpr int W = 4;   // waves per row segment
     constexpr int U = 8;   // rounds of one wave whose loads are in flight together
     __shared__ double s_ss[W];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row = blockIdx.x;
     const int nb = d / kBlock;
-    const int rounds = d / kSuper;
-    const int my = (rounds - wave + W - 1) / W;   // rounds of this wave: wave + W*k, k < my
-    uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (int64_t)row * d);
-    float* Dr = D + (int64_t)row * nb;
-    int32_t* Sr = S + (int64_t)row * nb;
+    // this workgroup's rounds: [r0, r0 + rcount); RMSNorm always takes the whole row
+    const int r0 = blockIdx.y * rps;
+    const int rcount = min(rps, d / kSuper - r0);
+    const int my = (rcount - wave + W - 1) / W;   // rounds of this wave: r0 + wave + W*k, k < my
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (int64_t)row * d) + 64 * r0;
+    float* Dr = D + (int64_t)row * nb + 8 * r0;
+    int32_t* Sr = S + (int64_t)row * nb + 8 * r0;
     const int g = lane >> 3;
 
     if (row >= n) {  // padded tail rows: deterministic zeros
@@ -141,10 +148,11 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
         return;  // the whole workgroup takes this branch
     }
 
-    const float4* a4 = reinterpret_cast<const float4*>(a + (int64_t)row * d);
+    const float4* a4 = reinterpret_cast<const float4*>(a + (int64_t)row * d) + 64 * r0;
+    // RMSNorm: b is the weight vector (and r0 == 0); SwiGLU: b is the up row
     const float4* b4 = reinterpret_cast<const float4*>(
-        KIND == kProdRms ? b : (b ? b + (int64_t)row * d : nullptr));
-    float4* y4 = reinterpret_cast<float4*>(y + (int64_t)row * d);
+        KIND == kProdRms ? b : (KIND == kProdSwiglu ? b + (int64_t)row * d + 256 * r0 : nullptr));
+    float4* y4 = reinterpret_cast<float4*>(y + (int64_t)row * d) + 64 * r0;
 
     float scale = 0.0f;
     float4 xr[MAXR > 0 ? MAXR : 1];
@@ -234,17 +242,29 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
 template <int KIND, bool WY>
 hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, int64_t d,
                          float eps, const PlaneView& pl, hipStream_t s) {
-    const int per_wave = (int)((d / kSuper + 3) / 4);
-    dim3 grid((unsigned)pl.rows), block(256);
+    const int rounds = (int)(d / kSuper);
+    const int per_wave = (rounds + 3) / 4;
+    // Rows with no row-wide reduction (SwiGLU, standalone) are split into
+    // segments of at least 4 rounds when there are too few rows to fill the
+    // chip (decode); RMSNorm keeps one workgroup per row.
+    int segs = 1;
+    if (KIND != kProdRms) {
+        const int64_t want = (2048 + pl.rows - 1) / pl.rows;
+        segs = (int)std::min<int64_t>(want, (rounds + 3) / 4);
+        if (segs < 1) segs = 1;
+    }
+    const int rps = (rounds + segs - 1) / segs;
+    segs = (rounds + rps - 1) / rps;
+    const dim3 grid((unsigned)pl.rows, (unsigned)segs), block(256);
     if (KIND == kProdRms && per_wave <= 8) {
         hipLaunchKernelGGL((k_producer<KIND, WY, 8>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows, rps);
     } else if (KIND == kProdRms && per_wave <= 16) {
         hipLaunchKernelGGL((k_producer<KIND, WY, 16>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows, rps);
     } else {
         hipLaunchKernelGGL((k_producer<KIND, WY, 0>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows);
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows, rps);
     }
     return hipGetLastError();
 }
