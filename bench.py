@@ -359,6 +359,29 @@ def main():
     kernels["gemm_q4k"]["TOPS"] = round(achieved, 1)
     kernels["gemm_q6k"]["TOPS"] = round(q6_ops_launch / (q6_avg_us * 1e-6) / 1e12, 1)
 
+    # the same step captured once into a HIP graph and replayed (launch census
+    # from the library's counters during the capture)
+    st_a = mmq.mmq_stats(chain.ctx)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain.step()
+    st_b = mmq.mmq_stats(chain.ctx)
+    mmq.mmq_cache_clear(chain.ctx)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
+    graph_rec = {"ms_per_step": round(graph_ms, 3), "tops": round(ops / (graph_ms * 1e-3) / 1e12, 2),
+                 "launches_per_step": sum(st_b[k] - st_a[k] for k in st_b if k.startswith("launches_"))}
+    log(f"graph replay: {graph_ms:.2f} ms/step")
+
     traffic = measured_traffic()
     decode = None if args.no_decode else decode_gemv(mmq, torch, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
@@ -391,6 +414,7 @@ def main():
                      "algorithmic_bytes_per_launch": round(q4_alg_bytes), "avg_launch_us": round(q4_avg_us, 2),
                      "frac_of_f16_mfma_peak": round(achieved / PEAK_F16_TOPS, 4)},
         "kernels": kernels,
+        "graph": graph_rec,
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
         "decode_gemv": decode,
         "cpu_baseline": cpu,

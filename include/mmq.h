@@ -36,6 +36,17 @@
  *     library never aborts the process.
  *   * Not thread-safe per context; distinct contexts may be used from
  *     distinct threads.
+ *   * HIP graph capture [r60 2.2]: producers and consumers may be captured
+ *     while their stream is being captured.  Nothing is allocated during a
+ *     capture: a call whose plane slot would have to grow fails with
+ *     MMQ_E_ARG, so make the same calls once before capturing.  Cache
+ *     bookkeeping happens when a call is captured, not when the graph is
+ *     replayed; a replay rewrites the plane slots its calls used, so call
+ *     mmq_cache_clear() after the capture and after each replay before eager
+ *     calls look planes up again.  After any capture the context never frees
+ *     plane memory before mmq_destroy (a grown slot keeps its old memory), so
+ *     a graph stays valid for the context's lifetime; destroying the context
+ *     invalidates its graphs.
  */
 #ifndef MMQ_H
 #define MMQ_H

@@ -90,6 +90,11 @@ struct mmq_ctx {
     int64_t plane_bytes = 0;
     int64_t weight_bytes = 0;
     mmq_stats_t st{};
+    // Once any call was captured into a graph, slot memory the graph may
+    // reference is never freed before mmq_destroy: a grown slot's old memory
+    // is retired here instead.
+    bool captured = false;
+    std::vector<void*> retired;
 };
 
 struct mmq_weight {
@@ -104,9 +109,21 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(MMQ_E_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+// True while `s` is being captured into a HIP graph (launches are recorded,
+// not run; synchronising or allocating is not allowed).
+bool capturing(const mmq_ctx* c, hipStream_t s) {
+    if (c->dry) return false;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return st == hipStreamCaptureStatusActive;
+}
+
 int after_launch(mmq_ctx* c, hipError_t e, hipStream_t s, const char* what) {
     if (e != hipSuccess) return hip_fail(e, what);
-    if (c->flags & MMQ_CTX_SYNC_CHECK) {
+    if ((c->flags & MMQ_CTX_SYNC_CHECK) && !capturing(c, s)) {
         e = hipStreamSynchronize(s);
         if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e, what);
@@ -174,7 +191,8 @@ void drop_overlapping(mmq_ctx* c, const void* p, int64_t bytes) {
 
 // Pick an entry for (key, n, d), growing its slot if needed.  The entry is
 // not marked used until the caller commits it.
-int acquire_slot(mmq_ctx* c, const void* key, int64_t n, int64_t d, int* out_idx) {
+int acquire_slot(mmq_ctx* c, const void* key, int64_t n, int64_t d, bool in_capture,
+                 int* out_idx) {
     int idx = find_entry(c, key, n, d);
     if (idx < 0) {
         for (int i = 0; i < kSlots && idx < 0; ++i)
@@ -188,12 +206,20 @@ int acquire_slot(mmq_ctx* c, const void* key, int64_t n, int64_t d, int* out_idx
     const int64_t need = plane_bytes_for(n, d, nullptr, nullptr);
     Slot& s = c->slots[idx];
     if (s.cap < need) {
+        if (in_capture)
+            return fail(MMQ_E_ARG,
+                        "plane slot must grow to %lld bytes during stream capture, where nothing "
+                        "may be allocated; make the same calls once before capturing",
+                        (long long)need);
         const int64_t total = c->plane_bytes - s.cap + need;
         if (c->cap >= 0 && total > c->cap)
             return fail(MMQ_E_OOM, "plane scratch cap %lld bytes exceeded (need %lld in total)",
                         (long long)c->cap, (long long)total);
         if (!c->dry) {
-            if (s.mem) {
+            if (s.mem && c->captured) {
+                c->retired.push_back(s.mem);  // a captured graph may still use it
+                s.mem = nullptr;
+            } else if (s.mem) {
                 hipError_t e = hipFree(s.mem);
                 if (e != hipSuccess) return hip_fail(e, "hipFree(plane slot)");
                 s.mem = nullptr;
@@ -271,7 +297,9 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
     } else {
         drop_overlapping(c, a, bytes);
     }
-    if ((rc = acquire_slot(c, key, n, d, &idx))) return rc;
+    const bool in_capture = capturing(c, (hipStream_t)stream);
+    if ((rc = acquire_slot(c, key, n, d, in_capture, &idx))) return rc;
+    if (in_capture) c->captured = true;
     const bool dead = kind != kProdF32 && !write_y;
     commit_entry(c, idx, key, n, d, dead);
     if (dead) c->dead.push_back({(uintptr_t)y, (uintptr_t)y + (uintptr_t)bytes});
@@ -288,6 +316,7 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
 // Consumer side: the plane of (a, n, d), quantising it on a miss.
 int plane_for(mmq_ctx* c, const char* who, const float* a, int64_t n, int64_t d, void* stream,
               PlaneView* out) {
+    if (capturing(c, (hipStream_t)stream)) c->captured = true;
     int idx = find_entry(c, a, n, d);
     if (idx >= 0) {
         c->st.cache_hits++;
@@ -369,6 +398,7 @@ void mmq_destroy(mmq_ctx* c) {
         (void)hipDeviceSynchronize();
         for (Slot& s : c->slots)
             if (s.mem) (void)hipFree(s.mem);
+        for (void* p : c->retired) (void)hipFree(p);
     }
     delete c;
 }
