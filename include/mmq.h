@@ -99,6 +99,7 @@ typedef struct mmq_stats_t {
     int64_t cache_entries;          /* live table entries now                 */
     int64_t plane_bytes;            /* device bytes held by plane slots       */
     int64_t weight_bytes;           /* device bytes held by registered weights */
+    int64_t launches_mmvq_q4k;
 } mmq_stats_t;
 
 /* ---- context ----------------------------------------------------------- */
@@ -132,8 +133,9 @@ int64_t mmq_plane_rows(int64_t n);
  * into device tiles for the consumers named in `uses` (MMQ_USE_*; 0 means
  * every consumer the type supports).  cols % 256 == 0.  raw_host may be
  * freed on return.  Synchronises the device.
- * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE (unknown type, GEMV use on
- * q4_K), MMQ_E_OOM, MMQ_E_HIP. */
+ * The default uses: q4_K MMQ_USE_GEMM, q6_K MMQ_USE_GEMM | MMQ_USE_GEMV.
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE (unknown type), MMQ_E_OOM,
+ * MMQ_E_HIP. */
 int mmq_register_weight(mmq_ctx* ctx, int type, int64_t rows, int64_t cols,
                         const void* raw_host, unsigned uses, mmq_weight** out);
 
@@ -176,8 +178,16 @@ int mmq_gemm_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,
 int mmq_gemm_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,
                  float* out, void* stream);
 
-/* One-token q6_K GEMV (n == 1): out[o] = sum_k D[k/32] q[k] * w[o][k]. */
+/* One-token q6_K GEMV (n == 1): out[o] = sum_k D[k/32] q[k] * w[o][k].
+ * w must be registered with MMQ_USE_GEMV. */
 int mmvq_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
+             void* stream);
+
+/* One-token q4_K GEMV, the sibling decode arm of the same routing
+ * [d37 Excerpt B: each K-quant type has its own one-token arm].  Per
+ * 32-block: D * (d*sc_j * sum(q_w * q) - dmin*m_j * S).  w must be
+ * registered with MMQ_USE_GEMV. */
+int mmvq_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
              void* stream);
 
 /* ---- window boundary, hooks, statistics ---------------------------------- */

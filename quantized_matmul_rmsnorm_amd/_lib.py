@@ -41,7 +41,7 @@ EXPORTS = [
     "mmq_create", "mmq_destroy", "mmq_last_error", "mmq_set_scratch_cap", "mmq_plane_rows",
     "mmq_register_weight", "mmq_weight_free", "mmq_weight_bytes",
     "mmq_quant_rms", "mmq_quant_swiglu", "mmq_quant_f32",
-    "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k",
+    "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k", "mmvq_q4k",
     "mmq_cache_clear", "mmq_cache_invalidate", "mmq_plane_export", "mmq_stats",
 ]
 
@@ -57,7 +57,7 @@ class mmq_stats_t(ctypes.Structure):
         "launches_quant_rms", "launches_quant_swiglu", "launches_quant_f32",
         "launches_gemm_q4k", "launches_gemm_q6k", "launches_mmvq_q6k",
         "cache_hits", "cache_misses", "cache_refusals", "cache_entries",
-        "plane_bytes", "weight_bytes")]
+        "plane_bytes", "weight_bytes", "launches_mmvq_q4k")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -94,6 +94,7 @@ def _load():
         "mmq_gemm_q4k": (I, [P, P, P, I64, P, P]),
         "mmq_gemm_q6k": (I, [P, P, P, I64, P, P]),
         "mmvq_q6k": (I, [P, P, P, P, P]),
+        "mmvq_q4k": (I, [P, P, P, P, P]),
         "mmq_cache_clear": (None, [P]),
         "mmq_cache_invalidate": (I, [P, P]),
         "mmq_plane_export": (I, [P, P, I64, I64, I, P, P, P, P]),
@@ -221,6 +222,11 @@ def mmq_gemm_q6k(ctx, w, a, n: int, out, stream=None):
 def mmvq_q6k(ctx, w, a, out, stream=None):
     f = _f32() if not isinstance(a, int) else None
     return _check(lib.mmvq_q6k(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
+
+
+def mmvq_q4k(ctx, w, a, out, stream=None):
+    f = _f32() if not isinstance(a, int) else None
+    return _check(lib.mmvq_q4k(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
 
 
 def mmq_cache_clear(ctx) -> None:

@@ -423,8 +423,6 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     if (uses & ~(MMQ_USE_GEMM | MMQ_USE_GEMV))
         return fail(MMQ_E_ARG, "%s: unknown uses 0x%x", who, uses);
     if (uses == 0) uses = type == MMQ_Q4_K ? MMQ_USE_GEMM : (MMQ_USE_GEMM | MMQ_USE_GEMV);
-    if (type == MMQ_Q4_K && (uses & MMQ_USE_GEMV))
-        return fail(MMQ_E_TYPE, "%s: the one-token GEMV is provided for q6_K only", who);
 
     mmq_weight* h = new mmq_weight();
     h->ctx = c;
@@ -442,8 +440,10 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     const int64_t wa_b = w.rows_pad * cols * npart * 2;
     const int64_t dmr_b = og * nsb * (type == MMQ_Q4_K ? 64 : 32) * 4;
     const int64_t mf_b = type == MMQ_Q4_K ? og * nsb * 512 * 2 : 0;
-    const int64_t ql_b = rows * nb * 16, qh_b = rows * nb * 8, sc_b = rows * nb * 2,
-                  dv_b = rows * nsb * 4;
+    // one-token GEMV tiles: q6_K ql/qh/sc/d; q4_K nibbles (in ql), (sc, m)
+    // pairs (in sc) and (d, dmin) per superblock (in d), no qh
+    const int64_t ql_b = rows * nb * 16, qh_b = type == MMQ_Q6_K ? rows * nb * 8 : 0,
+                  sc_b = rows * nb * 2, dv_b = rows * nsb * (type == MMQ_Q6_K ? 4 : 8);
     // the matmul addresses its tiles with 32-bit buffer offsets
     if ((uses & MMQ_USE_GEMM) && wa_b > (int64_t)0xFFFFFFFF) {
         delete h;
@@ -495,7 +495,8 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     }
     if (uses & MMQ_USE_GEMV) {
         void *p1 = nullptr, *p2 = nullptr, *p3 = nullptr, *p4 = nullptr;
-        if (!dalloc(ql_b, &p1) || !dalloc(qh_b, &p2) || !dalloc(sc_b, &p3) || !dalloc(dv_b, &p4)) {
+        if (!dalloc(ql_b, &p1) || (qh_b && !dalloc(qh_b, &p2)) || !dalloc(sc_b, &p3) ||
+            !dalloc(dv_b, &p4)) {
             cleanup();
             return fail(MMQ_E_OOM, "%s: GEMV tiles", who);
         }
@@ -580,6 +581,19 @@ int mmvq_q6k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
     return after_launch(c, launch_mmvq_q6k(w->w, pl, out, s), s, who);
+}
+
+int mmvq_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* stream) {
+    const char* who = "mmvq_q4k";
+    int rc = consume_check(c, w, a, 1, out, MMQ_Q4_K, MMQ_USE_GEMV, who);
+    if (rc) return rc;
+    if ((rc = use_device(c))) return rc;
+    PlaneView pl;
+    if ((rc = plane_for(c, who, a, 1, w->w.cols, stream, &pl))) return rc;
+    c->st.launches_mmvq_q4k++;
+    if (c->dry) return MMQ_OK;
+    hipStream_t s = (hipStream_t)stream;
+    return after_launch(c, launch_mmvq_q4k(w->w, pl, out, s), s, who);
 }
 
 void mmq_cache_clear(mmq_ctx* c) {

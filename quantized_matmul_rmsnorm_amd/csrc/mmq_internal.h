@@ -35,11 +35,11 @@ struct WeightDev {
     _Float16* wa = nullptr;   // f16 integer-valued A fragments
     float* dmr = nullptr;     // per (row group, superblock) scales, fragment order
     _Float16* mfrag = nullptr;// q4_K only: 6-bit mins as f16, fragment order
-    // one-token GEMV (q6_K)
-    uint4* gv_ql = nullptr;   // [rows][cols/32] low nibbles
-    uint2* gv_qh = nullptr;   // [rows][cols/32] high bit pairs
-    int16_t* gv_sc = nullptr; // [rows][cols/32] two int8 sub-scales
-    float* gv_d = nullptr;    // [rows][cols/256]
+    // one-token GEMV
+    uint4* gv_ql = nullptr;   // [rows][cols/32] 4-bit codes (q6_K: their low nibbles)
+    uint2* gv_qh = nullptr;   // q6_K: [rows][cols/32] high bit pairs
+    int16_t* gv_sc = nullptr; // [rows][cols/32] q6_K: two int8 sub-scales; q4_K: sc | m << 8
+    float* gv_d = nullptr;    // q6_K: [rows][cols/256] d; q4_K: [rows][cols/256][2] d, dmin
     int64_t bytes = 0;
 };
 
@@ -57,6 +57,8 @@ hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStr
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
                        hipStream_t s);
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
+                           hipStream_t s);
+hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
 
 }  // namespace mmq

@@ -1,47 +1,82 @@
-// mmvq.hip -- one-token q6_K GEMV over a q8 activation plane (gfx950).
+// mmvq.hip -- one-token q6_K / q4_K GEMV over a q8 activation plane (gfx950).
 //
-// Method ("72 · D3-7 ...", section 2 and Excerpts A/A2): at one token the
+// Method ("72 · D3-7 ...", section 2 and Excerpts A, A2, B): at one token the
 // matmul is a weight-streaming GEMV; the activation is quantised once into a
 // q8 plane (shared through the plane cache by every consumer of the same
 // buffer) and each output row is an integer dot of that plane with the row's
-// 6-bit weights, rescaled per 16-element half by the int8 sub-scale and per
-// 32-block by D * d.
+// packed weights, rescaled per block.  Each K-quant type has its own
+// one-token arm:
+//   q6_K: per 32-block, D * d * (sc0*I0 + sc1*I1), I0/I1 the dots of the
+//         16-value halves of (q_w - 32) with the codes;
+//   q4_K: per 32-block j of a superblock, D * (d*sc_j * I - dmin*m_j * S),
+//         I = sum(q_w * q), S the plane's code sum of the block.
 //
 // Design for CDNA4.  The kernel is bound by streaming the packed weights from
-// HBM, so the weights are read exactly once, in 1 KiB-per-wave coalesced
-// pieces, and the integer work runs on v_dot4_i32_i8 (4 int8 products per
-// instruction).  Each wave keeps its slice of the activation plane in
-// registers for its whole lifetime -- lane l owns 32-blocks l, l+64, ... -- and
-// walks output rows grid-stride; per row and block the lane reads 16 B of low
-// nibbles, 8 B of high bit pairs and 2 B of sub-scales (the registration
-// layout of repack.hip), rebuilds four packed dwords of 6-bit codes per
-// 16-element half with masks and shifts, and dots them with its codes.  The
-// "- 32" of the q6_K code is applied through the activation: the dot
-// accumulator starts at -32 * sum(q) of the half, computed once per lane.
-// One f32 FMA per block adds (D * d) * (sc0*I0 + sc1*I1); a wave-wide sum per
-// row finishes the output.
+// HBM, so the weights are read exactly once, with non-temporal loads, in
+// 1 KiB-per-wave coalesced pieces, and the integer work runs on
+// v_dot4_i32_i8 (4 int8 products per instruction).  Each wave keeps its slice
+// of the activation plane in registers for its whole lifetime -- lane l owns
+// 32-blocks l, l+64, ... -- and walks output rows grid-stride; per row and
+// block the lane reads the block's packed codes (16 B of 4-bit codes, plus
+// 8 B of high bit pairs for q6_K) and its scales (the registration layout of
+// repack.hip), rebuilds packed bytes with masks and shifts and dots them with
+// its codes.  For q6_K the "- 32" of the code is applied through the
+// activation: the dot accumulator starts at -32 * sum(q) of the half,
+// computed once per lane.  One f32 expression per block adds the block's
+// term; a wave-wide sum per row finishes the output.
 #include "mmq_internal.h"
 
 namespace mmq {
 namespace {
 
-struct ActBlock {
-    uint4 q0, q1;   // codes 0..15, 16..31
-    float D;
-    int c0, c1;     // -32 * sum of codes in each half
-};
-
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-__device__ __forceinline__ ActBlock load_act(const int8_t* Q, const float* Dp, int b, int nb) {
-    ActBlock a;
-    if (b < nb) {
-        const uint4* p = reinterpret_cast<const uint4*>(Q + (int64_t)b * kBlock);
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 nt_load(const uint4* p) {
+    const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 nt_load(const uint2* p) {
+    const u2v v = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(p));
+    return make_uint2(v.x, v.y);
+}
+
+struct MvArgs {
+    const uint4* ql;      // [od][nb] packed 4-bit codes
+    const uint2* qh;      // q6_K: [od][nb] high bit pairs
+    const int16_t* sc;    // [od][nb] scales
+    const float* dv;      // q6_K: [od][nsb] d; q4_K: [od][nsb][2] d, dmin
+    const int8_t* Q;      // plane codes (row 0)
+    const float* Dp;      // plane scales
+    const int32_t* Sp;    // plane sums
+    int id, od;
+    float* out;
+};
+
+// ---- q6_K arm ----
+struct Q6 {
+    struct Act {
+        uint4 q0, q1;   // codes 0..15, 16..31
+        float D;
+        int c0, c1;     // -32 * sum of codes in each half
+    };
+    struct W {
+        uint4 L;
+        uint2 H;
+        int16_t s;
+        float d;
+    };
+    static __device__ __forceinline__ Act act(const MvArgs& g, int b) {
+        Act a;
+        const uint4* p = reinterpret_cast<const uint4*>(g.Q + (int64_t)b * kBlock);
         a.q0 = p[0];
         a.q1 = p[1];
-        a.D = Dp[b];
+        a.D = g.Dp[b];
         const uint32_t ones = 0x01010101u;
         int s0 = dot4(a.q0.x, ones, 0); s0 = dot4(a.q0.y, ones, s0);
         s0 = dot4(a.q0.z, ones, s0);    s0 = dot4(a.q0.w, ones, s0);
@@ -49,34 +84,83 @@ __device__ __forceinline__ ActBlock load_act(const int8_t* Q, const float* Dp, i
         s1 = dot4(a.q1.z, ones, s1);    s1 = dot4(a.q1.w, ones, s1);
         a.c0 = -32 * s0;
         a.c1 = -32 * s1;
-    } else {
-        a.q0 = make_uint4(0, 0, 0, 0);
-        a.q1 = a.q0;
-        a.D = 0.0f;
-        a.c0 = a.c1 = 0;
+        return a;
     }
-    return a;
-}
+    static __device__ __forceinline__ W load(const MvArgs& g, int64_t o, int b, int nb, int nsb) {
+        W w;
+        const int64_t i = o * nb + b;
+        w.L = nt_load(g.ql + i);
+        w.H = nt_load(g.qh + i);
+        w.s = __builtin_nontemporal_load(g.sc + i);
+        w.d = __builtin_nontemporal_load(g.dv + o * nsb + (b >> 3));
+        return w;
+    }
+    static __device__ __forceinline__ float term(const Act& a, const W& w) {
+        const uint32_t m4 = 0x0F0F0F0Fu, m2 = 0x30303030u;
+        const uint4 L = w.L;
+        const uint2 H = w.H;
+        int i0 = a.c0;
+        i0 = dot4((L.x & m4) | ((H.x << 4) & m2), a.q0.x, i0);
+        i0 = dot4(((L.x >> 4) & m4) | ((H.x << 2) & m2), a.q0.y, i0);
+        i0 = dot4((L.y & m4) | (H.x & m2), a.q0.z, i0);
+        i0 = dot4(((L.y >> 4) & m4) | ((H.x >> 2) & m2), a.q0.w, i0);
+        int i1 = a.c1;
+        i1 = dot4((L.z & m4) | ((H.y << 4) & m2), a.q1.x, i1);
+        i1 = dot4(((L.z >> 4) & m4) | ((H.y << 2) & m2), a.q1.y, i1);
+        i1 = dot4((L.w & m4) | (H.y & m2), a.q1.z, i1);
+        i1 = dot4(((L.w >> 4) & m4) | ((H.y >> 2) & m2), a.q1.w, i1);
+        const int s0 = (int)(int8_t)(w.s & 0xFF);
+        const int s1 = (int)(int8_t)((uint16_t)w.s >> 8);
+        const int ic = s0 * i0 + s1 * i1;
+        return (a.D * w.d) * (float)ic;
+    }
+};
 
-// (D * d) * (sc0 * I0 + sc1 * I1) for one 32-block of one row.
-__device__ __forceinline__ float block_term(const ActBlock& a, uint4 L, uint2 H, int16_t sc,
-                                            float d) {
-    const uint32_t m4 = 0x0F0F0F0Fu, m2 = 0x30303030u;
-    int i0 = a.c0;
-    i0 = dot4((L.x & m4) | ((H.x << 4) & m2), a.q0.x, i0);
-    i0 = dot4(((L.x >> 4) & m4) | ((H.x << 2) & m2), a.q0.y, i0);
-    i0 = dot4((L.y & m4) | (H.x & m2), a.q0.z, i0);
-    i0 = dot4(((L.y >> 4) & m4) | ((H.x >> 2) & m2), a.q0.w, i0);
-    int i1 = a.c1;
-    i1 = dot4((L.z & m4) | ((H.y << 4) & m2), a.q1.x, i1);
-    i1 = dot4(((L.z >> 4) & m4) | ((H.y << 2) & m2), a.q1.y, i1);
-    i1 = dot4((L.w & m4) | (H.y & m2), a.q1.z, i1);
-    i1 = dot4(((L.w >> 4) & m4) | ((H.y >> 2) & m2), a.q1.w, i1);
-    const int s0 = (int)(int8_t)(sc & 0xFF);
-    const int s1 = (int)(int8_t)((uint16_t)sc >> 8);
-    const int ic = s0 * i0 + s1 * i1;
-    return (a.D * d) * (float)ic;
-}
+// ---- q4_K arm ----
+struct Q4 {
+    struct Act {
+        uint4 q0, q1;
+        float D;
+        int S;          // the plane's code sum of the block
+    };
+    struct W {
+        uint4 L;
+        int16_t s;      // sc | m << 8
+        f2v dd;         // d, dmin
+    };
+    static __device__ __forceinline__ Act act(const MvArgs& g, int b) {
+        Act a;
+        const uint4* p = reinterpret_cast<const uint4*>(g.Q + (int64_t)b * kBlock);
+        a.q0 = p[0];
+        a.q1 = p[1];
+        a.D = g.Dp[b];
+        a.S = g.Sp[b];
+        return a;
+    }
+    static __device__ __forceinline__ W load(const MvArgs& g, int64_t o, int b, int nb, int nsb) {
+        W w;
+        const int64_t i = o * nb + b;
+        w.L = nt_load(g.ql + i);
+        w.s = __builtin_nontemporal_load(g.sc + i);
+        w.dd = __builtin_nontemporal_load(reinterpret_cast<const f2v*>(g.dv) + o * nsb + (b >> 3));
+        return w;
+    }
+    static __device__ __forceinline__ float term(const Act& a, const W& w) {
+        const uint32_t m4 = 0x0F0F0F0Fu;
+        const uint4 L = w.L;
+        int i = dot4(L.x & m4, a.q0.x, 0);
+        i = dot4((L.x >> 4) & m4, a.q0.y, i);
+        i = dot4(L.y & m4, a.q0.z, i);
+        i = dot4((L.y >> 4) & m4, a.q0.w, i);
+        i = dot4(L.z & m4, a.q1.x, i);
+        i = dot4((L.z >> 4) & m4, a.q1.y, i);
+        i = dot4(L.w & m4, a.q1.z, i);
+        i = dot4((L.w >> 4) & m4, a.q1.w, i);
+        const float sc = (float)(w.s & 0xFF);
+        const float mn = (float)(((uint16_t)w.s >> 8) & 0xFF);
+        return a.D * ((w.dd.x * sc) * (float)i - (w.dd.y * mn) * (float)a.S);
+    }
+};
 
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
@@ -100,49 +184,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 // the current row's registers for that block are consumed, so a row's loads
 // are in flight while the previous row is reduced.
 // MAXR == 0: blocks are re-read from the plane for every row (any length).
-template <int MAXR>
-__global__ __launch_bounds__(256) void k_mmvq_q6k(const uint4* __restrict__ ql,
-                                                  const uint2* __restrict__ qh,
-                                                  const int16_t* __restrict__ sc,
-                                                  const float* __restrict__ dv,
-                                                  const int8_t* __restrict__ Q,
-                                                  const float* __restrict__ Dp, int id, int od,
-                                                  float* __restrict__ out) {
+template <class F, int MAXR>
+__global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * 4;
+    const int id = g.id, od = g.od;
     const int nb = id / kBlock;
     const int nsb = id / kSuper;
     const int rounds = (nb + 63) / 64;
 
     if constexpr (MAXR > 0) {
-        ActBlock act[MAXR];
-        uint4 L[MAXR];
-        uint2 H[MAXR];
-        int16_t S[MAXR];
-        float Dw[MAXR];
+        typename F::Act act[MAXR];
+        typename F::W w[MAXR];
 #pragma unroll
         for (int r = 0; r < MAXR; ++r)
-            if (r < rounds) act[r] = load_act(Q, Dp, 64 * r + lane, nb);
-        auto load_block = [&](int o, int r) {
-            const int b = 64 * r + lane;
-            const int64_t rb = (int64_t)o * nb;
-            {
-                typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
-                const u4v l4 = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(ql) + rb + b);
-                const u2v h2 = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(qh) + rb + b);
-                L[r] = make_uint4(l4.x, l4.y, l4.z, l4.w);
-                H[r] = make_uint2(h2.x, h2.y);
-            }
-            S[r] = __builtin_nontemporal_load(&sc[rb + b]);
-            Dw[r] = __builtin_nontemporal_load(&dv[(int64_t)o * nsb + (b >> 3)]);
-        };
+            if (r < rounds && 64 * r + lane < nb) act[r] = F::act(g, 64 * r + lane);
         int o = wave;
         if (o < od) {
 #pragma unroll
             for (int r = 0; r < MAXR; ++r)
-                if (r < rounds && 64 * r + lane < nb) load_block(o, r);
+                if (r < rounds && 64 * r + lane < nb) w[r] = F::load(g, o, 64 * r + lane, nb, nsb);
         }
         for (; o < od; o += nwaves) {
             const int on = o + nwaves;
@@ -150,27 +212,22 @@ __global__ __launch_bounds__(256) void k_mmvq_q6k(const uint4* __restrict__ ql,
 #pragma unroll
             for (int r = 0; r < MAXR; ++r) {
                 if (r < rounds && 64 * r + lane < nb) {
-                    acc += block_term(act[r], L[r], H[r], S[r], Dw[r]);
-                    if (on < od) load_block(on, r);
+                    acc += F::term(act[r], w[r]);
+                    if (on < od) w[r] = F::load(g, on, 64 * r + lane, nb, nsb);
                 }
             }
             acc = wave_sum(acc);
-            if (lane == 0) out[o] = acc;
+            if (lane == 0) g.out[o] = acc;
         }
     } else {
         for (int o = wave; o < od; o += nwaves) {
-            const int64_t rb = (int64_t)o * nb;
             float acc = 0.0f;
             for (int r = 0; r < rounds; ++r) {
                 const int b = 64 * r + lane;
-                if (b < nb) {
-                    const ActBlock a = load_act(Q, Dp, b, nb);
-                    acc += block_term(a, ql[rb + b], qh[rb + b], sc[rb + b],
-                                      dv[(int64_t)o * nsb + (b >> 3)]);
-                }
+                if (b < nb) acc += F::term(F::act(g, b), F::load(g, o, b, nb, nsb));
             }
             acc = wave_sum(acc);
-            if (lane == 0) out[o] = acc;
+            if (lane == 0) g.out[o] = acc;
         }
     }
 }
@@ -178,14 +235,15 @@ __global__ __launch_bounds__(256) void k_mmvq_q6k(const uint4* __restrict__ ql,
 // Workgroups of one launch: every row gets a wave when the rows fit in two
 // rounds of resident waves; larger matrices get exactly the resident waves
 // (each then walks rows grid-stride with its plane slice loaded once).
-template <int MAXR>
+template <class F, int MAXR>
 int64_t mmvq_grid(int64_t rows) {
     static int per_cu = -1, n_cu = 0;
     if (per_cu < 0) {
         int dev = 0, blk = 0;
         (void)hipGetDevice(&dev);
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq_q6k<MAXR>, 256, 0) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq<F, MAXR>, 256, 0) !=
+            hipSuccess)
             blk = 1;
         per_cu = blk > 0 ? blk : 1;
         if (n_cu <= 0) n_cu = 256;
@@ -195,27 +253,40 @@ int64_t mmvq_grid(int64_t rows) {
     return want <= 2 * resident ? want : resident;
 }
 
+template <class F>
+hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipStream_t s) {
+    MvArgs g;
+    g.ql = w.gv_ql;
+    g.qh = w.gv_qh;
+    g.sc = w.gv_sc;
+    g.dv = w.gv_d;
+    g.Q = pl.q;
+    g.Dp = pl.D;
+    g.Sp = pl.S;
+    g.id = (int)w.cols;
+    g.od = (int)w.rows;
+    g.out = out;
+    const int64_t nb = w.cols / kBlock;
+    const dim3 block(256);
+    if (nb <= 64 * 4)
+        hipLaunchKernelGGL((k_mmvq<F, 4>), dim3((unsigned)mmvq_grid<F, 4>(w.rows)), block, 0, s, g);
+    else if (nb <= 64 * 8)
+        hipLaunchKernelGGL((k_mmvq<F, 8>), dim3((unsigned)mmvq_grid<F, 8>(w.rows)), block, 0, s, g);
+    else
+        hipLaunchKernelGGL((k_mmvq<F, 0>), dim3((unsigned)mmvq_grid<F, 0>(w.rows)), block, 0, s, g);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s) {
-    const int64_t nb = w.cols / kBlock;
-    const int id = (int)w.cols, od = (int)w.rows;
-    const dim3 block(256);
-    if (nb <= 64 * 4) {
-        const dim3 grid((unsigned)mmvq_grid<4>(w.rows));
-        hipLaunchKernelGGL(k_mmvq_q6k<4>, grid, block, 0, s, w.gv_ql, w.gv_qh, w.gv_sc, w.gv_d,
-                           pl.q, pl.D, id, od, out);
-    } else if (nb <= 64 * 8) {
-        const dim3 grid((unsigned)mmvq_grid<8>(w.rows));
-        hipLaunchKernelGGL(k_mmvq_q6k<8>, grid, block, 0, s, w.gv_ql, w.gv_qh, w.gv_sc, w.gv_d,
-                           pl.q, pl.D, id, od, out);
-    } else {
-        const dim3 grid((unsigned)mmvq_grid<0>(w.rows));
-        hipLaunchKernelGGL(k_mmvq_q6k<0>, grid, block, 0, s, w.gv_ql, w.gv_qh, w.gv_sc, w.gv_d,
-                           pl.q, pl.D, id, od, out);
-    }
-    return hipGetLastError();
+    return launch_mmvq<Q6>(w, pl, out, s);
+}
+
+hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,
+                           hipStream_t s) {
+    return launch_mmvq<Q4>(w, pl, out, s);
 }
 
 }  // namespace mmq

@@ -36,6 +36,10 @@
 //                    i' = 16u + i
 //   sc[o][b]  int16: low byte = sub-scale of w_0..15, high byte = of w_16..31
 //   d[o][sb]  f32
+// One-token GEMV tiles (q4_K), per row o and 32-block b = 8*sb + j:
+//   ql[o][b]  uint4: the 4-bit codes, same byte order as the q6_K low nibbles
+//   sc[o][b]  int16: sc_j | m_j << 8
+//   d[o][sb]  f32 pair: d, dmin
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -183,6 +187,35 @@ __global__ void k_repack_q6k_gemv(const uint8_t* __restrict__ raw, int64_t rows,
     }
 }
 
+__global__ void k_repack_q4k_gemv(const uint8_t* __restrict__ raw, int64_t rows, int64_t cols,
+                                  uint4* __restrict__ ql, int16_t* __restrict__ scv,
+                                  float* __restrict__ dv) {
+    const int64_t nsb = cols / kSuper;
+    const int64_t nb = cols / kBlock;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nsb) return;
+    const int64_t o = idx / nsb, sb = idx % nsb;
+    const uint8_t* blk = raw + idx * 144;
+    float d, dmin;
+    int sc[8], mn[8];
+    q4k_decode(blk, d, dmin, sc, mn);
+    dv[2 * (o * nsb + sb)] = d;
+    dv[2 * (o * nsb + sb) + 1] = dmin;
+    for (int j = 0; j < 8; ++j) {
+        uint32_t L[4];
+        for (int u = 0; u < 4; ++u) {
+            uint32_t v = 0;
+            for (int i = 0; i < 4; ++i)
+                v |= (uint32_t)(q4k_quant(blk, 32 * j + 8 * u + i) |
+                                (q4k_quant(blk, 32 * j + 8 * u + i + 4) << 4)) << (8 * i);
+            L[u] = v;
+        }
+        const int64_t b = sb * 8 + j;
+        ql[o * nb + b] = make_uint4(L[0], L[1], L[2], L[3]);
+        scv[o * nb + b] = (int16_t)((uint16_t)sc[j] | ((uint16_t)mn[j] << 8));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s) {
@@ -200,8 +233,12 @@ hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStr
 hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s) {
     const int64_t total = w.rows * (w.cols / kSuper);
     const dim3 block(128), grid((unsigned)((total + 127) / 128));
-    hipLaunchKernelGGL(k_repack_q6k_gemv, grid, block, 0, s, raw_dev, w.rows, w.cols, w.gv_ql,
-                       w.gv_qh, w.gv_sc, w.gv_d);
+    if (w.type == 12)
+        hipLaunchKernelGGL(k_repack_q4k_gemv, grid, block, 0, s, raw_dev, w.rows, w.cols, w.gv_ql,
+                           w.gv_sc, w.gv_d);
+    else
+        hipLaunchKernelGGL(k_repack_q6k_gemv, grid, block, 0, s, raw_dev, w.rows, w.cols, w.gv_ql,
+                           w.gv_qh, w.gv_sc, w.gv_d);
     return hipGetLastError();
 }
 

@@ -87,9 +87,12 @@ def test_registration_validation(ctx):
     assert _status(mmq.mmq_register_weight, ctx, 13, 4, 256, raw) == mmq.MMQ_E_TYPE
     assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 300, raw) == mmq.MMQ_E_SHAPE
     assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 0, 256, raw) == mmq.MMQ_E_SHAPE
-    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw,
-                   mmq.MMQ_USE_GEMV) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw, 0x4) == mmq.MMQ_E_ARG
     w4 = _w(ctx, mmq.MMQ_Q4_K, 512, 256)
+    # q4_K one-token GEMV layout: 16 B of codes + 2 B (sc, m) per 32 weights, (d, dmin) per 256
+    w4v = _w(ctx, mmq.MMQ_Q4_K, 300, 512, mmq.MMQ_USE_GEMV)
+    assert mmq.mmq_weight_bytes(w4v) == 300 * 16 * (16 + 2) + 300 * 2 * 8
+    mmq.mmq_weight_free(w4v)
     w6 = _w(ctx, mmq.MMQ_Q6_K, 1000, 512)
     # q4_K: f16 tiles (2 B/weight) + scales + mins; q6_K adds the GEMV layout
     assert mmq.mmq_weight_bytes(w4) == 512 * 256 * 2 + 16 * 1 * 64 * 4 + 16 * 1 * 512 * 2
@@ -110,6 +113,12 @@ def test_consumer_type_checks(ctx):
     assert _status(mmq.mmq_gemm_q6k, ctx, w4, A, 8, O) == mmq.MMQ_E_TYPE
     assert _status(mmq.mmq_gemm_q4k, ctx, w6g, A, 8, O) == mmq.MMQ_E_TYPE
     assert _status(mmq.mmvq_q6k, ctx, w6g, A, O) == mmq.MMQ_E_TYPE     # not registered for GEMV
+    assert _status(mmq.mmvq_q4k, ctx, w4, A, O) == mmq.MMQ_E_TYPE      # q4_K default: matmul only
+    assert _status(mmq.mmvq_q4k, ctx, w6g, A, O) == mmq.MMQ_E_TYPE     # wrong type
+    w4v = _w(ctx, mmq.MMQ_Q4_K, 64, 256, mmq.MMQ_USE_GEMV)
+    assert _status(mmq.mmvq_q6k, ctx, w4v, A, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmvq_q4k, ctx, w4v, A, O) == mmq.MMQ_OK
+    assert mmq.mmq_stats(ctx)["launches_mmvq_q4k"] == 1
     assert _status(mmq.mmq_gemm_q4k, ctx, w4, A, 0, O) == mmq.MMQ_E_SHAPE
     other = mmq.mmq_create(0, mmq.MMQ_CTX_DRYRUN)
     try:

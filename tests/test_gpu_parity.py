@@ -201,6 +201,65 @@ def test_mmvq_parity(ctx, od, id_):
     mmq.mmq_weight_free(w)
 
 
+@pytest.mark.parametrize("od,id_", [(1000, 5120), (64, 256), (300, 13824), (33, 20480),
+                                    (5120, 5120), (13824, 5120)])
+def test_mmvq_q4k_parity(ctx, od, id_):
+    rng = synth.rng_for("test", od, f"mmvq4{id_}")
+    raw = synth.q4k_weights(rng, od, id_)
+    w = mmq.mmq_register_weight(ctx, 12, od, id_, raw, 2)
+    ah = _act("mmvq4", 1, id_)
+    a = dev_tensor(ah)
+    out = torch.full((od,), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmvq_q4k(ctx, w, a, out)
+    q, D, S = export_plane(ctx, a, 1, id_)
+    ref = oracle.gemm("q4_K", q, D, S, raw, od, id_)[0]
+    assert_gemm_close(out.cpu().numpy(), ref, f"mmvq q4_K {od}x{id_}")
+    mmq.mmq_weight_free(w)
+
+
+def test_decode_ffn_chain_q4k_gate_up_q6k_down(ctx):
+    """14B decode FFN at one token: RMSNorm(5120) -> plane shared by gate and up
+    (q4_K GEMV, two hits) -> SwiGLU(13824) of their outputs -> plane -> down
+    (q6_K GEMV, one hit).  Each GEMV is checked on the plane it consumed."""
+    c = mmq.mmq_create(0, 0)
+    try:
+        xh = synth.activations(synth.rng_for("decode14b", 1, "x"), 1, 5120)
+        wn = synth.rms_weight(synth.rng_for("decode14b", 1, "norm"), 5120)
+        shapes = {"gate": ("q4_K", 13824, 5120), "up": ("q4_K", 13824, 5120),
+                  "down": ("q6_K", 5120, 13824)}
+        raws, ws = {}, {}
+        for k, (wt, od, id_) in shapes.items():
+            raws[k] = synth.weights(wt, synth.rng_for("decode14b", 1, k), od, id_)
+            ws[k] = mmq.mmq_register_weight(c, WT[wt], od, id_, raws[k], mmq.MMQ_USE_GEMV)
+        y = torch.empty((1, 5120), dtype=torch.float32, device="cuda")
+        ysw = torch.empty((1, 13824), dtype=torch.float32, device="cuda")
+        outs = {k: torch.full((od,), float("nan"), dtype=torch.float32, device="cuda")
+                for k, (_, od, _) in shapes.items()}
+        mmq.mmq_quant_rms(c, dev_tensor(xh), dev_tensor(wn), y, 1, 5120, EPS, 0)
+        mmq.mmvq_q4k(c, ws["gate"], y, outs["gate"])
+        mmq.mmvq_q4k(c, ws["up"], y, outs["up"])
+        mmq.mmq_quant_swiglu(c, outs["gate"].view(1, -1), outs["up"].view(1, -1), ysw, 1, 13824, 0)
+        mmq.mmvq_q6k(c, ws["down"], ysw, outs["down"])
+        st = mmq.mmq_stats(c)
+        assert st["cache_hits"] == 3 and st["cache_misses"] == 0 and st["launches_quant_f32"] == 0
+        assert st["launches_mmvq_q4k"] == 2 and st["launches_mmvq_q6k"] == 1
+        p1 = export_plane(c, y, 1, 5120)
+        p2 = export_plane(c, ysw, 1, 13824)
+        assert_fused_close(p1, oracle.quantize(oracle.rmsnorm(xh, wn, EPS)), what="decode rms")
+        g, u = outs["gate"].cpu().numpy(), outs["up"].cpu().numpy()
+        for k in ("gate", "up"):
+            ref = oracle.gemm("q4_K", *p1, raws[k], 13824, 5120)[0]
+            assert_gemm_close(outs[k].cpu().numpy(), ref, k)
+        # the SwiGLU plane is the fused quantisation of the GPU's own gate/up outputs
+        assert_fused_close(p2, oracle.quantize(oracle.swiglu(g[None], u[None])), what="decode swiglu")
+        ref = oracle.gemm("q6_K", *p2, raws["down"], 5120, 13824)[0]
+        assert_gemm_close(outs["down"].cpu().numpy(), ref, "down")
+        for wt in ws.values():
+            mmq.mmq_weight_free(wt)
+    finally:
+        mmq.mmq_destroy(c)
+
+
 def test_mmvq_decode_chain_full_size(ctx):
     """14B decode: rms(5120) plane shared by attn_v and lm_head (hits), SwiGLU(13824)
     plane feeding ffn_down; lm_head checked on sampled rows."""
