@@ -81,7 +81,10 @@ extern "C" {
 #define MMQ_USE_GEMM 1u       /* prefill matmul (any n)                      */
 #define MMQ_USE_GEMV 2u       /* one-token GEMV (q6_K only)                  */
 
-#define MMQ_PLANE_ROWS 32     /* plane rows are padded to this multiple     */
+#define MMQ_PLANE_ROWS 32
+#define MMQ_WRITE_AUTO (-1)     /* write_y: skip when allowed, degrade otherwise */
+#define MMQ_FOREIGN_F32 1       /* mmq_register_foreign_consumer kinds */
+#define MMQ_FOREIGN_QUANT 2     /* plane rows are padded to this multiple     */
 
 typedef struct mmq_ctx mmq_ctx;
 typedef struct mmq_weight mmq_weight;
@@ -100,6 +103,8 @@ typedef struct mmq_stats_t {
     int64_t plane_bytes;            /* device bytes held by plane slots       */
     int64_t weight_bytes;           /* device bytes held by registered weights */
     int64_t launches_mmvq_q4k;
+    int64_t degraded_writes;        /* skip-write requests that wrote y (mixed consumers) */
+    int64_t unfused_fallbacks;      /* MMQ_WRITE_AUTO producers without plane memory      */
 } mmq_stats_t;
 
 /* ---- context ----------------------------------------------------------- */
@@ -147,8 +152,16 @@ int64_t mmq_weight_bytes(const mmq_weight* w);
 
 /* ---- producers [r52 2.2, 3.2; d37 Excerpt C] ----------------------------
  * Each quantises its f32 result in registers into a plane and records the
- * plane under key y.  write_y != 0 also stores y [n][d] (the entry is live);
+ * plane under key y.  write_y == 1 also stores y [n][d] (the entry is live);
  * write_y == 0 never touches y (the entry is dead: y is only the key).
+ * The degradation ladder [r52 3.1; r60 3.3]: skip-write is honoured only
+ * while the context is plane-only (mmq_plane_only); after
+ * mmq_register_foreign_consumer, write_y == 0 writes y and the plane
+ * (counted in degraded_writes).  write_y == MMQ_WRITE_AUTO skips the write
+ * when allowed and, if no plane memory can be had (scratch cap or device
+ * memory), falls back to writing y alone with no plane recorded (counted in
+ * unfused_fallbacks; returns MMQ_OK) -- every tier is correct, a lower one
+ * only costs time.
  * Preconditions: d % 256 == 0, n >= 1; x/gate/up/y 16-byte aligned.
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_OOM, MMQ_E_HIP. */
 
@@ -189,6 +202,18 @@ int mmvq_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
  * registered with MMQ_USE_GEMV. */
 int mmvq_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
              void* stream);
+
+/* ---- consumer set [r60 3.2-3.3: the registration-time nb_bt_only flag] -- */
+
+/* Declare a consumer outside this library that reads producer outputs as
+ * f32 (MMQ_FOREIGN_F32: a 2-D f32 weight's matmul; MMQ_FOREIGN_QUANT: a
+ * weight type with no plane path).  Clears the plane-only predicate for the
+ * context's lifetime; prints one stderr line the first time.
+ * Errors: MMQ_E_ARG. */
+int mmq_register_foreign_consumer(mmq_ctx* ctx, int kind);
+
+/* 1 while every consumer reads planes (skip-write allowed), else 0. */
+int mmq_plane_only(const mmq_ctx* ctx);
 
 /* ---- window boundary, hooks, statistics ---------------------------------- */
 

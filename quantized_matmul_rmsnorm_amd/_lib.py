@@ -35,6 +35,9 @@ MMQ_CTX_DRYRUN = 2
 MMQ_USE_GEMM = 1
 MMQ_USE_GEMV = 2
 MMQ_PLANE_ROWS = 32
+MMQ_WRITE_AUTO = -1
+MMQ_FOREIGN_F32 = 1
+MMQ_FOREIGN_QUANT = 2
 
 # Every symbol include/mmq.h declares (checked by the CPU tests).
 EXPORTS = [
@@ -42,6 +45,7 @@ EXPORTS = [
     "mmq_register_weight", "mmq_weight_free", "mmq_weight_bytes",
     "mmq_quant_rms", "mmq_quant_swiglu", "mmq_quant_f32",
     "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k", "mmvq_q4k",
+    "mmq_register_foreign_consumer", "mmq_plane_only",
     "mmq_cache_clear", "mmq_cache_invalidate", "mmq_plane_export", "mmq_stats",
 ]
 
@@ -57,7 +61,8 @@ class mmq_stats_t(ctypes.Structure):
         "launches_quant_rms", "launches_quant_swiglu", "launches_quant_f32",
         "launches_gemm_q4k", "launches_gemm_q6k", "launches_mmvq_q6k",
         "cache_hits", "cache_misses", "cache_refusals", "cache_entries",
-        "plane_bytes", "weight_bytes", "launches_mmvq_q4k")]
+        "plane_bytes", "weight_bytes", "launches_mmvq_q4k", "degraded_writes",
+        "unfused_fallbacks")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -95,6 +100,8 @@ def _load():
         "mmq_gemm_q6k": (I, [P, P, P, I64, P, P]),
         "mmvq_q6k": (I, [P, P, P, P, P]),
         "mmvq_q4k": (I, [P, P, P, P, P]),
+        "mmq_register_foreign_consumer": (I, [P, I]),
+        "mmq_plane_only": (I, [P]),
         "mmq_cache_clear": (None, [P]),
         "mmq_cache_invalidate": (I, [P, P]),
         "mmq_plane_export": (I, [P, P, I64, I64, I, P, P, P, P]),
@@ -227,6 +234,14 @@ def mmvq_q6k(ctx, w, a, out, stream=None):
 def mmvq_q4k(ctx, w, a, out, stream=None):
     f = _f32() if not isinstance(a, int) else None
     return _check(lib.mmvq_q4k(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
+
+
+def mmq_register_foreign_consumer(ctx, kind: int) -> None:
+    _check(lib.mmq_register_foreign_consumer(ctx, kind))
+
+
+def mmq_plane_only(ctx) -> bool:
+    return bool(lib.mmq_plane_only(ctx))
 
 
 def mmq_cache_clear(ctx) -> None:

@@ -95,6 +95,11 @@ struct mmq_ctx {
     // is retired here instead.
     bool captured = false;
     std::vector<void*> retired;
+    // Registration-time consumer-set predicate: true while every consumer of
+    // producer outputs reads planes.  A consumer that reads the f32 output
+    // directly (declared with mmq_register_foreign_consumer) clears it, and
+    // skip-write producers then degrade to writing y.
+    bool plane_only = true;
 };
 
 struct mmq_weight {
@@ -285,6 +290,15 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
     if (!a || !aligned16(a) || (kind != kProdF32 && (!b || !aligned16(b))) ||
         (kind != kProdF32 && (!y || !aligned16(y))))
         return fail(MMQ_E_ARG, "%s: null or non-16-byte-aligned pointer", who);
+    if (kind != kProdF32 && write_y != 0 && write_y != 1 && write_y != MMQ_WRITE_AUTO)
+        return fail(MMQ_E_ARG, "%s: write_y=%d (0, 1 or MMQ_WRITE_AUTO)", who, write_y);
+    // The degradation ladder: skip-write (y never written) only while every
+    // consumer reads planes; otherwise write y and the plane.
+    const int auto_mode = write_y == MMQ_WRITE_AUTO;
+    const bool want_skip = kind != kProdF32 && (write_y == 0 || write_y == MMQ_WRITE_AUTO);
+    const bool skip = want_skip && c->plane_only;
+    if (want_skip && !skip) c->st.degraded_writes++;
+    write_y = kind == kProdF32 ? 0 : (skip ? 0 : 1);
     const int64_t bytes = n * d * 4;
     const void* key = kind == kProdF32 ? (const void*)a : (const void*)y;
     if (kind == kProdF32 && overlaps_dead(c, a, bytes)) return refuse_dead(c, who, a);
@@ -298,7 +312,22 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
         drop_overlapping(c, a, bytes);
     }
     const bool in_capture = capturing(c, (hipStream_t)stream);
-    if ((rc = acquire_slot(c, key, n, d, in_capture, &idx))) return rc;
+    if ((rc = acquire_slot(c, key, n, d, in_capture, &idx))) {
+        // Last tier: with MMQ_WRITE_AUTO a producer that cannot get plane
+        // memory writes y alone and records nothing; consumers then quantise
+        // y themselves (and fail loudly if that cannot be done either).
+        if (rc != MMQ_E_OOM || auto_mode == 0 || kind == kProdF32) return rc;
+        c->st.unfused_fallbacks++;
+        if (kind == kProdRms) c->st.launches_quant_rms++;
+        else c->st.launches_quant_swiglu++;
+        revive(c, y, bytes);
+        fprintf(stderr, "libmmq: %s: no plane memory (%s); wrote y without a plane\n", who,
+                mmq_last_error());
+        if (c->dry) return MMQ_OK;
+        hipStream_t s = (hipStream_t)stream;
+        const PlaneView none{};
+        return after_launch(c, launch_producer(kind, a, b, y, n, d, eps, true, none, s), s, who);
+    }
     if (in_capture) c->captured = true;
     const bool dead = kind != kProdF32 && !write_y;
     commit_entry(c, idx, key, n, d, dead);
@@ -595,6 +624,21 @@ int mmvq_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     hipStream_t s = (hipStream_t)stream;
     return after_launch(c, launch_mmvq_q4k(w->w, pl, out, s), s, who);
 }
+
+int mmq_register_foreign_consumer(mmq_ctx* c, int kind) {
+    if (!c) return fail(MMQ_E_ARG, "mmq_register_foreign_consumer: null context");
+    if (kind != MMQ_FOREIGN_F32 && kind != MMQ_FOREIGN_QUANT)
+        return fail(MMQ_E_ARG, "mmq_register_foreign_consumer: unknown kind %d", kind);
+    if (c->plane_only)
+        fprintf(stderr,
+                "libmmq: a consumer that reads f32 activations directly was registered (%s); "
+                "skip-write producers now write y as well\n",
+                kind == MMQ_FOREIGN_F32 ? "2-D f32 weight" : "weight type without a plane path");
+    c->plane_only = false;
+    return MMQ_OK;
+}
+
+int mmq_plane_only(const mmq_ctx* c) { return c && c->plane_only ? 1 : 0; }
 
 void mmq_cache_clear(mmq_ctx* c) {
     if (!c) return;

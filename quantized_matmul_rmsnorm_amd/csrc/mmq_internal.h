@@ -43,7 +43,8 @@ struct WeightDev {
     int64_t bytes = 0;
 };
 
-// ---- producers (quant.hip) ----
+// ---- producers (quant.hip); a PlaneView with q == nullptr: RMSNorm / SwiGLU
+// write y only (the unfused tier) ----
 enum ProducerKind { kProdRms = 0, kProdSwiglu = 1, kProdF32 = 2 };
 hipError_t launch_producer(ProducerKind kind, const float* a, const float* b, float* y,
                            int64_t n, int64_t d, float eps, bool write_y,

@@ -112,7 +112,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // One workgroup (4 waves) per row; round r of the row belongs to wave r % 4.
 // MAXR > 0: a wave's rounds (at most MAXR) stay in registers between the
 // RMSNorm passes.
-template <int KIND, bool WRITE_Y, int MAXR>
+template <int KIND, bool WRITE_Y, int MAXR, bool QUANT = true>
 __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
                                                   const float* __restrict__ b,
                                                   float* __restrict__ y, int n, int d,
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
     int32_t* Sr = S + (int64_t)row * nb + 8 * r0;
     const int g = lane >> 3;
 
-    if (row >= n) {  // padded tail rows: deterministic zeros
+    if (QUANT && row >= n) {  // padded tail rows: deterministic zeros
         for (int k = 0; k < my; ++k) {
             const int r = wave + W * k;
             q4[64 * r + lane] = 0u;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
             v = xin;
         }
         if constexpr (WRITE_Y) y4[64 * r + lane] = v;
-        quant4(v, lane, q4 + 64 * r + lane, Dr + 8 * r + g, Sr + 8 * r + g);
+        if constexpr (QUANT) quant4(v, lane, q4 + 64 * r + lane, Dr + 8 * r + g, Sr + 8 * r + g);
     };
 
     if constexpr (MAXR > 0) {
@@ -239,9 +239,10 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
     }
 }
 
-template <int KIND, bool WY>
+template <int KIND, bool WY, bool QUANT = true>
 hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, int64_t d,
                          float eps, const PlaneView& pl, hipStream_t s) {
+    const int64_t rows = QUANT ? pl.rows : n;   // without a plane there is no padding
     const int rounds = (int)(d / kSuper);
     const int per_wave = (rounds + 3) / 4;
     // Rows with no row-wide reduction (SwiGLU, standalone) are split into
@@ -249,22 +250,22 @@ hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, in
     // chip (decode); RMSNorm keeps one workgroup per row.
     int segs = 1;
     if (KIND != kProdRms) {
-        const int64_t want = (2048 + pl.rows - 1) / pl.rows;
+        const int64_t want = (2048 + rows - 1) / rows;
         segs = (int)std::min<int64_t>(want, (rounds + 3) / 4);
         if (segs < 1) segs = 1;
     }
     const int rps = (rounds + segs - 1) / segs;
     segs = (rounds + rps - 1) / rps;
-    const dim3 grid((unsigned)pl.rows, (unsigned)segs), block(256);
+    const dim3 grid((unsigned)rows, (unsigned)segs), block(256);
     if (KIND == kProdRms && per_wave <= 8) {
-        hipLaunchKernelGGL((k_producer<KIND, WY, 8>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows, rps);
+        hipLaunchKernelGGL((k_producer<KIND, WY, 8, QUANT>), grid, block, 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
     } else if (KIND == kProdRms && per_wave <= 16) {
-        hipLaunchKernelGGL((k_producer<KIND, WY, 16>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows, rps);
+        hipLaunchKernelGGL((k_producer<KIND, WY, 16, QUANT>), grid, block, 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
     } else {
-        hipLaunchKernelGGL((k_producer<KIND, WY, 0>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)pl.rows, rps);
+        hipLaunchKernelGGL((k_producer<KIND, WY, 0, QUANT>), grid, block, 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
     }
     return hipGetLastError();
 }
@@ -274,6 +275,12 @@ hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, in
 hipError_t launch_producer(ProducerKind kind, const float* a, const float* b, float* y,
                            int64_t n, int64_t d, float eps, bool write_y,
                            const PlaneView& pl, hipStream_t s) {
+    if (pl.q == nullptr) {   // unfused: y only, no plane (RMSNorm, SwiGLU)
+        if (kind == kProdRms) return dispatch_maxr<kProdRms, true, false>(a, b, y, n, d, eps, pl, s);
+        if (kind == kProdSwiglu)
+            return dispatch_maxr<kProdSwiglu, true, false>(a, b, y, n, d, eps, pl, s);
+        return hipErrorInvalidValue;
+    }
     switch (kind) {
         case kProdRms:
             return write_y ? dispatch_maxr<kProdRms, true>(a, b, y, n, d, eps, pl, s)

@@ -215,3 +215,46 @@ def test_export_needs_a_plane_and_a_device(ctx):
     mmq.mmq_quant_f32(ctx, 0x100000, 8, 256)
     rc = _lib.lib.mmq_plane_export(ctx, 0x100000, 8, 256, 0, 0x1000, 0x2000, 0x3000, None)
     assert rc == mmq.MMQ_E_DEVICE
+
+
+def test_degradation_ladder_follows_the_consumer_set(ctx, capfd):
+    """Skip-write is honoured only while every consumer reads planes; a foreign
+    (f32-reading) consumer makes write_y=0 and MMQ_WRITE_AUTO write y as well."""
+    w = _w(ctx, mmq.MMQ_Q4_K, 128, 256)
+    X, W, Y, O = 0x100000, 0x200000, 0x1000000, 0x3000000
+    assert mmq.mmq_plane_only(ctx)
+    mmq.mmq_quant_rms(ctx, X, W, Y, 8, 256, 1e-6, mmq.MMQ_WRITE_AUTO)
+    assert _status(mmq.mmq_quant_f32, ctx, Y, 8, 256) == mmq.MMQ_E_DEAD_WRITE   # skipped: dead
+    mmq.mmq_cache_clear(ctx)
+    assert _status(mmq.mmq_register_foreign_consumer, ctx, 7) == mmq.MMQ_E_ARG
+    capfd.readouterr()
+    mmq.mmq_register_foreign_consumer(ctx, mmq.MMQ_FOREIGN_F32)
+    assert "f32" in capfd.readouterr().err
+    assert not mmq.mmq_plane_only(ctx)
+    mmq.mmq_quant_rms(ctx, X, W, Y, 8, 256, 1e-6, 0)        # degraded: y written, entry live
+    mmq.mmq_gemm_q4k(ctx, w, Y, 8, O)                        # hit
+    assert _status(mmq.mmq_quant_f32, ctx, Y, 8, 256) == mmq.MMQ_OK    # not dead
+    mmq.mmq_quant_swiglu(ctx, X, W, Y, 8, 256, mmq.MMQ_WRITE_AUTO)
+    st = mmq.mmq_stats(ctx)
+    assert st["degraded_writes"] == 2 and st["cache_refusals"] == 1 and st["cache_hits"] == 1
+    assert _status(mmq.mmq_quant_rms, ctx, X, W, Y, 8, 256, 1e-6, 2) == mmq.MMQ_E_ARG
+
+
+def test_auto_falls_back_to_unfused_without_plane_memory(ctx, capfd):
+    """MMQ_WRITE_AUTO: no plane memory -> y written alone, nothing recorded; a
+    consumer then quantises y itself and fails loudly if it cannot either."""
+    w = _w(ctx, mmq.MMQ_Q4_K, 128, 256)
+    X, W, Y, O = 0x100000, 0x200000, 0x1000000, 0x3000000
+    mmq.mmq_set_scratch_cap(ctx, 0)
+    capfd.readouterr()
+    assert _status(mmq.mmq_quant_rms, ctx, X, W, Y, 8, 256, 1e-6, mmq.MMQ_WRITE_AUTO) == mmq.MMQ_OK
+    assert "without a plane" in capfd.readouterr().err
+    st = mmq.mmq_stats(ctx)
+    assert st["unfused_fallbacks"] == 1 and st["cache_entries"] == 0
+    assert st["launches_quant_rms"] == 1
+    assert _status(mmq.mmq_gemm_q4k, ctx, w, Y, 8, O) == mmq.MMQ_E_OOM     # miss, no memory
+    # an explicit skip-write request does not fall back: it fails before any launch
+    assert _status(mmq.mmq_quant_rms, ctx, X, W, Y, 8, 256, 1e-6, 0) == mmq.MMQ_E_OOM
+    mmq.mmq_set_scratch_cap(ctx, -1)
+    mmq.mmq_quant_rms(ctx, X, W, Y, 8, 256, 1e-6, mmq.MMQ_WRITE_AUTO)
+    assert mmq.mmq_stats(ctx)["cache_entries"] == 1

@@ -367,3 +367,60 @@ def test_dead_write_refusal_launches_nothing():
         mmq.mmq_weight_free(w)
     finally:
         mmq.mmq_destroy(c)
+
+
+# ------------------------------------------------------------------ degradation ladder on the device
+def test_degraded_skip_write_writes_y_and_the_same_plane():
+    """After a foreign consumer is declared, write_y=0 writes y and records a
+    live plane that is byte-identical to the write_y=1 plane."""
+    n, d = 37, 3584
+    xh = synth.activations(synth.rng_for("ladder", n, "x"), n, d)
+    wn = synth.rms_weight(synth.rng_for("ladder", n, "w"), d)
+    ref_c = mmq.mmq_create(0, 0)
+    deg_c = mmq.mmq_create(0, 0)
+    try:
+        x, w = dev_tensor(xh), dev_tensor(wn)
+        y1 = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")
+        y0 = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")
+        mmq.mmq_quant_rms(ref_c, x, w, y1, n, d, EPS, 1)
+        mmq.mmq_register_foreign_consumer(deg_c, mmq.MMQ_FOREIGN_QUANT)
+        mmq.mmq_quant_rms(deg_c, x, w, y0, n, d, EPS, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)
+        for a, b in zip(export_plane(deg_c, y0, n, d), export_plane(ref_c, y1, n, d)):
+            assert np.array_equal(a, b)
+        assert mmq.mmq_stats(deg_c)["degraded_writes"] == 1
+        mmq.mmq_quant_f32(deg_c, y0, n, d)      # live: re-quantising is allowed
+    finally:
+        mmq.mmq_destroy(ref_c)
+        mmq.mmq_destroy(deg_c)
+
+
+@pytest.mark.parametrize("kind", ["rms", "swiglu"])
+def test_auto_without_plane_memory_writes_y_only(kind):
+    """MMQ_WRITE_AUTO with no plane memory allowed: the unfused tier writes y
+    (checked against the oracle's f32 producer) and records no plane."""
+    n, d = 40, 2560
+    c = mmq.mmq_create(0, 0)
+    try:
+        mmq.mmq_set_scratch_cap(c, 0)
+        y = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")
+        if kind == "rms":
+            xh = synth.activations(synth.rng_for("unfused", n, "x"), n, d)
+            wn = synth.rms_weight(synth.rng_for("unfused", n, "w"), d)
+            mmq.mmq_quant_rms(c, dev_tensor(xh), dev_tensor(wn), y, n, d, EPS, mmq.MMQ_WRITE_AUTO)
+            ref = oracle.rmsnorm(xh, wn, EPS)
+        else:
+            gh = synth.activations(synth.rng_for("unfused", n, "g"), n, d)
+            uh = synth.activations(synth.rng_for("unfused", n, "u"), n, d)
+            mmq.mmq_quant_swiglu(c, dev_tensor(gh), dev_tensor(uh), y, n, d, mmq.MMQ_WRITE_AUTO)
+            ref = oracle.swiglu(gh, uh)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        # same expressions as the oracle; only the f64 sum order (rms) or the
+        # device expf (swiglu) may move a value by a few ulp
+        np.testing.assert_allclose(got, ref, rtol=4e-7, atol=1e-30)
+        st = mmq.mmq_stats(c)
+        assert st["unfused_fallbacks"] == 1 and st["cache_entries"] == 0 and st["plane_bytes"] == 0
+    finally:
+        mmq.mmq_destroy(c)
