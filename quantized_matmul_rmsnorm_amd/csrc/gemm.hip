@@ -39,6 +39,8 @@
 // rescale FMAs in the gaps.  Outputs are stored
 // only for t < n and o < rows.  Workgroups are mapped so that each XCD works
 // on a contiguous group of output x token tiles (shared L2).
+#include <algorithm>
+
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -78,11 +80,17 @@ __device__ __forceinline__ half8 i8x8_to_f16(uint32_t x, uint32_t y) {
 // logical tiles so that the workgroups resident on one XCD (and its L2) share
 // weight and activation tiles.  Within the range, tiles are rastered in groups
 // of kGroupO output tiles with the token tile varying slowest inside a group.
-__device__ __forceinline__ void tile_of(int n_ttiles, int n_otiles, int& t_tile, int& o_tile) {
+// With a K split the logical index runs split-major, so the workgroups of one
+// XCD share a split (its weight and plane columns).
+__device__ __forceinline__ void tile_of(int n_ttiles, int n_otiles, int& t_tile, int& o_tile,
+                                        int& split) {
     const int nwg = gridDim.x;
     const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
     const int per = nwg >> 3, rem = nwg & 7;
-    const int L = xcd * per + min(xcd, rem) + li;
+    int L = xcd * per + min(xcd, rem) + li;
+    const int tiles = n_ttiles * n_otiles;
+    split = L / tiles;
+    L -= split * tiles;
     const int gsize = kGroupO * n_ttiles;
     const int group = L / gsize, r = L % gsize;
     const int go = min(kGroupO, n_otiles - group * kGroupO);
@@ -116,6 +124,8 @@ struct GemmArgs {
     float* out;           // [n][od]
     uint32_t wa_bytes, dmr_bytes, mfrag_bytes, q_bytes, ds_bytes;
     int n, plane_rows, id, od, n_ttiles, n_otiles;
+    int sb_per;           // superblocks per K split (all of them without a split)
+    int64_t part_stride;  // floats between the partial outputs of two splits
 };
 
 // The matmul kernel.  RA: depth of the weight-fragment register ring (the
@@ -140,8 +150,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     const int ogl = wave & 3;
     const int th = wave >> 2;
 
-    int t_tile, o_tile;
-    tile_of(g.n_ttiles, g.n_otiles, t_tile, o_tile);
+    int t_tile, o_tile, split;
+    tile_of(g.n_ttiles, g.n_otiles, t_tile, o_tile, split);
     const int t0 = t_tile * 128;
     const int og0 = o_tile * 4;
     const int id = g.id;
@@ -222,22 +232,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) res[i][r] = 0.0f;
 
-    const int nch = nb / CH;     // even: id is a multiple of 256
+    // this workgroup's K range: superblocks [sb0, sb1), blocks [8*sb0, b_end),
+    // chunks [c0, c_end); every split has at least one superblock
+    const int sb0 = split * g.sb_per;
+    const int sb1 = min(nsb, sb0 + g.sb_per);
+    const int b_end = sb1 * 8;
+    const int c0 = sb0 * SBCH, c_end = sb1 * SBCH;
 #pragma unroll
-    for (int b = 0; b < PD; ++b) load_a(b, b);   // nb >= 8 > PD
-    load_chunk(0, true);
-    store_chunk(0, 0, true, true);
-    load_chunk(1, false);
+    for (int b = 0; b < PD; ++b) load_a(8 * sb0 + b, b);   // 8 blocks per split > PD; slot b % RA
+    load_chunk(c0, true);
+    store_chunk(c0, 0, true, true);
+    load_chunk(c0 + 1, false);
     __syncthreads();
 
-    for (int sb = 0; sb < nsb; ++sb) {
+    for (int sb = sb0; sb < sb1; ++sb) {
 #pragma unroll
         for (int cc = 0; cc < SBCH; ++cc) {
             const int c = sb * SBCH + cc;
             const int buf = cc & 1;
             // stage chunk c+1 (loaded one chunk ago), load chunk c+2
-            store_chunk(min(c + 1, nch - 1), buf ^ 1, (cc + 1) % SBCH == 0, c + 1 < nch);
-            load_chunk(min(c + 2, nch - 1), cc % SBCH == 0);
+            store_chunk(min(c + 1, c_end - 1), buf ^ 1, (cc + 1) % SBCH == 0, c + 1 < c_end);
+            load_chunk(min(c + 2, c_end - 1), cc % SBCH == 0);
             half8 mf;
             if (Q4K && cc == SBCH - 1)
                 mf = bload<half8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
@@ -290,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
             for (int jj = 0; jj < CH; ++jj) {
                 const int j = cc * CH + jj;            // block within the superblock
                 const int b = sb * 8 + j;
-                load_a(min(b + PD, nb - 1), (j + PD) % RA);   // clamped: no branch, always in bounds
+                load_a(min(b + PD, b_end - 1), (j + PD) % RA);   // clamped: no branch, in bounds
                 if (jj + 1 < CH) read_b(jj + 1, bfr[(jj + 1) & 1]);
                 __builtin_amdgcn_s_setprio(1);   // wave priority only (not a queue priority)
                 mfma_block(j % RA, bfr[jj & 1], X[jj & 1]);
@@ -330,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     for (int i = 0; i < 2; ++i) {
         const int64_t t = t0 + (2 * th + i) * 32 + (lane & 31);
         if (t >= g.n) continue;
-        float* orow = g.out + t * (int64_t)od;
+        float* orow = g.out + split * g.part_stride + t * (int64_t)od;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t o = (int64_t)(og0 + ogl) * 32 + 8 * q + 4 * (lane >> 5);
@@ -346,10 +361,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     }
 }
 
+// Sum of the K-split partials in split order (deterministic): out[i] =
+// part[0][i] + part[1][i] + ...
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part,
+                                                      float* __restrict__ out, int splits,
+                                                      int64_t count) {
+    const int64_t n4 = count / 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 acc = reinterpret_cast<const float4*>(part)[i];
+        for (int k = 1; k < splits; ++k) {
+            const float4 v = reinterpret_cast<const float4*>(part + k * count)[i];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        reinterpret_cast<float4*>(out)[i] = acc;
+    }
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        float acc = part[i];
+        for (int k = 1; k < splits; ++k) acc += part[k * count + i];
+        out[i] = acc;
+    }
+}
+
 }  // namespace
 
+// K splits for a matmul of n tokens: only when the output tiles fill less
+// than one round of the chip, and then the count that minimises rounds per
+// split (each split keeps at least 4 superblocks).
+int gemm_splits(int64_t rows_pad, int64_t cols, int64_t n, int n_cu) {
+    const int64_t tiles = ((n + 127) / 128) * (rows_pad / 128);
+    if (n_cu <= 0 || tiles >= n_cu) return 1;
+    const int64_t nsb = cols / kSuper;
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(64, nsb / 4));
+    int best = 1;
+    double best_cost = (double)((tiles + n_cu - 1) / n_cu);
+    for (int64_t sp = 2; sp <= smax; ++sp) {
+        const int64_t per = (nsb + sp - 1) / sp;
+        const int64_t real = (nsb + per - 1) / per;
+        const double cost = (double)((tiles * real + n_cu - 1) / n_cu) / (double)real;
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = (int)real;
+        }
+    }
+    return best;
+}
+
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
-                       hipStream_t s) {
+                       float* part, int splits, hipStream_t s) {
     GemmArgs a;
     a.wa = (const half8*)w.wa;
     a.dmr = w.dmr;
@@ -357,9 +416,13 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.q = pl.q;
     a.D = pl.D;
     a.S = pl.S;
-    a.out = out;
     const int npart = w.type == 12 ? 1 : 2;
     const int64_t nsb = w.cols / kSuper, og = w.rows_pad / 32;
+    if (splits < 1 || part == nullptr) splits = 1;
+    a.sb_per = (int)((nsb + splits - 1) / splits);
+    splits = (int)((nsb + a.sb_per - 1) / a.sb_per);
+    a.out = splits > 1 ? part : out;
+    a.part_stride = splits > 1 ? n * w.rows : 0;
     a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * npart * 2);
     a.dmr_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 64 : 32) * 4);
     a.mfrag_bytes = w.type == 12 ? (uint32_t)(og * nsb * 512 * 2) : 0u;
@@ -370,14 +433,17 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.id = (int)w.cols;
     a.od = (int)w.rows;
     a.n_ttiles = (int)((n + 127) / 128);
-    if (w.type == 12) {
-        a.n_otiles = (int)(w.rows_pad / 128);
-        const dim3 grid((unsigned)(a.n_ttiles * a.n_otiles)), block(kThreads);
+    a.n_otiles = (int)(w.rows_pad / 128);
+    const dim3 grid((unsigned)(a.n_ttiles * a.n_otiles * splits)), block(kThreads);
+    if (w.type == 12)
         hipLaunchKernelGGL((k_gemm_da<true>), grid, block, 0, s, a);
-    } else {
-        a.n_otiles = (int)(w.rows_pad / 128);
-        const dim3 grid((unsigned)(a.n_ttiles * a.n_otiles)), block(kThreads);
+    else
         hipLaunchKernelGGL((k_gemm_da<false>), grid, block, 0, s, a);
+    if (splits > 1) {
+        const int64_t count = n * w.rows;
+        const int64_t want = (count / 4 + 255) / 256;
+        const dim3 rg((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 4096)));
+        hipLaunchKernelGGL(k_split_reduce, rg, dim3(256), 0, s, part, out, splits, count);
     }
     return hipGetLastError();
 }

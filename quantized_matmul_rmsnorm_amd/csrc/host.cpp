@@ -100,6 +100,9 @@ struct mmq_ctx {
     // directly (declared with mmq_register_foreign_consumer) clears it, and
     // skip-write producers then degrade to writing y.
     bool plane_only = true;
+    int n_cu = 256;              // compute units (K-split heuristic)
+    void* part = nullptr;        // K-split partial outputs, grow-only
+    int64_t part_cap = 0;
 };
 
 struct mmq_weight {
@@ -415,6 +418,7 @@ int mmq_create(int device, unsigned flags, mmq_ctx** out) {
             return fail(MMQ_E_DEVICE, "mmq_create: hipSetDevice(%d) failed", device);
         }
         c->device = device;
+        if (prop.multiProcessorCount > 0) c->n_cu = prop.multiProcessorCount;
     }
     *out = c;
     return MMQ_OK;
@@ -428,6 +432,7 @@ void mmq_destroy(mmq_ctx* c) {
         for (Slot& s : c->slots)
             if (s.mem) (void)hipFree(s.mem);
         for (void* p : c->retired) (void)hipFree(p);
+        if (c->part) (void)hipFree(c->part);
     }
     delete c;
 }
@@ -571,6 +576,36 @@ int mmq_quant_f32(mmq_ctx* c, const float* x, int64_t n, int64_t d, void* stream
     return produce(c, kProdF32, "mmq_quant_f32", x, nullptr, nullptr, n, d, 0.0f, 0, stream);
 }
 
+// Grow-only scratch for K-split partials (counted against the scratch cap
+// with the plane slots; never grown during a capture, retired if captured).
+static int acquire_part(mmq_ctx* c, int64_t bytes, bool in_capture, const char* who) {
+    if (bytes <= c->part_cap) return MMQ_OK;
+    if (in_capture)
+        return fail(MMQ_E_ARG, "%s: split-K scratch must grow to %lld bytes during stream "
+                    "capture; make the same calls once before capturing", who, (long long)bytes);
+    const int64_t total = c->plane_bytes - c->part_cap + bytes;
+    if (c->cap >= 0 && total > c->cap)
+        return fail(MMQ_E_OOM, "%s: scratch cap %lld bytes exceeded by split-K partials", who,
+                    (long long)c->cap);
+    if (!c->dry) {
+        if (c->part && c->captured) c->retired.push_back(c->part);
+        else if (c->part) (void)hipFree(c->part);
+        c->part = nullptr;
+        void* m = nullptr;
+        if (hipMalloc(&m, (size_t)bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            c->plane_bytes -= c->part_cap;
+            c->part_cap = 0;
+            return fail(MMQ_E_OOM, "%s: hipMalloc of %lld bytes of split-K scratch failed", who,
+                        (long long)bytes);
+        }
+        c->part = m;
+    }
+    c->plane_bytes += bytes - c->part_cap;
+    c->part_cap = bytes;
+    return MMQ_OK;
+}
+
 static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,
                        void* stream, int type, const char* who) {
     int rc = consume_check(c, w, a, n, out, type, MMQ_USE_GEMM, who);
@@ -580,13 +615,18 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
         return fail(MMQ_E_SHAPE, "%s: plane of %lld x %lld codes exceeds 2 GiB; split the tokens",
                     who, (long long)n, (long long)w->w.cols);
     if ((rc = use_device(c))) return rc;
+    const int splits = gemm_splits(w->w.rows_pad, w->w.cols, n, c->n_cu);
+    if (splits > 1 &&
+        (rc = acquire_part(c, (int64_t)splits * n * w->w.rows * 4,
+                           capturing(c, (hipStream_t)stream), who)))
+        return rc;
     PlaneView pl;
     if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;
     if (type == MMQ_Q4_K) c->st.launches_gemm_q4k++;
     else c->st.launches_gemm_q6k++;
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
-    return after_launch(c, launch_gemm(w->w, pl, n, out, s), s, who);
+    return after_launch(c, launch_gemm(w->w, pl, n, out, (float*)c->part, splits, s), s, who);
 }
 
 int mmq_gemm_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,

@@ -55,8 +55,12 @@ hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStr
 hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s);
 
 // ---- consumers ----
+// K splits the matmul uses for n tokens on n_cu compute units (1: none);
+// with splits > 1 the partials go to part [splits][n][rows] and are summed
+// into out in split order by a second kernel.
+int gemm_splits(int64_t rows_pad, int64_t cols, int64_t n, int n_cu);
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
-                       hipStream_t s);
+                       float* part, int splits, hipStream_t s);
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
 hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,

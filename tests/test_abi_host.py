@@ -258,3 +258,29 @@ def test_auto_falls_back_to_unfused_without_plane_memory(ctx, capfd):
     mmq.mmq_set_scratch_cap(ctx, -1)
     mmq.mmq_quant_rms(ctx, X, W, Y, 8, 256, 1e-6, mmq.MMQ_WRITE_AUTO)
     assert mmq.mmq_stats(ctx)["cache_entries"] == 1
+
+
+def test_split_k_scratch_is_checked_before_any_launch(ctx):
+    """A matmul with few output tiles holds K-split partials in the context's
+    scratch; a cap that cannot hold them fails before anything is enqueued."""
+    w = _w(ctx, mmq.MMQ_Q6_K, 3584, 18944, mmq.MMQ_USE_GEMM)
+    A, O = 0x100000, 0x200000
+    plane = mmq.mmq_plane_rows(8) * 18944 * 5 // 4
+    mmq.mmq_set_scratch_cap(ctx, plane + 3584 * 8 * 4)        # room for one split only
+    st0 = mmq.mmq_stats(ctx)
+    assert _status(mmq.mmq_gemm_q6k, ctx, w, A, 8, O) == mmq.MMQ_E_OOM
+    st1 = mmq.mmq_stats(ctx)
+    assert st1["launches_gemm_q6k"] == st0["launches_gemm_q6k"]
+    assert st1["cache_misses"] == st0["cache_misses"] and st1["launches_quant_f32"] == 0
+    mmq.mmq_set_scratch_cap(ctx, -1)
+    mmq.mmq_gemm_q6k(ctx, w, A, 8, O)
+    part = mmq.mmq_stats(ctx)["plane_bytes"] - plane
+    assert part % (3584 * 8 * 4) == 0 and part // (3584 * 8 * 4) >= 2
+    # many output tiles: no split, no partials
+    c2 = mmq.mmq_create(0, mmq.MMQ_CTX_DRYRUN)
+    try:
+        w2 = _w(c2, mmq.MMQ_Q4_K, 18944, 3584, mmq.MMQ_USE_GEMM)
+        mmq.mmq_gemm_q4k(c2, w2, A, 3314, O)
+        assert mmq.mmq_stats(c2)["plane_bytes"] == mmq.mmq_plane_rows(3314) * 3584 * 5 // 4
+    finally:
+        mmq.mmq_destroy(c2)

@@ -168,6 +168,20 @@ def test_gemm_parity(ctx, wtype, n, od, id_):
     mmq.mmq_weight_free(w)
 
 
+@pytest.mark.parametrize("wtype,n,od,id_", [("q6_K", 8, 3584, 18944), ("q4_K", 3, 18944, 3584),
+                                            ("q4_K", 70, 512, 2560), ("q6_K", 1, 1000, 5120),
+                                            ("q4_K", 130, 384, 4864)])
+def test_gemm_split_k_parity(ctx, wtype, n, od, id_):
+    """Few output tiles: the matmul splits K across workgroups (partials summed
+    in split order by a second kernel), including splits of unequal length."""
+    w, raw, (q, D, S), got = _gemm_case(ctx, wtype, n, od, id_, "splitk")
+    before = mmq.mmq_stats(ctx)["plane_bytes"]
+    assert before > mmq.mmq_plane_rows(n) * id_ * 1.25   # the partial scratch is held too
+    ref = oracle.gemm(wtype, q, D, S, raw, od, id_)
+    assert_gemm_close(got, ref, f"split-K {wtype} n={n} {od}x{id_}")
+    mmq.mmq_weight_free(w)
+
+
 @pytest.mark.parametrize("wtype,od,id_", [("q4_K", 18944, 3584), ("q6_K", 3584, 18944),
                                           ("q4_K", 512, 3584), ("q6_K", 512, 3584)])
 def test_gemm_full_size_sampled(ctx, wtype, od, id_):
