@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--small-n", action="store_true", help="add the small-n band sweep (us per call)")
     # one untimed device copy of this many MiB before the chain: the plain copy
     # kernel of known size that scales the HBM byte counters of a --pmc run
     p.add_argument("--copy-calibration", type=int, default=0, help=argparse.SUPPRESS)
@@ -216,6 +217,39 @@ def decode_gemv(mmq, torch, synth):
             res[name] = {"us": round(_graph_time_us(torch, fn, 50), 3)}
     finally:
         mmq.mmq_cache_clear(ctx)
+        mmq.mmq_destroy(ctx)
+    return res
+
+
+def small_n_sweep(mmq, torch, synth):
+    """The small-n band: matmul-call time for n = 1..128 tokens at the 7B/14B
+    shapes, weights registered for both paths (n <= 8 takes the GEMV path when
+    one pass holds the tokens, larger n the matmul tiles with a K split).  Each
+    point is a captured-graph replay over rotated weight copies."""
+    ctx = mmq.mmq_create(0, 0)
+    res = {}
+    try:
+        for wt, od, id_ in (("q4_K", 18944, 3584), ("q4_K", 3584, 3584), ("q6_K", 3584, 18944),
+                            ("q6_K", 512, 3584), ("q4_K", 13824, 5120), ("q6_K", 5120, 13824)):
+            raw = synth.weights(wt, synth.rng_for("smalln", 0, wt), od, id_)
+            code = mmq.MMQ_Q4_K if wt == "q4_K" else mmq.MMQ_Q6_K
+            copies = max(2, int(600e6 // (od * id_ * 2)))
+            ws = [mmq.mmq_register_weight(ctx, code, od, id_, raw, mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV)
+                  for _ in range(copies)]
+            fn = mmq.mmq_gemm_q4k if wt == "q4_K" else mmq.mmq_gemm_q6k
+            row = {}
+            for n in (1, 2, 4, 8, 16, 32, 128):
+                a = torch.from_numpy(synth.activations(synth.rng_for("smalln", n, "a"), n, id_)).cuda()
+                out = torch.empty((n, od), dtype=torch.float32, device="cuda")
+                fn(ctx, ws[0], a, n, out)
+                torch.cuda.synchronize()
+                row[n] = round(_graph_time_us(torch, lambda i: fn(ctx, ws[i % copies], a, n, out),
+                                              2 * copies), 2)
+                mmq.mmq_cache_clear(ctx)
+            res[f"{wt} {od}x{id_}"] = row
+            for w in ws:
+                mmq.mmq_weight_free(w)
+    finally:
         mmq.mmq_destroy(ctx)
     return res
 
@@ -407,6 +441,7 @@ def main():
 
     traffic = measured_traffic()
     decode = None if args.no_decode else decode_gemv(mmq, torch, synth)
+    small = small_n_sweep(mmq, torch, synth) if args.small_n else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     rec = {
@@ -440,6 +475,7 @@ def main():
         "graph": graph_rec,
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
         "decode_gemv": decode,
+        "small_n_us": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

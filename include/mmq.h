@@ -105,6 +105,7 @@ typedef struct mmq_stats_t {
     int64_t launches_mmvq_q4k;
     int64_t degraded_writes;        /* skip-write requests that wrote y (mixed consumers) */
     int64_t unfused_fallbacks;      /* MMQ_WRITE_AUTO producers without plane memory      */
+    int64_t small_n_gemv;           /* matmul calls served by the few-token GEMV path     */
 } mmq_stats_t;
 
 /* ---- context ----------------------------------------------------------- */
@@ -184,6 +185,12 @@ int mmq_quant_f32(mmq_ctx* ctx, const float* x, int64_t n, int64_t d, void* stre
  * overlaps a dead key, in which case it returns MMQ_E_DEAD_WRITE.
  * out[t][o] = sum_k D[t][k/32] q[t][k] * w[o][k] for t < n, o < rows,
  * row-major [n][rows] f32, caller-owned; w is the dequantised weight.
+ * The small-n band [r60 3.2: the matmul is tuned for n >= 16; d37 2]: for
+ * n <= 8 on a weight also registered with MMQ_USE_GEMV the call runs on the
+ * dot4 GEMV path (one launch per pass of up to 8 tokens); otherwise the
+ * matmul tiles, with K split across workgroups when the output tiles alone
+ * do not fill the device (partials held in the context's scratch, summed in
+ * a fixed order).
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE, MMQ_E_DEAD_WRITE, MMQ_E_OOM,
  * MMQ_E_HIP. */
 int mmq_gemm_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,

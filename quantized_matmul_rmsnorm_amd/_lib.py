@@ -62,7 +62,7 @@ class mmq_stats_t(ctypes.Structure):
         "launches_gemm_q4k", "launches_gemm_q6k", "launches_mmvq_q6k",
         "cache_hits", "cache_misses", "cache_refusals", "cache_entries",
         "plane_bytes", "weight_bytes", "launches_mmvq_q4k", "degraded_writes",
-        "unfused_fallbacks")]
+        "unfused_fallbacks", "small_n_gemv")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

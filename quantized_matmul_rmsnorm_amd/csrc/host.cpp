@@ -606,6 +606,8 @@ static int acquire_part(mmq_ctx* c, int64_t bytes, bool in_capture, const char* 
     return MMQ_OK;
 }
 
+constexpr int64_t kSmallN = 8;
+
 static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,
                        void* stream, int type, const char* who) {
     int rc = consume_check(c, w, a, n, out, type, MMQ_USE_GEMM, who);
@@ -615,6 +617,26 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
         return fail(MMQ_E_SHAPE, "%s: plane of %lld x %lld codes exceeds 2 GiB; split the tokens",
                     who, (long long)n, (long long)w->w.cols);
     if ((rc = use_device(c))) return rc;
+    // The small-n band: with GEMV tiles registered, up to kSmallN tokens run
+    // on the dot4 GEMV path (one launch streams the packed weights once for
+    // a pass of up to 8 tokens) instead of the 128-token matmul tiles.
+    const bool small = n <= kSmallN && (w->w.uses & MMQ_USE_GEMV) && mmvqn_supported(w->w.cols, n);
+    if (small) {
+        PlaneView pl;
+        if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;
+        if (type == MMQ_Q4_K) c->st.launches_gemm_q4k++;
+        else c->st.launches_gemm_q6k++;
+        c->st.small_n_gemv++;
+        if (c->dry) return MMQ_OK;
+        hipStream_t s = (hipStream_t)stream;
+        hipError_t e;
+        if (n == 1)
+            e = type == MMQ_Q4_K ? launch_mmvq_q4k(w->w, pl, out, s) : launch_mmvq_q6k(w->w, pl, out, s);
+        else
+            e = type == MMQ_Q4_K ? launch_mmvqn_q4k(w->w, pl, n, out, c->n_cu, s)
+                                 : launch_mmvqn_q6k(w->w, pl, n, out, c->n_cu, s);
+        return after_launch(c, e, s, who);
+    }
     const int splits = gemm_splits(w->w.rows_pad, w->w.cols, n, c->n_cu);
     if (splits > 1 &&
         (rc = acquire_part(c, (int64_t)splits * n * w->w.rows * 4,

@@ -65,5 +65,12 @@ hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
 hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
+// A few tokens at once over the GEMV tiles (out [n][rows]); used when the n
+// tokens' plane fits the LDS in one pass.
+int mmvqn_supported(int64_t cols, int64_t n);
+hipError_t launch_mmvqn_q6k(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
+                            int n_cu, hipStream_t s);
+hipError_t launch_mmvqn_q4k(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
+                            int n_cu, hipStream_t s);
 
 }  // namespace mmq

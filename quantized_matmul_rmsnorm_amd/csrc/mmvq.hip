@@ -24,6 +24,8 @@
 // activation: the dot accumulator starts at -32 * sum(q) of the half,
 // computed once per lane.  One f32 expression per block adds the block's
 // term; a wave-wide sum per row finishes the output.
+#include <algorithm>
+
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -253,6 +255,129 @@ int64_t mmvq_grid(int64_t rows) {
     return want <= 2 * resident ? want : resident;
 }
 
+// ---- a few tokens at once (2 <= n <= 8) ----
+// One 32-block of one token, as staged in LDS (40 bytes, two arrays): the
+// codes, then D and a sum word (q6_K: the two 16-value half sums as int16;
+// q4_K: the block's code sum S).
+struct ActRec {
+    uint4 q0, q1;
+    float D;
+    int aux;
+};
+constexpr int kRecBytes = 32 + 8;
+
+__device__ __forceinline__ Q6::Act to_act(const ActRec& r, Q6*) {
+    Q6::Act a;
+    a.q0 = r.q0; a.q1 = r.q1; a.D = r.D;
+    a.c0 = -32 * (int)(int16_t)(r.aux & 0xFFFF);
+    a.c1 = -32 * (r.aux >> 16);
+    return a;
+}
+__device__ __forceinline__ Q4::Act to_act(const ActRec& r, Q4*) {
+    Q4::Act a;
+    a.q0 = r.q0; a.q1 = r.q1; a.D = r.D; a.S = r.aux;
+    return a;
+}
+
+// Workgroups of 8 waves share the NT tokens' plane (tokens t0 .. t0+NT-1,
+// missing tokens as zeros) staged once in LDS; each wave walks groups of R
+// rows grid-stride, loads a block of the R rows per round (the next round's
+// loads in flight) and applies it to all NT tokens.  out is [n][od].
+template <class F, int NT, int R>
+__global__ __launch_bounds__(512) void k_mmvqn(const MvArgs g, int n, int t0) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    uint4* lds_q = reinterpret_cast<uint4*>(lds_raw);                      // [NT*nb][2]
+    int2* lds_m = reinterpret_cast<int2*>(lds_raw + (size_t)NT * (g.id / kBlock) * 32);  // [NT*nb]
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * 8 + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * 8;
+    const int id = g.id, od = g.od;
+    const int nb = id / kBlock;
+    const int nsb = id / kSuper;
+    const int64_t plane_row = (int64_t)id;            // codes per plane row
+    for (int rec = threadIdx.x; rec < NT * nb; rec += blockDim.x) {
+        const int t = rec / nb, b = rec - t * nb;
+        ActRec r;
+        if (t0 + t < n) {
+            const int8_t* qrow = g.Q + (int64_t)(t0 + t) * plane_row;
+            const uint4* p = reinterpret_cast<const uint4*>(qrow + (int64_t)b * kBlock);
+            r.q0 = p[0];
+            r.q1 = p[1];
+            r.D = g.Dp[(int64_t)(t0 + t) * nb + b];
+            if constexpr (sizeof(typename F::Act) == sizeof(Q6::Act) &&
+                          __is_same(F, Q6)) {
+                const uint32_t ones = 0x01010101u;
+                int s0 = dot4(r.q0.x, ones, 0); s0 = dot4(r.q0.y, ones, s0);
+                s0 = dot4(r.q0.z, ones, s0);    s0 = dot4(r.q0.w, ones, s0);
+                int s1 = dot4(r.q1.x, ones, 0); s1 = dot4(r.q1.y, ones, s1);
+                s1 = dot4(r.q1.z, ones, s1);    s1 = dot4(r.q1.w, ones, s1);
+                r.aux = (int)((uint32_t)(s0 & 0xFFFF) | ((uint32_t)s1 << 16));
+            } else {
+                r.aux = g.Sp[(int64_t)(t0 + t) * nb + b];
+            }
+        } else {
+            r.q0 = make_uint4(0, 0, 0, 0);
+            r.q1 = r.q0;
+            r.D = 0.0f;
+            r.aux = 0;
+        }
+        lds_q[2 * rec] = r.q0;
+        lds_q[2 * rec + 1] = r.q1;
+        lds_m[rec] = make_int2(__float_as_int(r.D), r.aux);
+    }
+    __syncthreads();
+
+    const int rounds = (nb + 63) / 64;
+    const int groups = (od + R - 1) / R;
+    for (int grp = wave; grp < groups; grp += nwaves) {
+        const int o0 = grp * R;
+        float acc[R][NT];
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[i][t] = 0.0f;
+        typename F::W cur[R], nxt[R];
+        auto load_round = [&](int r, typename F::W* dst) {
+            const int b = 64 * r + lane;
+            if (b < nb) {
+#pragma unroll
+                for (int i = 0; i < R; ++i)
+                    if (o0 + i < od) dst[i] = F::load(g, o0 + i, b, nb, nsb);
+            }
+        };
+        load_round(0, cur);
+        for (int r = 0; r < rounds; ++r) {
+            if (r + 1 < rounds) load_round(r + 1, nxt);
+            const int b = 64 * r + lane;
+            if (b < nb) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    ActRec rr;
+                    rr.q0 = lds_q[2 * (t * nb + b)];
+                    rr.q1 = lds_q[2 * (t * nb + b) + 1];
+                    const int2 m = lds_m[t * nb + b];
+                    rr.D = __int_as_float(m.x);
+                    rr.aux = m.y;
+                    const typename F::Act a = to_act(rr, (F*)nullptr);
+#pragma unroll
+                    for (int i = 0; i < R; ++i)
+                        if (o0 + i < od) acc[i][t] += F::term(a, cur[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) cur[i] = nxt[i];
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float v = wave_sum(acc[i][t]);
+                if (lane == 0 && o0 + i < od && t0 + t < n)
+                    g.out[(int64_t)(t0 + t) * od + o0 + i] = v;
+            }
+    }
+}
+
 template <class F>
 hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipStream_t s) {
     MvArgs g;
@@ -277,7 +402,72 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     return hipGetLastError();
 }
 
+// Tokens per pass: as many of {8, 4, 2} as the LDS holds (160 KiB).
+int mmvqn_tokens(int64_t cols, int64_t n) {
+    const int64_t rec = (cols / kBlock) * kRecBytes;
+    int nt = n > 4 ? 8 : (n > 2 ? 4 : 2);
+    while (nt > 2 && nt * rec > 160 * 1024) nt /= 2;
+    return nt * rec <= 160 * 1024 ? nt : 0;
+}
+
+template <class F, int NT>
+hipError_t launch_nt(const MvArgs& g, int64_t n, int64_t t0, int n_cu, hipStream_t s) {
+    constexpr int R = 4;
+    const size_t lds = (size_t)NT * (g.id / kBlock) * kRecBytes;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void*)k_mmvqn<F, NT, R>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr = true;
+    }
+    const int64_t groups = (g.od + R - 1) / R;
+    const int64_t want = (groups + 7) / 8;
+    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, n_cu)));
+    hipLaunchKernelGGL((k_mmvqn<F, NT, R>), grid, dim3(512), lds, s, g, (int)n, (int)t0);
+    return hipGetLastError();
+}
+
+template <class F>
+hipError_t launch_mmvqn(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
+                        int n_cu, hipStream_t s) {
+    MvArgs g;
+    g.ql = w.gv_ql;
+    g.qh = w.gv_qh;
+    g.sc = w.gv_sc;
+    g.dv = w.gv_d;
+    g.Q = pl.q;
+    g.Dp = pl.D;
+    g.Sp = pl.S;
+    g.id = (int)w.cols;
+    g.od = (int)w.rows;
+    g.out = out;
+    const int nt = mmvqn_tokens(w.cols, n);
+    if (nt == 0) return hipErrorInvalidValue;
+    for (int64_t t0 = 0; t0 < n; t0 += nt) {
+        hipError_t e = nt == 8   ? launch_nt<F, 8>(g, n, t0, n_cu, s)
+                       : nt == 4 ? launch_nt<F, 4>(g, n, t0, n_cu, s)
+                                 : launch_nt<F, 2>(g, n, t0, n_cu, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
+
+// The GEMV path pays off while one pass holds all n tokens (each further
+// pass streams the weights again); the crossover against the split-K matmul
+// was measured at the 7B/14B shapes for n = 1..8.
+int mmvqn_supported(int64_t cols, int64_t n) { return n >= 1 && mmvqn_tokens(cols, n) >= n; }
+
+hipError_t launch_mmvqn_q6k(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
+                            int n_cu, hipStream_t s) {
+    return launch_mmvqn<Q6>(w, pl, n, out, n_cu, s);
+}
+
+hipError_t launch_mmvqn_q4k(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
+                            int n_cu, hipStream_t s) {
+    return launch_mmvqn<Q4>(w, pl, n, out, n_cu, s);
+}
 
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s) {

@@ -284,3 +284,19 @@ def test_split_k_scratch_is_checked_before_any_launch(ctx):
         assert mmq.mmq_stats(c2)["plane_bytes"] == mmq.mmq_plane_rows(3314) * 3584 * 5 // 4
     finally:
         mmq.mmq_destroy(c2)
+
+
+def test_small_n_routing(ctx):
+    """n <= 8 on a weight registered for both paths takes the GEMV path when
+    one pass holds the tokens; otherwise the matmul tiles."""
+    both = mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV
+    w = _w(ctx, mmq.MMQ_Q4_K, 256, 5120, both)
+    wg = _w(ctx, mmq.MMQ_Q4_K, 256, 5120, mmq.MMQ_USE_GEMM)
+    wd = _w(ctx, mmq.MMQ_Q6_K, 256, 18944, both)
+    A, O = 0x100000, 0x4000000
+    for n, weight, fn, routed in [(1, w, mmq.mmq_gemm_q4k, 1), (8, w, mmq.mmq_gemm_q4k, 1),
+                                  (9, w, mmq.mmq_gemm_q4k, 0), (4, wg, mmq.mmq_gemm_q4k, 0),
+                                  (4, wd, mmq.mmq_gemm_q6k, 1), (5, wd, mmq.mmq_gemm_q6k, 0)]:
+        before = mmq.mmq_stats(ctx)["small_n_gemv"]
+        fn(ctx, weight, A + n * 0x10000000, n, O)
+        assert mmq.mmq_stats(ctx)["small_n_gemv"] - before == routed, (n, routed)

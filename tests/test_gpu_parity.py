@@ -168,6 +168,33 @@ def test_gemm_parity(ctx, wtype, n, od, id_):
     mmq.mmq_weight_free(w)
 
 
+@pytest.mark.parametrize("wtype,n,od,id_", [("q4_K", 2, 1000, 5120), ("q6_K", 3, 300, 13824),
+                                            ("q4_K", 5, 13824, 5120), ("q6_K", 8, 3584, 18944),
+                                            ("q6_K", 4, 3584, 18944),
+                                            ("q6_K", 6, 64, 256), ("q4_K", 1, 700, 2048),
+                                            ("q4_K", 7, 33, 20480)])
+def test_gemm_small_n_gemv_path(ctx, wtype, n, od, id_):
+    """n <= 8 on a weight registered for both paths runs on the dot4 GEMV
+    kernels when one pass of the LDS holds the n tokens (the 18944-wide plane
+    holds 4, so n = 8 there takes the matmul tiles instead; so does n = 7 at
+    width 20480)."""
+    rng = synth.rng_for("test", n * 7 + od, f"smalln{wtype}{id_}")
+    raw = synth.weights(wtype, rng, od, id_)
+    w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw, mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV)
+    a = dev_tensor(_act("smalln", n, id_))
+    out = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
+    before = mmq.mmq_stats(ctx)["small_n_gemv"]
+    (mmq.mmq_gemm_q4k if wtype == "q4_K" else mmq.mmq_gemm_q6k)(ctx, w, a, n, out)
+    torch.cuda.synchronize()
+    rec = id_ // 32 * 40                     # LDS bytes per token: 40 B per 32-block
+    one_pass = n <= max([t for t in (2, 4, 8) if t * rec <= 160 * 1024], default=0)
+    assert mmq.mmq_stats(ctx)["small_n_gemv"] == before + (1 if one_pass else 0)
+    q, D, S = export_plane(ctx, a, n, id_)
+    ref = oracle.gemm(wtype, q, D, S, raw, od, id_)
+    assert_gemm_close(out.cpu().numpy(), ref, f"small-n {wtype} n={n} {od}x{id_}")
+    mmq.mmq_weight_free(w)
+
+
 @pytest.mark.parametrize("wtype,n,od,id_", [("q6_K", 8, 3584, 18944), ("q4_K", 3, 18944, 3584),
                                             ("q4_K", 70, 512, 2560), ("q6_K", 1, 1000, 5120),
                                             ("q4_K", 130, 384, 4864)])
