@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--small-n", action="store_true", help="add the small-n band sweep (us per call)")
+    p.add_argument("--f16-reference", action="store_true",
+                   help="add a dense f16 GEMM of the gate shape through torch.matmul (context)")
     # one untimed device copy of this many MiB before the chain: the plain copy
     # kernel of known size that scales the HBM byte counters of a --pmc run
     p.add_argument("--copy-calibration", type=int, default=0, help=argparse.SUPPRESS)
@@ -254,6 +256,28 @@ def small_n_sweep(mmq, torch, synth):
     return res
 
 
+def f16_reference(torch):
+    """Context for the matmul roofline: a plain dense f16 GEMM of the gate
+    shape (3314 x 3584 times 3584 x 18944, f32 accumulation inside the vendor
+    library that torch.matmul calls), random operands, timed like the chain."""
+    a = torch.randn((TOKENS, HIDDEN), dtype=torch.float16, device="cuda")
+    b = torch.randn((HIDDEN, FFN), dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / 20
+    del a, b, c
+    return {"shape": f"{TOKENS}x{HIDDEN} @ {HIDDEN}x{FFN}", "us": round(us, 2),
+            "TFLOP_s": round(2 * TOKENS * HIDDEN * FFN / (us * 1e-6) / 1e12, 1)}
+
+
 def cpu_baseline(seconds: float):
     """The CPU oracle (as it is) on a bounded sample of one layer of the chain:
     producers and all seven matmuls for a growing number of tokens, run until
@@ -442,6 +466,7 @@ def main():
     traffic = measured_traffic()
     decode = None if args.no_decode else decode_gemv(mmq, torch, synth)
     small = small_n_sweep(mmq, torch, synth) if args.small_n else None
+    f16ref = f16_reference(torch) if args.f16_reference else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     rec = {
@@ -476,6 +501,7 @@ def main():
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
         "decode_gemv": decode,
         "small_n_us": small,
+        "f16_gemm_reference": f16ref,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
