@@ -235,6 +235,8 @@ int acquire_slot(mmq_ctx* c, const void* key, int64_t n, int64_t d, bool in_capt
             void* m = nullptr;
             hipError_t e = hipMalloc(&m, (size_t)need);
             if (e != hipSuccess) {
+                // the slot lost its memory: whatever entry used it is gone too
+                c->entries[idx].used = false;
                 c->plane_bytes -= s.cap;
                 s.cap = 0;
                 (void)hipGetLastError();
@@ -308,12 +310,7 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
     if ((rc = use_device(c))) return rc;
     int idx;
     // The producer replaces whatever was cached for bytes it (re)defines.
-    if (kind != kProdF32) {
-        drop_overlapping(c, y, bytes);
-        if (write_y) revive(c, y, bytes);  // a real write makes these bytes valid again
-    } else {
-        drop_overlapping(c, a, bytes);
-    }
+    drop_overlapping(c, kind != kProdF32 ? (const void*)y : (const void*)a, bytes);
     const bool in_capture = capturing(c, (hipStream_t)stream);
     if ((rc = acquire_slot(c, key, n, d, in_capture, &idx))) {
         // Last tier: with MMQ_WRITE_AUTO a producer that cannot get plane
@@ -332,6 +329,7 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
         return after_launch(c, launch_producer(kind, a, b, y, n, d, eps, true, none, s), s, who);
     }
     if (in_capture) c->captured = true;
+    if (kind != kProdF32 && write_y) revive(c, y, bytes);  // a real write makes these bytes valid
     const bool dead = kind != kProdF32 && !write_y;
     commit_entry(c, idx, key, n, d, dead);
     if (dead) c->dead.push_back({(uintptr_t)y, (uintptr_t)y + (uintptr_t)bytes});

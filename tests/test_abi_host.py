@@ -300,3 +300,14 @@ def test_small_n_routing(ctx):
         before = mmq.mmq_stats(ctx)["small_n_gemv"]
         fn(ctx, weight, A + n * 0x10000000, n, O)
         assert mmq.mmq_stats(ctx)["small_n_gemv"] - before == routed, (n, routed)
+
+
+def test_failed_producer_leaves_dead_marks(ctx):
+    """A producer that fails before its launch (no plane memory) must not
+    revive the dead range of a buffer it never wrote."""
+    X, W, Y = 0x100000, 0x200000, 0x1000000
+    mmq.mmq_quant_rms(ctx, X, W, Y, 8, 256, 1e-6, 0)           # Y promised unread
+    mmq.mmq_set_scratch_cap(ctx, mmq.mmq_stats(ctx)["plane_bytes"])
+    assert _status(mmq.mmq_quant_rms, ctx, X, W, Y, 64, 2048, 1e-6, 1) == mmq.MMQ_E_OOM
+    assert _status(mmq.mmq_quant_f32, ctx, Y, 8, 256) == mmq.MMQ_E_DEAD_WRITE
+    mmq.mmq_set_scratch_cap(ctx, -1)
