@@ -363,22 +363,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
 
 // Sum of the K-split partials in split order (deterministic): out[i] =
 // part[0][i] + part[1][i] + ...
+// Partial k starts at part + k * pstride (pstride a multiple of 64 floats).
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part,
                                                       float* __restrict__ out, int splits,
-                                                      int64_t count) {
+                                                      int64_t count, int64_t pstride) {
     const int64_t n4 = count / 4;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
         float4 acc = reinterpret_cast<const float4*>(part)[i];
         for (int k = 1; k < splits; ++k) {
-            const float4 v = reinterpret_cast<const float4*>(part + k * count)[i];
+            const float4 v = reinterpret_cast<const float4*>(part + k * pstride)[i];
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         reinterpret_cast<float4*>(out)[i] = acc;
     }
     for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
         float acc = part[i];
-        for (int k = 1; k < splits; ++k) acc += part[k * count + i];
+        for (int k = 1; k < splits; ++k) acc += part[k * pstride + i];
         out[i] = acc;
     }
 }
@@ -407,6 +408,8 @@ int gemm_splits(int64_t rows_pad, int64_t cols, int64_t n, int n_cu) {
     return best;
 }
 
+int64_t gemm_part_stride(int64_t n, int64_t rows) { return (n * rows + 63) / 64 * 64; }
+
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
                        float* part, int splits, hipStream_t s) {
     GemmArgs a;
@@ -422,7 +425,7 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.sb_per = (int)((nsb + splits - 1) / splits);
     splits = (int)((nsb + a.sb_per - 1) / a.sb_per);
     a.out = splits > 1 ? part : out;
-    a.part_stride = splits > 1 ? n * w.rows : 0;
+    a.part_stride = splits > 1 ? gemm_part_stride(n, w.rows) : 0;
     a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * npart * 2);
     a.dmr_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 64 : 32) * 4);
     a.mfrag_bytes = w.type == 12 ? (uint32_t)(og * nsb * 512 * 2) : 0u;
@@ -443,7 +446,8 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
         const int64_t count = n * w.rows;
         const int64_t want = (count / 4 + 255) / 256;
         const dim3 rg((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 4096)));
-        hipLaunchKernelGGL(k_split_reduce, rg, dim3(256), 0, s, part, out, splits, count);
+        hipLaunchKernelGGL(k_split_reduce, rg, dim3(256), 0, s, part, out, splits, count,
+                           a.part_stride);
     }
     return hipGetLastError();
 }

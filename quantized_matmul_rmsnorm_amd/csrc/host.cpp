@@ -637,7 +637,7 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
     }
     const int splits = gemm_splits(w->w.rows_pad, w->w.cols, n, c->n_cu);
     if (splits > 1 &&
-        (rc = acquire_part(c, (int64_t)splits * n * w->w.rows * 4,
+        (rc = acquire_part(c, (int64_t)splits * gemm_part_stride(n, w->w.rows) * 4,
                            capturing(c, (hipStream_t)stream), who)))
         return rc;
     PlaneView pl;

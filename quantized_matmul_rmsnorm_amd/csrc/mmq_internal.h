@@ -56,9 +56,10 @@ hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStr
 
 // ---- consumers ----
 // K splits the matmul uses for n tokens on n_cu compute units (1: none);
-// with splits > 1 the partials go to part [splits][n][rows] and are summed
+// with splits > 1 the partials go to part [splits][stride] and are summed
 // into out in split order by a second kernel.
 int gemm_splits(int64_t rows_pad, int64_t cols, int64_t n, int n_cu);
+int64_t gemm_part_stride(int64_t n, int64_t rows);   // floats per partial (16-byte aligned)
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
                        float* part, int splits, hipStream_t s);
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,

@@ -197,7 +197,7 @@ def test_gemm_small_n_gemv_path(ctx, wtype, n, od, id_):
 
 @pytest.mark.parametrize("wtype,n,od,id_", [("q6_K", 8, 3584, 18944), ("q4_K", 3, 18944, 3584),
                                             ("q4_K", 70, 512, 2560), ("q6_K", 1, 1000, 5120),
-                                            ("q4_K", 130, 384, 4864)])
+                                            ("q4_K", 130, 384, 4864), ("q6_K", 9, 1001, 2560)])
 def test_gemm_split_k_parity(ctx, wtype, n, od, id_):
     """Few output tiles: the matmul splits K across workgroups (partials summed
     in split order by a second kernel), including splits of unequal length."""
