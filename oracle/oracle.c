@@ -22,6 +22,12 @@
  * tiny shapes, the integer special case (unit scales -> exact int matmul),
  * quantiser invariants, the RMSNorm and SwiGLU closed forms, and an
  * independent field encoder for both superblock formats.
+ *
+ * Parity unpinned: (1) bit-compatibility of the two superblock byte layouts
+ * with real GGUF files (no such file is available; the layouts are this
+ * project's reading of the public format, pinned only for self-consistency
+ * by the encoder round trips); (2) agreement with a worked numeric example
+ * from the pages, which print none for the plane or the matmul.
  */
 #include <math.h>
 #include <stdint.h>
