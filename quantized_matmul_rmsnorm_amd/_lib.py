@@ -184,7 +184,15 @@ def mmq_plane_rows(n: int) -> int:
 def mmq_register_weight(ctx, wtype: int, rows: int, cols: int, raw_host, uses: int = 0):
     """raw_host: a C-contiguous numpy uint8 array (or bytes) of the raw superblocks."""
     import numpy as np
-    arr = np.ascontiguousarray(raw_host, dtype=np.uint8)
+    if isinstance(raw_host, (bytes, bytearray, memoryview)):
+        arr = np.frombuffer(raw_host, dtype=np.uint8)
+    else:
+        arr = np.ascontiguousarray(raw_host, dtype=np.uint8)
+    bpb = {MMQ_Q4_K: 144, MMQ_Q6_K: 210}.get(wtype)
+    if bpb is not None and cols % 256 == 0 and arr.size != rows * (cols // 256) * bpb:
+        # the C call reads exactly that many bytes from the pointer it is given
+        raise ValueError(f"raw_host holds {arr.size} bytes; {rows} x {cols} of type {wtype} "
+                         f"needs {rows * (cols // 256) * bpb}")
     out = ctypes.c_void_p()
     _check(lib.mmq_register_weight(ctx, wtype, rows, cols, arr.ctypes.data_as(ctypes.c_void_p),
                                    uses, ctypes.byref(out)))

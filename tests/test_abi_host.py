@@ -311,3 +311,10 @@ def test_failed_producer_leaves_dead_marks(ctx):
     assert _status(mmq.mmq_quant_rms, ctx, X, W, Y, 64, 2048, 1e-6, 1) == mmq.MMQ_E_OOM
     assert _status(mmq.mmq_quant_f32, ctx, Y, 8, 256) == mmq.MMQ_E_DEAD_WRITE
     mmq.mmq_set_scratch_cap(ctx, -1)
+
+
+def test_binding_checks_the_raw_buffer_size(ctx):
+    with pytest.raises(ValueError):
+        mmq.mmq_register_weight(ctx, mmq.MMQ_Q4_K, 4, 256, np.zeros(144 * 3, np.uint8))
+    w = mmq.mmq_register_weight(ctx, mmq.MMQ_Q6_K, 2, 512, bytes(2 * 2 * 210))
+    mmq.mmq_weight_free(w)
