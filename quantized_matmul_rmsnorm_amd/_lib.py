@@ -189,7 +189,8 @@ def mmq_register_weight(ctx, wtype: int, rows: int, cols: int, raw_host, uses: i
     else:
         arr = np.ascontiguousarray(raw_host, dtype=np.uint8)
     bpb = {MMQ_Q4_K: 144, MMQ_Q6_K: 210}.get(wtype)
-    if bpb is not None and cols % 256 == 0 and arr.size != rows * (cols // 256) * bpb:
+    if bpb is not None and rows >= 1 and cols >= 256 and cols % 256 == 0 and \
+            arr.size != rows * (cols // 256) * bpb:
         # the C call reads exactly that many bytes from the pointer it is given
         raise ValueError(f"raw_host holds {arr.size} bytes; {rows} x {cols} of type {wtype} "
                          f"needs {rows * (cols // 256) * bpb}")
