@@ -76,26 +76,31 @@ __device__ __forceinline__ half8 i8x8_to_f16(uint32_t x, uint32_t y) {
     return h;
 }
 
-// Hardware places workgroup i on XCD i % 8; give each XCD a contiguous range of
-// logical tiles so that the workgroups resident on one XCD (and its L2) share
-// weight and activation tiles.  Within the range, tiles are rastered in groups
-// of kGroupO output tiles with the token tile varying slowest inside a group.
-// With a K split the logical index runs split-major, so the workgroups of one
-// XCD share a split (its weight and plane columns).
-__device__ __forceinline__ void tile_of(int n_ttiles, int n_otiles, int& t_tile, int& o_tile,
-                                        int& split) {
-    const int nwg = gridDim.x;
-    const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
-    const int per = nwg >> 3, rem = nwg & 7;
-    int L = xcd * per + min(xcd, rem) + li;
-    const int tiles = n_ttiles * n_otiles;
-    split = L / tiles;
-    L -= split * tiles;
+// Token and output tile of logical tile L: tiles are rastered in groups of
+// kGroupO output tiles with the token tile varying slowest inside a group.
+__device__ __forceinline__ void raster(int L, int n_ttiles, int n_otiles, int& t_tile,
+                                       int& o_tile) {
     const int gsize = kGroupO * n_ttiles;
     const int group = L / gsize, r = L % gsize;
     const int go = min(kGroupO, n_otiles - group * kGroupO);
     o_tile = group * kGroupO + r % go;
     t_tile = r / go;
+}
+
+// Hardware places workgroup i on XCD i % 8; give each XCD a contiguous range of
+// logical indices so that the workgroups resident on one XCD (and its L2) share
+// weight and activation tiles.  A launch covers `count` logical tiles from
+// `base`; with a K split the logical index runs split-major, so the workgroups
+// of one XCD share a split (its weight and plane columns).
+__device__ __forceinline__ void tile_of(int base, int count, int n_ttiles, int n_otiles,
+                                        int& t_tile, int& o_tile, int& split, int& local) {
+    const int nwg = gridDim.x;
+    const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    int L = xcd * per + min(xcd, rem) + li;
+    split = L / count;
+    local = L - split * count;
+    raster(base + local, n_ttiles, n_otiles, t_tile, o_tile);
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
@@ -126,6 +131,8 @@ struct GemmArgs {
     int n, plane_rows, id, od, n_ttiles, n_otiles;
     int sb_per;           // superblocks per K split (all of them without a split)
     int64_t part_stride;  // floats between the partial outputs of two splits
+    int tile_base, tile_count;  // logical tiles of this launch
+    int compact;          // 1: partials go to part[split][tile][128][128]
 };
 
 // The matmul kernel.  RA: depth of the weight-fragment register ring (the
@@ -150,8 +157,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     const int ogl = wave & 3;
     const int th = wave >> 2;
 
-    int t_tile, o_tile, split;
-    tile_of(g.n_ttiles, g.n_otiles, t_tile, o_tile, split);
+    int t_tile, o_tile, split, local;
+    tile_of(g.tile_base, g.tile_count, g.n_ttiles, g.n_otiles, t_tile, o_tile, split, local);
     const int t0 = t_tile * 128;
     const int og0 = o_tile * 4;
     const int id = g.id;
@@ -341,6 +348,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     }
 
     const int od = g.od;
+    if (g.compact) {
+        // the whole 128 x 128 tile, bounds applied by the tile reduce
+        float* tp = g.out + ((int64_t)split * g.tile_count + local) * (128 * 128);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            float* row = tp + ((2 * th + i) * 32 + (lane & 31)) * 128;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(row + ogl * 32 + 8 * q + 4 * (lane >> 5)) =
+                    make_float4(res[i][4 * q], res[i][4 * q + 1], res[i][4 * q + 2], res[i][4 * q + 3]);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t t = t0 + (2 * th + i) * 32 + (lane & 31);
@@ -384,6 +404,37 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
     }
 }
 
+// Sum of the compact partial tiles of the tail launch: out for tile `local`
+// of the logical range [base, base + count) = sum over splits, in order.
+// 16 workgroups per tile, 8 rows of 128 each (one float4 per thread).
+__global__ __launch_bounds__(256) void k_tile_reduce(const float* __restrict__ part,
+                                                     float* __restrict__ out, int splits,
+                                                     int count, int base, int n_ttiles,
+                                                     int n_otiles, int n, int od) {
+    const int local = blockIdx.x >> 4, chunk = blockIdx.x & 15;
+    int t_tile, o_tile;
+    raster(base + local, n_ttiles, n_otiles, t_tile, o_tile);
+    const int tt = chunk * 8 + (threadIdx.x >> 5);
+    const int oo = (threadIdx.x & 31) * 4;
+    const float* p = part + (int64_t)local * (128 * 128) + tt * 128 + oo;
+    float4 acc = *reinterpret_cast<const float4*>(p);
+    for (int k = 1; k < splits; ++k) {
+        const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)k * count * (128 * 128));
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const int64_t t = (int64_t)t_tile * 128 + tt;
+    const int64_t o = (int64_t)o_tile * 128 + oo;
+    if (t >= n) return;
+    float* orow = out + t * (int64_t)od;
+    if (o + 3 < od && (od & 3) == 0) {
+        *reinterpret_cast<float4*>(orow + o) = acc;
+    } else {
+        const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+        for (int e = 0; e < 4; ++e)
+            if (o + e < od) orow[o + e] = a4[e];
+    }
+}
+
 }  // namespace
 
 // K splits for a matmul of n tokens: only when the output tiles fill less
@@ -410,8 +461,39 @@ int gemm_splits(int64_t rows_pad, int64_t cols, int64_t n, int n_cu) {
 
 int64_t gemm_part_stride(int64_t n, int64_t rows) { return (n * rows + 63) / 64 * 64; }
 
+// How a matmul is launched on n_cu compute units:
+//  * few output tiles: K split across all of them (gemm_splits);
+//  * many tiles whose last round would be nearly empty (under 1/8 full): the
+//    full rounds run unsplit and the leftover tiles run K-split into compact
+//    partial tiles that a tile reduce sums -- the leftover tiles then take a
+//    fraction of a round instead of a whole one.
+GemmPlan gemm_plan(const WeightDev& w, int64_t n, int n_cu) {
+    GemmPlan p;
+    const int64_t nsb = w.cols / kSuper;
+    const int64_t tiles = ((n + 127) / 128) * (w.rows_pad / 128);
+    p.splits = gemm_splits(w.rows_pad, w.cols, n, n_cu);
+    if (p.splits > 1) {
+        const int64_t per = (nsb + p.splits - 1) / p.splits;
+        p.splits = (int)((nsb + per - 1) / per);
+        p.part_floats = p.splits * gemm_part_stride(n, w.rows);
+        return p;
+    }
+    const int64_t tail = n_cu > 0 ? tiles % n_cu : 0;
+    if (n_cu > 0 && tiles > n_cu && tail > 0 && tail * 8 <= n_cu && nsb >= 2) {
+        int64_t ts = std::min<int64_t>(nsb, std::max<int64_t>(2, n_cu / tail));
+        const int64_t per = (nsb + ts - 1) / ts;
+        ts = (nsb + per - 1) / per;
+        if (ts >= 2) {
+            p.tail_tiles = (int)tail;
+            p.tail_splits = (int)ts;
+            p.part_floats = ts * tail * 128 * 128;
+        }
+    }
+    return p;
+}
+
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
-                       float* part, int splits, hipStream_t s) {
+                       float* part, const GemmPlan& plan, hipStream_t s) {
     GemmArgs a;
     a.wa = (const half8*)w.wa;
     a.dmr = w.dmr;
@@ -421,11 +503,6 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.S = pl.S;
     const int npart = w.type == 12 ? 1 : 2;
     const int64_t nsb = w.cols / kSuper, og = w.rows_pad / 32;
-    if (splits < 1 || part == nullptr) splits = 1;
-    a.sb_per = (int)((nsb + splits - 1) / splits);
-    splits = (int)((nsb + a.sb_per - 1) / a.sb_per);
-    a.out = splits > 1 ? part : out;
-    a.part_stride = splits > 1 ? gemm_part_stride(n, w.rows) : 0;
     a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * npart * 2);
     a.dmr_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 64 : 32) * 4);
     a.mfrag_bytes = w.type == 12 ? (uint32_t)(og * nsb * 512 * 2) : 0u;
@@ -437,17 +514,47 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.od = (int)w.rows;
     a.n_ttiles = (int)((n + 127) / 128);
     a.n_otiles = (int)(w.rows_pad / 128);
-    const dim3 grid((unsigned)(a.n_ttiles * a.n_otiles * splits)), block(kThreads);
-    if (w.type == 12)
-        hipLaunchKernelGGL((k_gemm_da<true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((k_gemm_da<false>), grid, block, 0, s, a);
+    const int tiles = a.n_ttiles * a.n_otiles;
+    auto go = [&](unsigned grid) {
+        if (w.type == 12)
+            hipLaunchKernelGGL((k_gemm_da<true>), dim3(grid), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gemm_da<false>), dim3(grid), dim3(kThreads), 0, s, a);
+    };
+    const int splits = part != nullptr ? plan.splits : 1;
     if (splits > 1) {
+        a.sb_per = (int)((nsb + splits - 1) / splits);
+        a.out = part;
+        a.part_stride = gemm_part_stride(n, w.rows);
+        a.tile_base = 0;
+        a.tile_count = tiles;
+        a.compact = 0;
+        go((unsigned)(tiles * splits));
         const int64_t count = n * w.rows;
         const int64_t want = (count / 4 + 255) / 256;
         const dim3 rg((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 4096)));
         hipLaunchKernelGGL(k_split_reduce, rg, dim3(256), 0, s, part, out, splits, count,
                            a.part_stride);
+        return hipGetLastError();
+    }
+    const int tail = part != nullptr ? plan.tail_tiles : 0;
+    a.sb_per = (int)nsb;
+    a.out = out;
+    a.part_stride = 0;
+    a.tile_base = 0;
+    a.tile_count = tiles - tail;
+    a.compact = 0;
+    go((unsigned)(tiles - tail));
+    if (tail > 0) {
+        const int ts = plan.tail_splits;
+        a.sb_per = (int)((nsb + ts - 1) / ts);
+        a.out = part;
+        a.tile_base = tiles - tail;
+        a.tile_count = tail;
+        a.compact = 1;
+        go((unsigned)(tail * ts));
+        hipLaunchKernelGGL(k_tile_reduce, dim3((unsigned)(tail * 16)), dim3(256), 0, s, part, out,
+                           ts, tail, tiles - tail, a.n_ttiles, a.n_otiles, a.n, a.od);
     }
     return hipGetLastError();
 }

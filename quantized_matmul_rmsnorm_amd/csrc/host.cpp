@@ -635,10 +635,9 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
                                  : launch_mmvqn_q6k(w->w, pl, n, out, c->n_cu, s);
         return after_launch(c, e, s, who);
     }
-    const int splits = gemm_splits(w->w.rows_pad, w->w.cols, n, c->n_cu);
-    if (splits > 1 &&
-        (rc = acquire_part(c, (int64_t)splits * gemm_part_stride(n, w->w.rows) * 4,
-                           capturing(c, (hipStream_t)stream), who)))
+    const GemmPlan plan = gemm_plan(w->w, n, c->n_cu);
+    if (plan.part_floats > 0 &&
+        (rc = acquire_part(c, plan.part_floats * 4, capturing(c, (hipStream_t)stream), who)))
         return rc;
     PlaneView pl;
     if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;
@@ -646,7 +645,7 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
     else c->st.launches_gemm_q6k++;
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
-    return after_launch(c, launch_gemm(w->w, pl, n, out, (float*)c->part, splits, s), s, who);
+    return after_launch(c, launch_gemm(w->w, pl, n, out, (float*)c->part, plan, s), s, who);
 }
 
 int mmq_gemm_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,

@@ -60,8 +60,18 @@ hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStr
 // into out in split order by a second kernel.
 int gemm_splits(int64_t rows_pad, int64_t cols, int64_t n, int n_cu);
 int64_t gemm_part_stride(int64_t n, int64_t rows);   // floats per partial (16-byte aligned)
+// The launch plan: a K split of every tile (splits > 1), or a K split of
+// only the tail tiles that would leave the last round nearly empty
+// (tail_tiles > 0, partials as compact 128 x 128 tiles); part_floats is the
+// scratch it needs (0: none).
+struct GemmPlan {
+    int splits = 1;
+    int tail_tiles = 0, tail_splits = 0;
+    int64_t part_floats = 0;
+};
+GemmPlan gemm_plan(const WeightDev& w, int64_t n, int n_cu);
 hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
-                       float* part, int splits, hipStream_t s);
+                       float* part, const GemmPlan& plan, hipStream_t s);
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
 hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,

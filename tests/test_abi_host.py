@@ -276,12 +276,18 @@ def test_split_k_scratch_is_checked_before_any_launch(ctx):
     mmq.mmq_gemm_q6k(ctx, w, A, 8, O)
     part = mmq.mmq_stats(ctx)["plane_bytes"] - plane
     assert part % (3584 * 8 * 4) == 0 and part // (3584 * 8 * 4) >= 2     # 3584*8 is a multiple of 64
-    # many output tiles: no split, no partials
+    # many output tiles whose last round is well filled: no split, no partials
     c2 = mmq.mmq_create(0, mmq.MMQ_CTX_DRYRUN)
     try:
-        w2 = _w(c2, mmq.MMQ_Q4_K, 18944, 3584, mmq.MMQ_USE_GEMM)
+        plane = mmq.mmq_plane_rows(3314) * 3584 * 5 // 4
+        w2 = _w(c2, mmq.MMQ_Q4_K, 3584, 3584, mmq.MMQ_USE_GEMM)     # 728 tiles: 2.84 rounds
         mmq.mmq_gemm_q4k(c2, w2, A, 3314, O)
-        assert mmq.mmq_stats(c2)["plane_bytes"] == mmq.mmq_plane_rows(3314) * 3584 * 5 // 4
+        assert mmq.mmq_stats(c2)["plane_bytes"] == plane
+        # 3848 tiles = 15 rounds + 8: the 8 leftover tiles run K-split (14 superblocks ->
+        # 14 splits) into compact 128 x 128 partial tiles
+        w3 = _w(c2, mmq.MMQ_Q4_K, 18944, 3584, mmq.MMQ_USE_GEMM)
+        mmq.mmq_gemm_q4k(c2, w3, A, 3314, O)
+        assert mmq.mmq_stats(c2)["plane_bytes"] == plane + 14 * 8 * 128 * 128 * 4
     finally:
         mmq.mmq_destroy(c2)
 

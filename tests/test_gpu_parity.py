@@ -209,6 +209,21 @@ def test_gemm_split_k_parity(ctx, wtype, n, od, id_):
     mmq.mmq_weight_free(w)
 
 
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+def test_gemm_tail_round_split(ctx, wtype):
+    """258 output tiles on 256 CUs: 256 run whole, the 2 leftover tiles (the
+    last output tile, both token tiles) run K-split into compact partial tiles
+    summed by the tile reduce.  All outputs of the leftover tiles are checked,
+    plus sampled others."""
+    n, od, id_ = 256, 16512, 1024
+    w, raw, (q, D, S), got = _gemm_case(ctx, wtype, n, od, id_, "tail")
+    rng = np.random.default_rng(11)
+    outs = np.unique(np.concatenate([np.arange(16384, od), rng.integers(0, 16384, 200)]))
+    ref = oracle.gemm(wtype, q, D, S, raw, od, id_, outs=outs)
+    assert_gemm_close(got[:, outs], ref, f"tail split {wtype}")
+    mmq.mmq_weight_free(w)
+
+
 @pytest.mark.parametrize("wtype,od,id_", [("q4_K", 18944, 3584), ("q6_K", 3584, 18944),
                                           ("q4_K", 512, 3584), ("q6_K", 512, 3584)])
 def test_gemm_full_size_sampled(ctx, wtype, od, id_):
