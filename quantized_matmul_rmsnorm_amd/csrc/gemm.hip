@@ -29,8 +29,10 @@
 // wave streams its own weight fragments (stored in MFMA fragment order at
 // registration) straight from L2 into a small register ring a few blocks
 // ahead; the activation codes of the tile are staged per 4-block chunk
-// through two LDS buffers, converted int8 -> f16 once per workgroup, and each
-// block's B fragments are read from LDS one block ahead.  All global reads use
+// through three LDS buffers, converted int8 -> f16 once per workgroup, and each
+// block's B fragments are read from LDS one block ahead (the next chunk's
+// first block included: one barrier in the middle of each chunk step makes
+// that chunk visible, so no step starts by waiting on LDS).  All global reads use
 // raw buffer loads with 32-bit offsets; plane rows past the plane's padded
 // row count fall outside the buffer and read as zero.  Staging and prefetch
 // indices are clamped instead of guarded, so a superblock's two chunks form
@@ -146,8 +148,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     constexpr int RA = Q4K ? 4 : 2;         // weight-fragment ring depth (divides 8)
     constexpr int PD = RA - 1;              // prefetch distance in blocks
     constexpr int BPAD = 4, DPAD = 16;
-    __shared__ half8 sB[2][CH][4 * 2 * 64 + BPAD];
-    __shared__ float sD[2][CH][128 + DPAD];
+    constexpr int NBUF = 3;
+    constexpr int kBarAt = 1;               // the chunk step's barrier follows block 1
+    static_assert(kBarAt < CH - 1, "the next chunk's first read must follow the barrier");
+    __shared__ half8 sB[NBUF][CH][4 * 2 * 64 + BPAD];
+    __shared__ float sD[NBUF][CH][128 + DPAD];
     __shared__ __attribute__((aligned(16))) _Float16 sP[Q4K ? 3 : 1][4][64][8];
     __shared__ __attribute__((aligned(16))) float sDM[2][kThreads];
 
@@ -252,26 +257,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     load_chunk(c0 + 1, false);
     __syncthreads();
 
+    half8 bfr[2][2][2];   // B fragments [ring][t group][k16], one block ahead
+    auto read_b = [&](int bufi, int jj, half8 (*dst)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int k16 = 0; k16 < 2; ++k16)
+                dst[i][k16] = sB[bufi][jj][((2 * th + i) * 2 + k16) * 64 + lane];
+    };
+    read_b(0, 0, bfr[0]);
+    // three staging buffers: chunk c lives in buffer (c - c0) % 3.  Chunk c+1
+    // is stored at the start of chunk c's step and one barrier follows in its
+    // middle, so the first B fragments of chunk c+1 can be read before the
+    // step ends, and the store of chunk c+2 never meets a read of chunk c-1.
+    int bcur = 0;
     for (int sb = sb0; sb < sb1; ++sb) {
 #pragma unroll
         for (int cc = 0; cc < SBCH; ++cc) {
             const int c = sb * SBCH + cc;
-            const int buf = cc & 1;
+            const int bnext = bcur == NBUF - 1 ? 0 : bcur + 1;
             // stage chunk c+1 (loaded one chunk ago), load chunk c+2
-            store_chunk(min(c + 1, c_end - 1), buf ^ 1, (cc + 1) % SBCH == 0, c + 1 < c_end);
+            store_chunk(min(c + 1, c_end - 1), bnext, (cc + 1) % SBCH == 0, c + 1 < c_end);
             load_chunk(min(c + 2, c_end - 1), cc % SBCH == 0);
             half8 mf;
             if (Q4K && cc == SBCH - 1)
                 mf = bload<half8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
             f32x16 X[2][2];
-            half8 bfr[2][2][2];   // B fragments [ring][t group][k16], one block ahead
-            auto read_b = [&](int jj, half8 (*dst)[2]) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int k16 = 0; k16 < 2; ++k16)
-                        dst[i][k16] = sB[buf][jj][((2 * th + i) * 2 + k16) * 64 + lane];
-            };
             auto mfma_block = [&](int slot, half8 (*bf)[2], f32x16* Xo) {
 #pragma unroll
                 for (int k16 = 0; k16 < 2; ++k16) {
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
 #pragma unroll
             for (int jj = 0; jj < CH; ++jj)
 #pragma unroll
-                for (int i = 0; i < 2; ++i) dav[jj][i] = sD[buf][jj][(2 * th + i) * 32 + (lane & 31)];
+                for (int i = 0; i < 2; ++i) dav[jj][i] = sD[bcur][jj][(2 * th + i) * 32 + (lane & 31)];
             auto epilogue_block = [&](int jj, const f32x16* Xi) {
                 const int j = cc * CH + jj;
 #pragma unroll
@@ -307,17 +318,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
                     }
                 }
             };
-            read_b(0, bfr[0]);
 #pragma unroll
             for (int jj = 0; jj < CH; ++jj) {
                 const int j = cc * CH + jj;            // block within the superblock
                 const int b = sb * 8 + j;
                 load_a(min(b + PD, b_end - 1), (j + PD) % RA);   // clamped: no branch, in bounds
-                if (jj + 1 < CH) read_b(jj + 1, bfr[(jj + 1) & 1]);
+                if (jj + 1 < CH) read_b(bcur, jj + 1, bfr[(jj + 1) & 1]);
+                else read_b(bnext, 0, bfr[0]);         // next chunk: stored at this step's start, past the barrier
                 __builtin_amdgcn_s_setprio(1);   // wave priority only (not a queue priority)
                 mfma_block(j % RA, bfr[jj & 1], X[jj & 1]);
                 __builtin_amdgcn_s_setprio(0);
                 if (jj > 0) epilogue_block(jj - 1, X[(jj - 1) & 1]);
+                if (jj == kBarAt) __syncthreads();
             }
             epilogue_block(CH - 1, X[(CH - 1) & 1]);
 
@@ -343,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
                         for (int r = 0; r < 16; ++r) res[i][r] = fmaf(dmv[r], acc[i][r], res[i][r]);
                 }
             }
-            __syncthreads();
+            bcur = bnext;
         }
     }
 
