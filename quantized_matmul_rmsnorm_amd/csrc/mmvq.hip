@@ -23,7 +23,9 @@
 // its codes.  For q6_K the "- 32" of the code is applied through the
 // activation: the dot accumulator starts at -32 * sum(q) of the half,
 // computed once per lane.  One f32 expression per block adds the block's
-// term; a wave-wide sum per row finishes the output.
+// term; a wave-wide sum per row finishes the output.  The weights of the
+// wave's next row (next two rows for long rows) are in flight while a row is
+// reduced.
 #include <algorithm>
 
 #include "mmq_internal.h"
@@ -182,11 +184,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // MAXR > 0: the lane's activation blocks stay in registers (nb <= 64 * MAXR),
-// and the weights of the wave's next row are loaded block by block as soon as
-// the current row's registers for that block are consumed, so a row's loads
-// are in flight while the previous row is reduced.
+// and the weights of the wave's next PF rows are in flight: a row's
+// registers for a block are refilled with the row PF steps ahead as soon as
+// the block is consumed.
 // MAXR == 0: blocks are re-read from the plane for every row (any length).
-template <class F, int MAXR>
+template <class F, int MAXR, int PF>
 __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -198,28 +200,38 @@ __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
 
     if constexpr (MAXR > 0) {
         typename F::Act act[MAXR];
-        typename F::W w[MAXR];
+        typename F::W w[PF][MAXR];
 #pragma unroll
         for (int r = 0; r < MAXR; ++r)
             if (r < rounds && 64 * r + lane < nb) act[r] = F::act(g, 64 * r + lane);
-        int o = wave;
-        if (o < od) {
 #pragma unroll
-            for (int r = 0; r < MAXR; ++r)
-                if (r < rounds && 64 * r + lane < nb) w[r] = F::load(g, o, 64 * r + lane, nb, nsb);
-        }
-        for (; o < od; o += nwaves) {
-            const int on = o + nwaves;
-            float acc = 0.0f;
+        for (int p = 0; p < PF; ++p) {
+            const int op = wave + p * nwaves;
+            if (op < od) {
 #pragma unroll
-            for (int r = 0; r < MAXR; ++r) {
-                if (r < rounds && 64 * r + lane < nb) {
-                    acc += F::term(act[r], w[r]);
-                    if (on < od) w[r] = F::load(g, on, 64 * r + lane, nb, nsb);
-                }
+                for (int r = 0; r < MAXR; ++r)
+                    if (r < rounds && 64 * r + lane < nb) w[p][r] = F::load(g, op, 64 * r + lane, nb, nsb);
             }
-            acc = wave_sum(acc);
-            if (lane == 0) g.out[o] = acc;
+        }
+        int o = wave;
+        while (o < od) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                if (o < od) {
+                    const int on = o + PF * nwaves;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < MAXR; ++r) {
+                        if (r < rounds && 64 * r + lane < nb) {
+                            acc += F::term(act[r], w[p][r]);
+                            if (on < od) w[p][r] = F::load(g, on, 64 * r + lane, nb, nsb);
+                        }
+                    }
+                    acc = wave_sum(acc);
+                    if (lane == 0) g.out[o] = acc;
+                }
+                o += nwaves;
+            }
         }
     } else {
         for (int o = wave; o < od; o += nwaves) {
@@ -237,14 +249,14 @@ __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
 // Workgroups of one launch: every row gets a wave when the rows fit in two
 // rounds of resident waves; larger matrices get exactly the resident waves
 // (each then walks rows grid-stride with its plane slice loaded once).
-template <class F, int MAXR>
+template <class F, int MAXR, int PF>
 int64_t mmvq_grid(int64_t rows) {
     static int per_cu = -1, n_cu = 0;
     if (per_cu < 0) {
         int dev = 0, blk = 0;
         (void)hipGetDevice(&dev);
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq<F, MAXR>, 256, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq<F, MAXR, PF>, 256, 0) !=
             hipSuccess)
             blk = 1;
         per_cu = blk > 0 ? blk : 1;
@@ -378,6 +390,12 @@ __global__ __launch_bounds__(512) void k_mmvqn(const MvArgs g, int n, int t0) {
     }
 }
 
+template <class F, int MAXR, int PF>
+void launch_rows(const MvArgs& g, int64_t rows, hipStream_t s) {
+    hipLaunchKernelGGL((k_mmvq<F, MAXR, PF>), dim3((unsigned)mmvq_grid<F, MAXR, PF>(rows)), dim3(256),
+                       0, s, g);
+}
+
 template <class F>
 hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipStream_t s) {
     MvArgs g;
@@ -391,14 +409,20 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     g.id = (int)w.cols;
     g.od = (int)w.rows;
     g.out = out;
+    // register arrays sized to the lane's blocks per row (fewer registers,
+    // more resident waves); rows of 5..8 rounds keep two rows per wave in flight
     const int64_t nb = w.cols / kBlock;
-    const dim3 block(256);
-    if (nb <= 64 * 4)
-        hipLaunchKernelGGL((k_mmvq<F, 4>), dim3((unsigned)mmvq_grid<F, 4>(w.rows)), block, 0, s, g);
-    else if (nb <= 64 * 8)
-        hipLaunchKernelGGL((k_mmvq<F, 8>), dim3((unsigned)mmvq_grid<F, 8>(w.rows)), block, 0, s, g);
-    else
-        hipLaunchKernelGGL((k_mmvq<F, 0>), dim3((unsigned)mmvq_grid<F, 0>(w.rows)), block, 0, s, g);
+    switch ((nb + 63) / 64) {
+    case 1: launch_rows<F, 1, 1>(g, w.rows, s); break;
+    case 2: launch_rows<F, 2, 1>(g, w.rows, s); break;
+    case 3: launch_rows<F, 3, 1>(g, w.rows, s); break;
+    case 4: launch_rows<F, 4, 1>(g, w.rows, s); break;
+    case 5: launch_rows<F, 5, 2>(g, w.rows, s); break;
+    case 6: launch_rows<F, 6, 2>(g, w.rows, s); break;
+    case 7: launch_rows<F, 7, 2>(g, w.rows, s); break;
+    case 8: launch_rows<F, 8, 2>(g, w.rows, s); break;
+    default: launch_rows<F, 0, 1>(g, w.rows, s);
+    }
     return hipGetLastError();
 }
 

@@ -10,8 +10,8 @@
 // -127, 127), S = sum(q); an all-zero block has D = 0, q = 0, S = 0.
 //
 // Geometry.  One workgroup of 4 waves per row (per row segment for SwiGLU and
-// the standalone quantise when there are too few rows to fill the chip, as at
-// one token); the row is swept in rounds of 256 values, round r belonging to
+// the standalone quantise, whose rows need no row-wide reduction); the row is
+// swept in rounds of 256 values, round r belonging to
 // wave r % 4: in round r lane l owns the
 // float4 at 256*r + 4*l, so each wave access is one
 // contiguous 1 KiB (the pages' rule that a full-width coalesced access must
@@ -246,13 +246,16 @@ hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, in
     const int rounds = (int)(d / kSuper);
     const int per_wave = (rounds + 3) / 4;
     // Rows with no row-wide reduction (SwiGLU, standalone) are split into
-    // segments of at least 4 rounds when there are too few rows to fill the
-    // chip (decode); RMSNorm keeps one workgroup per row.
+    // segments: when there are few rows (decode), as many segments of at least
+    // 4 rounds as it takes to fill the chip; rows of 16 rounds or more, up to 8
+    // segments of at least 8 rounds (the last one may be shorter), so that the
+    // workgroups of a large launch are short and its last round ends evenly.
+    // RMSNorm keeps one workgroup per row.
     int segs = 1;
     if (KIND != kProdRms) {
-        const int64_t want = (2048 + rows - 1) / rows;
-        segs = (int)std::min<int64_t>(want, (rounds + 3) / 4);
-        if (segs < 1) segs = 1;
+        const int64_t fill = std::min<int64_t>((2048 + rows - 1) / rows, (rounds + 3) / 4);
+        const int64_t split = std::min<int64_t>(8, rounds / 8);
+        segs = (int)std::max<int64_t>(1, std::max(fill, split));
     }
     const int rps = (rounds + segs - 1) / segs;
     segs = (rounds + rps - 1) / rps;

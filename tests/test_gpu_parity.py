@@ -241,8 +241,14 @@ def test_gemm_full_size_sampled(ctx, wtype, od, id_):
 
 
 # ------------------------------------------------------------------ one-token GEMV
-@pytest.mark.parametrize("od,id_", [(1000, 5120), (64, 256), (300, 13824), (33, 20480),
-                                    (1024, 5120)])
+# one shape per register-array size (blocks per lane and row 1..8, then the
+# re-reading form past 8); 20000 and 9000 rows make waves walk several rows
+# (one row in flight at 3 blocks per lane, two at 5)
+GEMV_SHAPES = [(64, 256), (4100, 4096), (1000, 5120), (1024, 5120), (20000, 5120), (777, 8192),
+               (9000, 10240), (130, 12288), (300, 13824), (65, 16384), (33, 20480)]
+
+
+@pytest.mark.parametrize("od,id_", GEMV_SHAPES)
 def test_mmvq_parity(ctx, od, id_):
     rng = synth.rng_for("test", od, f"mmvq{id_}")
     raw = synth.q6k_weights(rng, od, id_)
@@ -257,8 +263,7 @@ def test_mmvq_parity(ctx, od, id_):
     mmq.mmq_weight_free(w)
 
 
-@pytest.mark.parametrize("od,id_", [(1000, 5120), (64, 256), (300, 13824), (33, 20480),
-                                    (5120, 5120), (13824, 5120)])
+@pytest.mark.parametrize("od,id_", GEMV_SHAPES + [(5120, 5120), (13824, 5120)])
 def test_mmvq_q4k_parity(ctx, od, id_):
     rng = synth.rng_for("test", od, f"mmvq4{id_}")
     raw = synth.q4k_weights(rng, od, id_)
