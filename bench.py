@@ -320,6 +320,53 @@ def cpu_baseline(seconds: float):
             "cpu_model": _cpu_model(), "seconds": round(t_used, 2)}
 
 
+def measured_peaks(torch):
+    """Ceilings measured on this device, beside the published peaks: the
+    matrix pipe's rate for the f16 and int8 32x32 MFMA instructions (a
+    benchmark kernel of independent MFMA chains, libmmq_peak.so) and the
+    device-to-device copy rate of a 1 GiB buffer (read + write bytes)."""
+    import ctypes
+    from quantized_matmul_rmsnorm_amd import build as _b
+    lib = ctypes.CDLL(_b.LIB_PEAK)
+    for fn in (lib.mmq_peak_mfma_f16, lib.mmq_peak_mfma_i8):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    chains = lib.mmq_peak_chains()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * n_cu, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn, ops_per_mfma in (("mfma_f16_32x32x16_TFLOPs", lib.mmq_peak_mfma_f16, 2 * 32 * 32 * 16),
+                                   ("mfma_i8_32x32x32_TOPs", lib.mmq_peak_mfma_i8, 2 * 32 * 32 * 32)):
+        if fn(out.data_ptr(), blocks, iters, stream.cuda_stream) != 0:
+            raise RuntimeError(f"{name}: launch failed")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            if fn(out.data_ptr(), blocks, iters, stream.cuda_stream) != 0:
+                raise RuntimeError(f"{name}: launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        ops = 3 * blocks * 4 * iters * chains * ops_per_mfma
+        res[name] = round(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    nel = (1 << 30) // 4
+    src = torch.ones(nel, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    res["hbm_copy_GB_s"] = round(5 * 2 * nel * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst, out
+    return res
+
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "quantized_matmul_rmsnorm_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_da_q4k_traffic_7b_chain.txt")
@@ -369,7 +416,7 @@ def main():
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     from quantized_matmul_rmsnorm_amd import build as _b
-    if not os.path.exists(_b.LIB):
+    if not (os.path.exists(_b.LIB) and os.path.exists(_b.LIB_PEAK)):
         _b.build()
     import quantized_matmul_rmsnorm_amd as mmq
     import synth
@@ -464,7 +511,12 @@ def main():
     log(f"graph replay: {graph_ms:.2f} ms/step")
 
     traffic = measured_traffic()
+    peaks = measured_peaks(torch)
+    log(f"measured: f16 MFMA {peaks['mfma_f16_32x32x16_TFLOPs']} TFLOP/s, int8 MFMA "
+        f"{peaks['mfma_i8_32x32x32_TOPs']} TOP/s, copy {peaks['hbm_copy_GB_s']} GB/s")
     decode = None if args.no_decode else decode_gemv(mmq, torch, synth)
+    if decode is not None:
+        decode["aggregate_frac_measured_copy"] = round(decode["aggregate_GB_s"] / peaks["hbm_copy_GB_s"], 4)
     small = small_n_sweep(mmq, torch, synth) if args.small_n else None
     f16ref = f16_reference(torch) if args.f16_reference else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
@@ -495,7 +547,10 @@ def main():
                      "kernel": "k_gemm_da<true> (q4_K)",
                      "ops_per_launch": q4_ops_launch,
                      "algorithmic_bytes_per_launch": round(q4_alg_bytes), "avg_launch_us": round(q4_avg_us, 2),
-                     "frac_of_f16_mfma_peak": round(achieved / PEAK_F16_TOPS, 4)},
+                     "frac_of_f16_mfma_peak": round(achieved / PEAK_F16_TOPS, 4),
+                     "frac_of_measured_f16_mfma": round(achieved / peaks["mfma_f16_32x32x16_TFLOPs"], 4),
+                     "frac_of_measured_i8_mfma": round(achieved / peaks["mfma_i8_32x32x32_TOPs"], 4)},
+        "measured_peaks": peaks,
         "kernels": kernels,
         "graph": graph_rec,
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},

@@ -1,0 +1,40 @@
+/* mmq_peak.h -- measured matrix-core ceilings (libmmq_peak.so).
+ *
+ * A measurement aid for the benchmark's roofline, separate from the matmul
+ * library: it runs the two 32x32 MFMA instructions a q8 matmul on gfx950 can
+ * use (f16 32x32x16, on integer-valued operands, and int8 32x32x32) back to
+ * back, so the achieved rate of the matmul can be set against what the
+ * matrix pipe delivers on this device at its clock under load, beside the
+ * published peaks.
+ *
+ * Each launch runs `blocks` workgroups of 256 threads (4 waves); every wave
+ * issues `iters` rounds of mmq_peak_chains() independent MFMAs on register
+ * operands and writes one value per thread to `out`, so a launch performs
+ *   blocks * 4 * iters * mmq_peak_chains() * (2*32*32*16)   f16 operations, or
+ *   blocks * 4 * iters * mmq_peak_chains() * (2*32*32*32)   int8 operations.
+ * Time the launch with events on `stream`.
+ *
+ * Arguments: `out` is a caller-owned device buffer of blocks * 256 elements
+ * (float for f16, int32 for int8; its contents are meaningless); blocks >= 1,
+ * 1 <= iters <= 2^20; `stream` is the caller's HIP stream (0 for the null
+ * stream).  Returns 0 on success, -1 for an invalid argument (nothing is
+ * launched), or the HIP error code of the launch.
+ */
+#ifndef MMQ_PEAK_H
+#define MMQ_PEAK_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int mmq_peak_chains(void);
+int mmq_peak_mfma_f16(float* out, int blocks, int iters, hipStream_t stream);
+int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMQ_PEAK_H */

@@ -1,4 +1,5 @@
-"""Build libmmq.so (the gfx950 HIP kernels and the C-ABI host library) in-tree.
+"""Build libmmq.so (the gfx950 HIP kernels and the C-ABI host library) in-tree,
+and libmmq_peak.so (measured MFMA ceilings; loaded by the benchmark only).
 
 hipcc cross-compiles for gfx950 without a GPU.  Every HIP translation unit is
 built with -O3, no fast-math (the quantiser relies on IEEE division and
@@ -16,7 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmmq.so")
+LIB_PEAK = os.path.join(PKG, "libmmq_peak.so")
 SOURCES = ["quant.hip", "repack.hip", "gemm.hip", "mmvq.hip", "host.cpp"]
+PEAK_SOURCES = ["peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -36,16 +39,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs,
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build() -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAK_SOURCES], LIB_PEAK)
     return LIB
 
 

@@ -10,10 +10,15 @@
 //
 // How it maps onto CDNA4.  The integer dots run on v_mfma_f32_32x32x16_f16 with
 // integer-valued f16 operands: the activation codes (|q| <= 127) and the
-// registration-time weight values sc_j*q_w (q4_K, <= 945) or sc*(q_w-32) split
-// into an even part and a 0/1 part (q6_K, |v| <= 4096) are exact in f16,
-// every product is exact in f32 and every partial sum of one block stays below
-// 2^24, so the MFMA returns the exact integer block dot as an f32.  Folding the
+// weight values -- for q4_K sc_j*q_w (<= 945), folded at registration; for
+// q6_K v = sc*(q_w-32) (|v| <= 4096, 13 bits), formed by each wave from the
+// stored code q_w-32 and its f16 sub-scale as hi = f16(v) and lo = v - hi
+// (one packed multiply and one packed fma per pair; |lo| <= 1) -- are exact
+// in f16, every product is exact in f32 and every partial sum of one block
+// stays below 2^24, so the MFMA returns the exact integer block dot as an f32.
+// (Streaming the q6_K code instead of the two parts halves the bytes each
+// wave loads per weight, and the vector-memory return path is what this
+// kernel's q6_K arm waits on.)  Folding the
 // weight's sub-scale into the operand leaves one FMA per output per block
 // (acc += D[t][b] * X) with D constant per lane, because tokens sit on the
 // MFMA's N axis (lane % 32) and outputs on its M axis (registers).  An int8
@@ -141,11 +146,10 @@ struct GemmArgs {
 // prefetch distance is RA-1 blocks).
 template <bool Q4K>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
-    constexpr int NPART = Q4K ? 1 : 2;
     constexpr int CH = 4;                   // 32-blocks per staged activation chunk
     constexpr int SBCH = 8 / CH;
     constexpr int NDM = Q4K ? 2 : 1;
-    constexpr int RA = Q4K ? 4 : 2;         // weight-fragment ring depth (divides 8)
+    constexpr int RA = 4;                   // weight-fragment ring depth (divides 8)
     constexpr int PD = RA - 1;              // prefetch distance in blocks
     constexpr int BPAD = 4, DPAD = 16;
     constexpr int NBUF = 3;
@@ -178,16 +182,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     const auto rM = rsrc(g.dmr, g.dmr_bytes);
     const auto rF = rsrc(g.mfrag, g.mfrag_bytes);
 
-    // this wave's weight fragments: block b, k16, part at voffA + b * 2*NPART KiB
-    const uint32_t voffA = ((uint32_t)(og0 + ogl) * (uint32_t)K16 * NPART) * 1024u + (uint32_t)lane * 16u;
-    half8 ring[RA][2][NPART];
+    // this wave's weight fragments: block b, half k16 at voffA + (2b + k16) KiB
+    const uint32_t voffA = ((uint32_t)(og0 + ogl) * (uint32_t)K16) * 1024u + (uint32_t)lane * 16u;
+    half8 ring[RA][2];
     auto load_a = [&](int b, int slot) {
 #pragma unroll
         for (int k16 = 0; k16 < 2; ++k16)
-#pragma unroll
-            for (int p = 0; p < NPART; ++p)
-                ring[slot][k16][p] = bload<half8>(rA, voffA + (uint32_t)((k16 * NPART + p) * 1024),
-                                                  (uint32_t)b * (2u * NPART * 1024u));
+            ring[slot][k16] = bload<half8>(rA, voffA + (uint32_t)(k16 * 1024), (uint32_t)b * 2048u);
     };
 
     const int tb = tid >> 2;
@@ -238,6 +239,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
         if (first) sDM[(c / SBCH) & 1][tid] = rdm;
     };
 
+    // q6_K: this lane's row's 16 sub-scales of the current superblock as f16
+    // pairs (sc[2j], sc[2j+1]) for block j, and those of the next superblock
+    uint32_t scv[8], scn[8];
+    auto load_sc = [&](int sbx, uint32_t* dst) {
+        const uint32_t off = (uint32_t)((((og0 + ogl) * nsb + sbx) * 32 + (lane & 31)) * 32);
+        const uint4 a = bload<uint4>(rF, off, 0u);
+        const uint4 b = bload<uint4>(rF, off + 16u, 0u);
+        dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+        dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+    };
     f32x16 acc[2], res[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -252,6 +263,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     const int c0 = sb0 * SBCH, c_end = sb1 * SBCH;
 #pragma unroll
     for (int b = 0; b < PD; ++b) load_a(8 * sb0 + b, b);   // 8 blocks per split > PD; slot b % RA
+    if (!Q4K) {
+        load_sc(sb0, scv);
+        load_sc(min(sb0 + 1, sb1 - 1), scn);
+    }
     load_chunk(c0, true);
     store_chunk(c0, 0, true, true);
     load_chunk(c0 + 1, false);
@@ -283,19 +298,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
             if (Q4K && cc == SBCH - 1)
                 mf = bload<half8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
             f32x16 X[2][2];
-            auto mfma_block = [&](int slot, half8 (*bf)[2], f32x16* Xo) {
+            auto mfma_block = [&](int j, int slot, half8 (*bf)[2], f32x16* Xo) {
+                if constexpr (Q4K) {
 #pragma unroll
-                for (int k16 = 0; k16 < 2; ++k16) {
+                    for (int k16 = 0; k16 < 2; ++k16) {
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        if (k16 == 0) {
-                            const f32x16 zero = {};
-                            Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][0][0], bf[i][0], zero, 0, 0, 0);
-                        } else {
-                            Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][1][0], bf[i][1], Xo[i], 0, 0, 0);
+                        for (int i = 0; i < 2; ++i) {
+                            if (k16 == 0) {
+                                const f32x16 zero = {};
+                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][0], bf[i][0], zero, 0, 0, 0);
+                            } else {
+                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][1], bf[i][1], Xo[i], 0, 0, 0);
+                            }
                         }
-                        if (!Q4K)
-                            Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][k16][NPART - 1], bf[i][k16], Xo[i], 0, 0, 0);
+                    }
+                } else {
+                    // A = sc * c split exactly into hi = f16(sc * c) and
+                    // lo = sc * c - hi (|lo| <= 1): both are exact f16 integers
+                    const uint32_t sp = scv[j];
+                    const half2v s2[2] = {__builtin_bit_cast(half2v, __builtin_amdgcn_perm(sp, sp, 0x01000100u)),
+                                          __builtin_bit_cast(half2v, __builtin_amdgcn_perm(sp, sp, 0x03020302u))};
+#pragma unroll
+                    for (int k16 = 0; k16 < 2; ++k16) {
+                        const half8 c = ring[slot][k16];
+                        half8 hi, lo;
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            const half2v cp = {c[2 * p], c[2 * p + 1]};
+                            const half2v h = cp * s2[k16];
+                            const half2v l = __builtin_elementwise_fma(cp, s2[k16], -h);
+                            hi[2 * p] = h[0]; hi[2 * p + 1] = h[1];
+                            lo[2 * p] = l[0]; lo[2 * p + 1] = l[1];
+                        }
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            if (k16 == 0) {
+                                const f32x16 zero = {};
+                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, bf[i][0], zero, 0, 0, 0);
+                            } else {
+                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, bf[i][1], Xo[i], 0, 0, 0);
+                            }
+                            Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, bf[i][k16], Xo[i], 0, 0, 0);
+                        }
                     }
                 }
             };
@@ -326,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
                 if (jj + 1 < CH) read_b(bcur, jj + 1, bfr[(jj + 1) & 1]);
                 else read_b(bnext, 0, bfr[0]);         // next chunk: stored at this step's start, past the barrier
                 __builtin_amdgcn_s_setprio(1);   // wave priority only (not a queue priority)
-                mfma_block(j % RA, bfr[jj & 1], X[jj & 1]);
+                mfma_block(j, j % RA, bfr[jj & 1], X[jj & 1]);
                 __builtin_amdgcn_s_setprio(0);
                 if (jj > 0) epilogue_block(jj - 1, X[(jj - 1) & 1]);
                 if (jj == kBarAt) __syncthreads();
@@ -356,6 +400,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
                 }
             }
             bcur = bnext;
+        }
+        if (!Q4K) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) scv[i] = scn[i];
+            load_sc(min(sb + 2, sb1 - 1), scn);
         }
     }
 
@@ -513,11 +562,10 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.q = pl.q;
     a.D = pl.D;
     a.S = pl.S;
-    const int npart = w.type == 12 ? 1 : 2;
     const int64_t nsb = w.cols / kSuper, og = w.rows_pad / 32;
-    a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * npart * 2);
+    a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * 2);
     a.dmr_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 64 : 32) * 4);
-    a.mfrag_bytes = w.type == 12 ? (uint32_t)(og * nsb * 512 * 2) : 0u;
+    a.mfrag_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 512 * 2 : 32 * 16 * 2));
     a.q_bytes = (uint32_t)(pl.rows * pl.d);
     a.ds_bytes = (uint32_t)(pl.rows * (pl.d / kBlock) * 4);
     a.n = (int)n;

@@ -468,10 +468,12 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     const int64_t nsb = cols / kSuper, nb = cols / kBlock, og = w.rows_pad / 32;
     const int64_t bpb = type == MMQ_Q4_K ? 144 : 210;
     const int64_t raw_bytes = rows * nsb * bpb;
-    const int npart = type == MMQ_Q4_K ? 1 : 2;
-    const int64_t wa_b = w.rows_pad * cols * npart * 2;
+    // matmul tiles: one f16 per weight (q4_K sc*q, q6_K q-32), superblock
+    // scales, and per (row group, superblock) the q4_K mins or the q6_K
+    // sub-scales as f16
+    const int64_t wa_b = w.rows_pad * cols * 2;
     const int64_t dmr_b = og * nsb * (type == MMQ_Q4_K ? 64 : 32) * 4;
-    const int64_t mf_b = type == MMQ_Q4_K ? og * nsb * 512 * 2 : 0;
+    const int64_t mf_b = og * nsb * (type == MMQ_Q4_K ? 512 * 2 : 32 * 16 * 2);
     // one-token GEMV tiles: q6_K ql/qh/sc/d; q4_K nibbles (in ql), (sc, m)
     // pairs (in sc) and (d, dmin) per superblock (in d), no qh
     const int64_t ql_b = rows * nb * 16, qh_b = type == MMQ_Q6_K ? rows * nb * 8 : 0,

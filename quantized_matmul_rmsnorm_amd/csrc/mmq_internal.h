@@ -32,9 +32,10 @@ struct WeightDev {
     int64_t rows = 0, cols = 0, rows_pad = 0;
     unsigned uses = 0;
     // prefill matmul tiles
-    _Float16* wa = nullptr;   // f16 integer-valued A fragments
+    _Float16* wa = nullptr;   // f16 integer-valued A fragments (q4_K sc*q, q6_K q-32)
     float* dmr = nullptr;     // per (row group, superblock) scales, fragment order
-    _Float16* mfrag = nullptr;// q4_K only: 6-bit mins as f16, fragment order
+    _Float16* mfrag = nullptr;// q4_K: 6-bit mins as f16, fragment order;
+                              // q6_K: [row group][superblock][32 rows][16] f16 sub-scales
     // one-token GEMV
     uint4* gv_ql = nullptr;   // [rows][cols/32] 4-bit codes (q6_K: their low nibbles)
     uint2* gv_qh = nullptr;   // q6_K: [rows][cols/32] high bit pairs

@@ -22,10 +22,9 @@
 //         dmr[og][sb][{d,dmin}][half][r] f32, r/half as the MFMA output row
 //             of ol: ol = 8*(r/4) + 4*half + r%4
 //         mfrag[og][sb][lane][j] = f16(m_j) for both lane halves (exact)
-//   q6_K: v = sc * (q - 32) in [-4096, 4096] needs 13 bits, more than f16
-//         holds exactly, so it is split v = hi + lo with lo = v & 1 and hi
-//         even (exact in f16 up to 4096):
-//         wa[og][k16][part][lane][e] = f16(part ? lo : hi)
+//   q6_K: wa[og][k16][lane][e] = f16(q - 32)     (exact; the matmul forms
+//             sc * (q - 32), 13 bits, as two exact f16 parts in registers)
+//         mfrag[og][sb][ol][i] = f16(sc_i), i = 0..15 (exact)
 //         dmr[og][sb][half][r] = d
 // One-token GEMV tiles (q6_K, read by mmvq.hip), per row o and 32-block b
 // (weights w_0..w_31):
@@ -123,7 +122,8 @@ __global__ void k_repack_q4k_gemm(const uint8_t* __restrict__ raw, int64_t rows,
 }
 
 __global__ void k_repack_q6k_gemm(const uint8_t* __restrict__ raw, int64_t rows, int64_t cols,
-                                  _Float16* __restrict__ wa, float* __restrict__ dmr) {
+                                  _Float16* __restrict__ wa, float* __restrict__ dmr,
+                                  _Float16* __restrict__ wsc) {
     const int64_t nsb = cols / kSuper;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= rows * nsb) return;
@@ -133,18 +133,15 @@ __global__ void k_repack_q6k_gemm(const uint8_t* __restrict__ raw, int64_t rows,
     const int8_t* scales = reinterpret_cast<const int8_t*>(blk + 192);
     const int64_t K16 = cols / 16;
     for (int e = 0; e < kSuper; ++e) {
-        const int v = (int)scales[e / 16] * (q6k_quant(blk, e) - 32);
-        const int lo = v & 1;
-        const int hi = v - lo;
         int64_t og, k16; int lane, el;
         frag_pos(o, sb * kSuper + e, og, lane, el, k16);
-        const int64_t base = (og * K16 + k16) * 2;
-        wa[((base + 0) * 64 + lane) * 8 + el] = (_Float16)(float)hi;
-        wa[((base + 1) * 64 + lane) * 8 + el] = (_Float16)(float)lo;
+        wa[((og * K16 + k16) * 64 + lane) * 8 + el] = (_Float16)(float)(q6k_quant(blk, e) - 32);
     }
     const int64_t og = o / 32;
+    const int ol = (int)(o % 32);
+    for (int i = 0; i < 16; ++i) wsc[((og * nsb + sb) * 32 + ol) * 16 + i] = (_Float16)(float)scales[i];
     int half;
-    const int r = out_reg((int)(o % 32), half);
+    const int r = out_reg(ol, half);
     dmr[(og * nsb + sb) * 32 + half * 16 + r] = d;
 }
 
@@ -226,7 +223,7 @@ hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStr
                            w.dmr, w.mfrag);
     else
         hipLaunchKernelGGL(k_repack_q6k_gemm, grid, block, 0, s, raw_dev, w.rows, w.cols, w.wa,
-                           w.dmr);
+                           w.dmr, w.mfrag);
     return hipGetLastError();
 }
 

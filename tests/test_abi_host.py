@@ -37,6 +37,28 @@ def test_every_declared_symbol_is_exported():
         assert getattr(ctypes.CDLL(_lib.LIB_PATH), name) is not None
 
 
+def test_peak_library_exports_its_header():
+    """libmmq_peak.so (the benchmark's measured MFMA ceilings) exports exactly
+    what include/mmq_peak.h declares, and rejects bad arguments without a
+    launch (no device is touched: the checks come first)."""
+    from quantized_matmul_rmsnorm_amd import build as _b
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mmq_peak.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(mmq\w+)\s*\(", text)))
+    assert declared == ["mmq_peak_chains", "mmq_peak_mfma_f16", "mmq_peak_mfma_i8"]
+    out = subprocess.run(["nm", "-D", "--defined-only", _b.LIB_PEAK], capture_output=True,
+                         text=True, check=True).stdout
+    dyn = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(declared) <= dyn
+    lib = ctypes.CDLL(_b.LIB_PEAK)
+    assert lib.mmq_peak_chains() == 8
+    for fn in (lib.mmq_peak_mfma_f16, lib.mmq_peak_mfma_i8):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        assert fn(None, 1, 1, None) == -1
+        assert fn(ctypes.c_void_p(0x1000), 0, 1, None) == -1
+        assert fn(ctypes.c_void_p(0x1000), 1, 0, None) == -1
+        assert fn(ctypes.c_void_p(0x1000), 1, (1 << 20) + 1, None) == -1
+
+
 def test_no_device_is_reported():
     with pytest.raises(mmq.MmqError) as e:
         mmq.mmq_create(999, 0)
@@ -97,7 +119,9 @@ def test_registration_validation(ctx):
     # q4_K: f16 tiles (2 B/weight) + scales + mins; q6_K adds the GEMV layout
     assert mmq.mmq_weight_bytes(w4) == 512 * 256 * 2 + 16 * 1 * 64 * 4 + 16 * 1 * 512 * 2
     rows_pad = 1024
-    gemm6 = rows_pad * 512 * 4 + (rows_pad // 32) * 2 * 32 * 4
+    # q6_K matmul tiles: f16 centred codes (2 B/weight), d per row and
+    # superblock, and 16 f16 sub-scales per row and superblock
+    gemm6 = rows_pad * 512 * 2 + (rows_pad // 32) * 2 * 32 * 4 + rows_pad * 2 * 16 * 2
     gemv6 = 1000 * 16 * (16 + 8 + 2) + 1000 * 2 * 4
     assert mmq.mmq_weight_bytes(w6) == gemm6 + gemv6
     assert mmq.mmq_stats(ctx)["weight_bytes"] == mmq.mmq_weight_bytes(w4) + mmq.mmq_weight_bytes(w6)
