@@ -278,22 +278,33 @@ def f16_reference(torch):
             "TFLOP_s": round(2 * TOKENS * HIDDEN * FFN / (us * 1e-6) / 1e12, 1)}
 
 
-def cpu_baseline(seconds: float):
-    """The CPU oracle (as it is) on a bounded sample of one layer of the chain:
-    producers and all seven matmuls for a growing number of tokens, run until
-    about `seconds` of CPU time; reported in the chain's unit (TOPS)."""
+_LAYER0 = []
+
+
+def _layer0_inputs():
+    """Layer 0's weights and activations of the chain, generated once."""
+    if not _LAYER0:
+        import synth
+        raws = {name: synth.weights(wt, synth.rng_for("chain7b", 0, name), od, id_)
+                for name, wt, od, id_, _ in LAYER_GEMMS}
+        _LAYER0.extend([
+            raws,
+            synth.activations(synth.rng_for("chain7b", 0, "x_attn"), TOKENS, HIDDEN),
+            synth.activations(synth.rng_for("chain7b", 0, "attn_out"), TOKENS, HIDDEN),
+            synth.activations(synth.rng_for("chain7b", 0, "x_ffn"), TOKENS, HIDDEN),
+            synth.rms_weight(synth.rng_for("chain7b", 0, "norm_attn"), HIDDEN),
+            synth.rms_weight(synth.rng_for("chain7b", 0, "norm_ffn"), HIDDEN)])
+    return _LAYER0
+
+
+def _oracle_layer_sample(seconds: float):
+    """The CPU oracle on layer 0 of the chain (both RMSNorm producers, the
+    standalone quantise, SwiGLU and all seven matmuls) for a growing number
+    of tokens until about `seconds`; returns (TOPS, tokens, seconds)."""
     import oracle
-    import synth
     t_used = 0.0
-    ops = 0
     tok_done = 0
-    raws = {name: synth.weights(wt, synth.rng_for("chain7b", 0, name), od, id_)
-            for name, wt, od, id_, _ in LAYER_GEMMS}
-    x = synth.activations(synth.rng_for("chain7b", 0, "x_attn"), TOKENS, HIDDEN)
-    a = synth.activations(synth.rng_for("chain7b", 0, "attn_out"), TOKENS, HIDDEN)
-    h = synth.activations(synth.rng_for("chain7b", 0, "x_ffn"), TOKENS, HIDDEN)
-    n1 = synth.rms_weight(synth.rng_for("chain7b", 0, "norm_attn"), HIDDEN)
-    n2 = synth.rms_weight(synth.rng_for("chain7b", 0, "norm_ffn"), HIDDEN)
+    raws, x, a, h, n1, n2 = _layer0_inputs()
     chunk = 4
     while t_used < seconds and tok_done + chunk <= TOKENS:
         sl = slice(tok_done, tok_done + chunk)
@@ -312,12 +323,57 @@ def cpu_baseline(seconds: float):
         t_used += time.perf_counter() - t0
         tok_done += chunk
     ops = 2 * tok_done * sum(od * id_ for _, _, od, id_, _ in LAYER_GEMMS)
-    return {"value": round(ops / t_used / 1e12, 6), "unit": "TOPS", "cores": oracle.threads(),
+    return ops / t_used / 1e12, tok_done, t_used
+
+
+def _oracle_decode_full():
+    """The CPU oracle on the whole 14B decode step of the GEMV leg: RMSNorm and
+    SwiGLU producers at one token, then the attn_v, ffn_down and lm_head q6_K
+    GEMVs in full; returns (GB/s over the GEMVs' algorithmic bytes, seconds)."""
+    import oracle
+    import synth
+    x = synth.activations(synth.rng_for("decode14b", 0, "x"), 1, 5120)
+    wn = synth.rms_weight(synth.rng_for("decode14b", 0, "norm"), 5120)
+    g = synth.activations(synth.rng_for("decode14b", 0, "gate"), 1, 13824)
+    u = synth.activations(synth.rng_for("decode14b", 0, "up"), 1, 13824)
+    shapes = {"attn_v": (1024, 5120), "ffn_down": (5120, 13824), "lm_head": (152064, 5120)}
+    raws = {k: synth.q6k_weights(synth.rng_for("decode14b", 0, k), od, id_) for k, (od, id_) in shapes.items()}
+    t0 = time.perf_counter()
+    p5 = oracle.quantize(oracle.rmsnorm(x, wn, 1e-6))
+    p13 = oracle.quantize(oracle.swiglu(g, u))
+    byts = 0.0
+    for k, (od, id_) in shapes.items():
+        oracle.gemm("q6_K", *(p5 if id_ == 5120 else p13), raws[k], od, id_)
+        byts += od * id_ / 256 * 210 + id_ * 1.25 + od * 4
+    dt = time.perf_counter() - t0
+    return byts / dt / 1e9, dt
+
+
+def cpu_baseline(seconds: float):
+    """The CPU oracle (as it is) on a bounded sample of one layer of the chain,
+    reported in the chain's unit (TOPS) on all the threads it uses; beside it,
+    the same sample on one thread (a shorter one) and the 14B decode GEMV step
+    in full (GB/s)."""
+    import oracle
+    tops, tok_done, t_used = _oracle_layer_sample(seconds)
+    n_all = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        tops1, tok1, t1 = _oracle_layer_sample(max(1.0, seconds / 4))
+    finally:
+        oracle.set_threads(n_all)
+    dec_gbs, dec_s = _oracle_decode_full()
+    return {"value": round(tops, 6), "unit": "TOPS", "cores": n_all,
             "kind": "oracle",
             "sample": f"layer 0 of the chain (both RMSNorm producers, the standalone quantise, "
                       f"SwiGLU and all 7 matmuls) for {tok_done} of {TOKENS} tokens, "
                       f"{t_used:.1f} s; the work is linear in tokens",
-            "cpu_model": _cpu_model(), "seconds": round(t_used, 2)}
+            "cpu_model": _cpu_model(), "seconds": round(t_used, 2),
+            "one_thread": {"value": round(tops1, 6), "unit": "TOPS", "tokens": tok1,
+                           "seconds": round(t1, 2)},
+            "decode_gemv_full": {"value": round(dec_gbs, 3), "unit": "GB/s", "seconds": round(dec_s, 2),
+                                 "sample": "14B decode step in full: RMSNorm 5120 and SwiGLU 13824 "
+                                           "producers, attn_v, ffn_down and lm_head q6_K GEMVs"}}
 
 
 def measured_peaks(torch):
