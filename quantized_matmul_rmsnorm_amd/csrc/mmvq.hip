@@ -23,9 +23,9 @@
 // its codes.  For q6_K the "- 32" of the code is applied through the
 // activation: the dot accumulator starts at -32 * sum(q) of the half,
 // computed once per lane.  One f32 expression per block adds the block's
-// term; a wave-wide sum per row finishes the output.  The weights of the
-// wave's next row (next two rows for long rows) are in flight while a row is
-// reduced.
+// term; a wave-wide sum per row finishes the output.  For rows of up to 256
+// blocks the plane slice stays in registers and the weights of the wave's
+// next row are in flight while a row is reduced.
 #include <algorithm>
 
 #include "mmq_internal.h"
@@ -184,11 +184,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // MAXR > 0: the lane's activation blocks stay in registers (nb <= 64 * MAXR),
-// and the weights of the wave's next PF rows are in flight: a row's
-// registers for a block are refilled with the row PF steps ahead as soon as
-// the block is consumed.
+// and the weights of the wave's next row are loaded block by block as soon as
+// the current row's registers for that block are consumed, so a row's loads
+// are in flight while the previous row is reduced.
 // MAXR == 0: blocks are re-read from the plane for every row (any length).
-template <class F, int MAXR, int PF>
+template <class F, int MAXR>
 __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -200,38 +200,28 @@ __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
 
     if constexpr (MAXR > 0) {
         typename F::Act act[MAXR];
-        typename F::W w[PF][MAXR];
+        typename F::W w[MAXR];
 #pragma unroll
         for (int r = 0; r < MAXR; ++r)
             if (r < rounds && 64 * r + lane < nb) act[r] = F::act(g, 64 * r + lane);
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int op = wave + p * nwaves;
-            if (op < od) {
-#pragma unroll
-                for (int r = 0; r < MAXR; ++r)
-                    if (r < rounds && 64 * r + lane < nb) w[p][r] = F::load(g, op, 64 * r + lane, nb, nsb);
-            }
-        }
         int o = wave;
-        while (o < od) {
+        if (o < od) {
 #pragma unroll
-            for (int p = 0; p < PF; ++p) {
-                if (o < od) {
-                    const int on = o + PF * nwaves;
-                    float acc = 0.0f;
+            for (int r = 0; r < MAXR; ++r)
+                if (r < rounds && 64 * r + lane < nb) w[r] = F::load(g, o, 64 * r + lane, nb, nsb);
+        }
+        for (; o < od; o += nwaves) {
+            const int on = o + nwaves;
+            float acc = 0.0f;
 #pragma unroll
-                    for (int r = 0; r < MAXR; ++r) {
-                        if (r < rounds && 64 * r + lane < nb) {
-                            acc += F::term(act[r], w[p][r]);
-                            if (on < od) w[p][r] = F::load(g, on, 64 * r + lane, nb, nsb);
-                        }
-                    }
-                    acc = wave_sum(acc);
-                    if (lane == 0) g.out[o] = acc;
+            for (int r = 0; r < MAXR; ++r) {
+                if (r < rounds && 64 * r + lane < nb) {
+                    acc += F::term(act[r], w[r]);
+                    if (on < od) w[r] = F::load(g, on, 64 * r + lane, nb, nsb);
                 }
-                o += nwaves;
             }
+            acc = wave_sum(acc);
+            if (lane == 0) g.out[o] = acc;
         }
     } else {
         for (int o = wave; o < od; o += nwaves) {
@@ -249,14 +239,14 @@ __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
 // Workgroups of one launch: every row gets a wave when the rows fit in two
 // rounds of resident waves; larger matrices get exactly the resident waves
 // (each then walks rows grid-stride with its plane slice loaded once).
-template <class F, int MAXR, int PF>
+template <class F, int MAXR>
 int64_t mmvq_grid(int64_t rows) {
     static int per_cu = -1, n_cu = 0;
     if (per_cu < 0) {
         int dev = 0, blk = 0;
         (void)hipGetDevice(&dev);
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq<F, MAXR, PF>, 256, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq<F, MAXR>, 256, 0) !=
             hipSuccess)
             blk = 1;
         per_cu = blk > 0 ? blk : 1;
@@ -390,10 +380,9 @@ __global__ __launch_bounds__(512) void k_mmvqn(const MvArgs g, int n, int t0) {
     }
 }
 
-template <class F, int MAXR, int PF>
+template <class F, int MAXR>
 void launch_rows(const MvArgs& g, int64_t rows, hipStream_t s) {
-    hipLaunchKernelGGL((k_mmvq<F, MAXR, PF>), dim3((unsigned)mmvq_grid<F, MAXR, PF>(rows)), dim3(256),
-                       0, s, g);
+    hipLaunchKernelGGL((k_mmvq<F, MAXR>), dim3((unsigned)mmvq_grid<F, MAXR>(rows)), dim3(256), 0, s, g);
 }
 
 template <class F>
@@ -409,19 +398,16 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     g.id = (int)w.cols;
     g.od = (int)w.rows;
     g.out = out;
-    // register arrays sized to the lane's blocks per row (fewer registers,
-    // more resident waves); rows of 5..8 rounds keep two rows per wave in flight
+    // up to 4 blocks per lane and row: register arrays sized to exactly that
+    // many (fewer registers, more resident waves); longer rows re-read the
+    // plane per row, which leaves room for 8 waves per SIMD, a wave per row
     const int64_t nb = w.cols / kBlock;
     switch ((nb + 63) / 64) {
-    case 1: launch_rows<F, 1, 1>(g, w.rows, s); break;
-    case 2: launch_rows<F, 2, 1>(g, w.rows, s); break;
-    case 3: launch_rows<F, 3, 1>(g, w.rows, s); break;
-    case 4: launch_rows<F, 4, 1>(g, w.rows, s); break;
-    case 5: launch_rows<F, 5, 2>(g, w.rows, s); break;
-    case 6: launch_rows<F, 6, 2>(g, w.rows, s); break;
-    case 7: launch_rows<F, 7, 2>(g, w.rows, s); break;
-    case 8: launch_rows<F, 8, 2>(g, w.rows, s); break;
-    default: launch_rows<F, 0, 1>(g, w.rows, s);
+    case 1: launch_rows<F, 1>(g, w.rows, s); break;
+    case 2: launch_rows<F, 2>(g, w.rows, s); break;
+    case 3: launch_rows<F, 3>(g, w.rows, s); break;
+    case 4: launch_rows<F, 4>(g, w.rows, s); break;
+    default: launch_rows<F, 0>(g, w.rows, s);
     }
     return hipGetLastError();
 }
