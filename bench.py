@@ -379,8 +379,9 @@ def cpu_baseline(seconds: float):
 def measured_peaks(torch):
     """Ceilings measured on this device, beside the published peaks: the
     matrix pipe's rate for the f16 and int8 32x32 MFMA instructions (a
-    benchmark kernel of independent MFMA chains, libmmq_peak.so) and the
-    device-to-device copy rate of a 1 GiB buffer (read + write bytes)."""
+    benchmark kernel of independent MFMA chains, libmmq_peak.so), a read-only
+    stream over 2 GiB (the same library) and the device-to-device copy rate
+    of a 1 GiB buffer (read + write bytes)."""
     import ctypes
     from quantized_matmul_rmsnorm_amd import build as _b
     lib = ctypes.CDLL(_b.LIB_PEAK)
@@ -407,6 +408,24 @@ def measured_peaks(torch):
         torch.cuda.synchronize()
         ops = 3 * blocks * 4 * iters * chains * ops_per_mfma
         res[name] = round(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    lib.mmq_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.mmq_peak_read.restype = ctypes.c_int
+    rbytes = 2 << 30
+    rbuf = torch.ones(rbytes // 4, dtype=torch.float32, device="cuda")
+    rblocks = 8 * n_cu
+    rout = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+    for rep in range(6):    # one warm-up, five timed
+        if rep == 1:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        if lib.mmq_peak_read(rbuf.data_ptr(), rbytes, rout.data_ptr(), rblocks, stream.cuda_stream) != 0:
+            raise RuntimeError("read stream: launch failed")
+    e1 = torch.cuda.Event(enable_timing=True)
+    e1.record()
+    torch.cuda.synchronize()
+    res["hbm_read_GB_s"] = round(5 * rbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del rbuf, rout
     nel = (1 << 30) // 4
     src = torch.ones(nel, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -569,10 +588,12 @@ def main():
     traffic = measured_traffic()
     peaks = measured_peaks(torch)
     log(f"measured: f16 MFMA {peaks['mfma_f16_32x32x16_TFLOPs']} TFLOP/s, int8 MFMA "
-        f"{peaks['mfma_i8_32x32x32_TOPs']} TOP/s, copy {peaks['hbm_copy_GB_s']} GB/s")
+        f"{peaks['mfma_i8_32x32x32_TOPs']} TOP/s, read {peaks['hbm_read_GB_s']} GB/s, "
+        f"copy {peaks['hbm_copy_GB_s']} GB/s")
     decode = None if args.no_decode else decode_gemv(mmq, torch, synth)
     if decode is not None:
         decode["aggregate_frac_measured_copy"] = round(decode["aggregate_GB_s"] / peaks["hbm_copy_GB_s"], 4)
+        decode["aggregate_frac_measured_read"] = round(decode["aggregate_GB_s"] / peaks["hbm_read_GB_s"], 4)
     small = small_n_sweep(mmq, torch, synth) if args.small_n else None
     f16ref = f16_reference(torch) if args.f16_reference else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)

@@ -1,4 +1,5 @@
-/* mmq_peak.h -- measured matrix-core ceilings (libmmq_peak.so).
+/* mmq_peak.h -- measured ceilings: matrix-core rates and a read-only HBM
+ * stream (libmmq_peak.so).
  *
  * A measurement aid for the benchmark's roofline, separate from the matmul
  * library: it runs the two 32x32 MFMA instructions a q8 matmul on gfx950 can
@@ -24,6 +25,7 @@
 #define MMQ_PEAK_H
 
 #include <hip/hip_runtime_api.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -32,6 +34,14 @@ extern "C" {
 int mmq_peak_chains(void);
 int mmq_peak_mfma_f16(float* out, int blocks, int iters, hipStream_t stream);
 int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t stream);
+
+/* Read-only HBM stream: reads `bytes` (a multiple of 16, > 0) of the device
+ * buffer `src` once with 16-byte non-temporal loads, `blocks` workgroups of
+ * 256 threads walking it grid-stride, and writes one folded value per thread
+ * to `out` (blocks * 256 uint32, caller-owned).  Time it with events on
+ * `stream`.  Returns 0, -1 for an invalid argument (nothing launched), or the
+ * HIP error code of the launch. */
+int mmq_peak_read(const void* src, int64_t bytes, unsigned* out, int blocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }
