@@ -355,3 +355,40 @@ def test_binding_checks_the_raw_buffer_size(ctx):
         mmq.mmq_register_weight(ctx, mmq.MMQ_Q4_K, 4, 256, np.zeros(144 * 3, np.uint8))
     w = mmq.mmq_register_weight(ctx, mmq.MMQ_Q6_K, 2, 512, bytes(2 * 2 * 210))
     mmq.mmq_weight_free(w)
+
+
+def test_size_limits_of_the_32_bit_buffer_offsets(ctx):
+    """The matmul addresses its tiles and the plane with 32-bit buffer offsets,
+    so registration refuses matmul tiles of 4 GiB or more and a matmul call
+    refuses a plane of 2 GiB or more, both with MMQ_E_SHAPE and a message that
+    says how to split; nothing is launched and no plane is recorded."""
+    out = ctypes.c_void_p()
+    # 2^20 x 2048 q4_K: f16 tiles of exactly 4 GiB (the raw buffer is never
+    # read: the shape is refused first, so a dummy address stands in for it)
+    rc = _lib.lib.mmq_register_weight(ctx, mmq.MMQ_Q4_K, 1 << 20, 2048, ctypes.c_void_p(0x1000),
+                                      mmq.MMQ_USE_GEMM, ctypes.byref(out))
+    assert rc == mmq.MMQ_E_SHAPE and "4 GiB" in _lib.last_error()
+    assert out.value is None
+    # one row fewer than a 128-row tile group below the limit is accepted
+    rc = _lib.lib.mmq_register_weight(ctx, mmq.MMQ_Q4_K, (1 << 20) - 128, 2048,
+                                      ctypes.c_void_p(0x1000), mmq.MMQ_USE_GEMM, ctypes.byref(out))
+    assert rc == mmq.MMQ_OK
+    big = out.value
+    # GEMV-only registration has no matmul tiles and no such limit
+    rc = _lib.lib.mmq_register_weight(ctx, mmq.MMQ_Q6_K, 1 << 20, 2048, ctypes.c_void_p(0x1000),
+                                      mmq.MMQ_USE_GEMV, ctypes.byref(out))
+    assert rc == mmq.MMQ_OK
+    mmq.mmq_weight_free(out.value)
+    w = _w(ctx, mmq.MMQ_Q4_K, 128, 2048)
+    st0 = mmq.mmq_stats(ctx)
+    n = (1 << 31) // 2048             # plane of exactly 2 GiB of codes
+    assert _status(mmq.mmq_gemm_q4k, ctx, w, 0x10000000, n, 0x20000000) == mmq.MMQ_E_SHAPE
+    assert "2 GiB" in _lib.last_error()
+    st1 = mmq.mmq_stats(ctx)
+    assert st1["launches_gemm_q4k"] == st0["launches_gemm_q4k"]
+    assert st1["launches_quant_f32"] == st0["launches_quant_f32"]
+    assert st1["cache_entries"] == st0["cache_entries"]
+    # 32 tokens fewer (the plane's row padding) fits
+    assert _status(mmq.mmq_gemm_q4k, ctx, w, 0x10000000, n - 32, 0x20000000) == mmq.MMQ_OK
+    mmq.mmq_weight_free(w)
+    mmq.mmq_weight_free(big)
