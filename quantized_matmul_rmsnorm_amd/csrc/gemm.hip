@@ -26,8 +26,9 @@
 // for every output of every block -- three VALU ops against the one here, and
 // the VALU, not the matrix core, is what bounds this kernel.
 // Per superblock the sum over its 8 blocks is scaled by d (one FMA per output);
-// the q4_K min term sum_j (D*S)[t][j] * m_j is one extra MFMA per superblock
-// with m_j exact in f16 and D*S split into two f16 parts (22 significant bits).
+// the q4_K min term sum_j (D*S)[t][j] * m_j is two bf16 MFMAs per superblock
+// with m_j exact in bf16 and D*S split exactly into three bf16 parts (bf16
+// has f32's exponent range, so no activation scale overflows or underflows).
 //
 // Tiling.  A workgroup of 8 waves computes 128 outputs x 128 tokens; wave w
 // owns output group w%4 (32 rows) and token groups 2*(w/4), 2*(w/4)+1.  Each
@@ -56,6 +57,11 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 bits of x, rounded to nearest even, and the value of such bits
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float bf16_value(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 constexpr int kThreads = 512;
 constexpr int kGroupO = 4;     // output tiles per raster group
@@ -157,7 +163,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     static_assert(kBarAt < CH - 1, "the next chunk's first read must follow the barrier");
     __shared__ half8 sB[NBUF][CH][4 * 2 * 64 + BPAD];
     __shared__ float sD[NBUF][CH][128 + DPAD];
-    __shared__ __attribute__((aligned(16))) _Float16 sP[Q4K ? 3 : 1][4][64][8];
+    // q4_K min term: D*S per (token, block) as three bf16 parts, B fragments of
+    // two MFMAs: [hi | mid] and [lo | 0] over the superblock's 8 blocks
+    __shared__ __attribute__((aligned(16))) uint16_t sP[Q4K ? 3 : 1][4][2][64][8];
     __shared__ __attribute__((aligned(16))) float sDM[2][kThreads];
 
     const int tid = threadIdx.x;
@@ -229,12 +237,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
         const int b = c * CH + jb;
         sD[buf][jb][tb] = rd;
         if (Q4K) {
+            // P = hi + mid + lo exactly (three 8-bit significands hold the
+            // 24 of an f32, and bf16 keeps f32's exponent range)
             const float P = rd * (float)rs;
-            const _Float16 hi = (_Float16)P;
-            const _Float16 lo = (_Float16)(P - (float)hi);
+            const uint16_t hi = bf16_bits(P);
+            const float r1 = P - bf16_value(hi);
+            const uint16_t mid = bf16_bits(r1);
+            const uint16_t lo = bf16_bits(r1 - bf16_value(mid));
             const int slot = real ? ((b >> 3) & 1) : 2;
-            sP[slot][tg][tl][b & 7] = hi;
-            sP[slot][tg][tl + 32][b & 7] = lo;
+            sP[slot][tg][0][tl][b & 7] = hi;
+            sP[slot][tg][0][tl + 32][b & 7] = mid;
+            sP[slot][tg][1][tl][b & 7] = lo;
         }
         if (first) sDM[(c / SBCH) & 1][tid] = rdm;
     };
@@ -267,6 +280,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
         load_sc(sb0, scv);
         load_sc(min(sb0 + 1, sb1 - 1), scn);
     }
+    if (Q4K) {   // the zero half of the [lo | 0] fragments, never written again
+        for (int e = tid; e < 3 * 4 * 32 * 8; e += kThreads)
+            sP[e >> 10][(e >> 8) & 3][1][32 + ((e >> 3) & 31)][e & 7] = 0;
+    }
     load_chunk(c0, true);
     store_chunk(c0, 0, true, true);
     load_chunk(c0 + 1, false);
@@ -294,9 +311,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
             // stage chunk c+1 (loaded one chunk ago), load chunk c+2
             store_chunk(min(c + 1, c_end - 1), bnext, (cc + 1) % SBCH == 0, c + 1 < c_end);
             load_chunk(min(c + 2, c_end - 1), cc % SBCH == 0);
-            half8 mf;
+            bf16x8 mf;
             if (Q4K && cc == SBCH - 1)
-                mf = bload<half8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
+                mf = bload<bf16x8>(rF, (uint32_t)((((og0 + ogl) * nsb + sb) * 64 + lane) * 16), 0u);
             f32x16 X[2][2];
             auto mfma_block = [&](int j, int slot, half8 (*bf)[2], f32x16* Xo) {
                 if constexpr (Q4K) {
@@ -383,9 +400,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
                 if (Q4K) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
-                        const half8 pf = *reinterpret_cast<const half8*>(&sP[sb & 1][2 * th + i][lane][0]);
+                        const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(&sP[sb & 1][2 * th + i][0][lane][0]);
+                        const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(&sP[sb & 1][2 * th + i][1][lane][0]);
                         const f32x16 zero = {};
-                        const f32x16 mn = __builtin_amdgcn_mfma_f32_32x32x16_f16(mf, pf, zero, 0, 0, 0);
+                        f32x16 mn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mf, p0, zero, 0, 0, 0);
+                        mn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mf, p1, mn, 0, 0, 0);
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const float v = fmaf(dmv[r], acc[i][r], res[i][r]);

@@ -21,7 +21,7 @@
 //   q4_K: wa[og][k16][lane][e] = f16(sc_j * q)        (exact: <= 63*15 = 945)
 //         dmr[og][sb][{d,dmin}][half][r] f32, r/half as the MFMA output row
 //             of ol: ol = 8*(r/4) + 4*half + r%4
-//         mfrag[og][sb][lane][j] = f16(m_j) for both lane halves (exact)
+//         mfrag[og][sb][lane][j] = bf16(m_j) for both lane halves (exact)
 //   q6_K: wa[og][k16][lane][e] = f16(q - 32)     (exact; the matmul forms
 //             sc * (q - 32), 13 bits, as two exact f16 parts in registers)
 //         mfrag[og][sb][ol][i] = f16(sc_i), i = 0..15 (exact)
@@ -114,10 +114,12 @@ __global__ void k_repack_q4k_gemm(const uint8_t* __restrict__ raw, int64_t rows,
     float* dm = dmr + (og * nsb + sb) * 64;
     dm[half * 16 + r] = d;
     dm[32 + half * 16 + r] = dmin;
-    _Float16* mf = mfrag + (og * nsb + sb) * 512;
+    // mins as bf16 bits (exact: at most 6 significant bits)
+    uint16_t* mf = reinterpret_cast<uint16_t*>(mfrag) + (og * nsb + sb) * 512;
     for (int j = 0; j < 8; ++j) {
-        mf[ol * 8 + j] = (_Float16)(float)mn[j];
-        mf[(ol + 32) * 8 + j] = (_Float16)(float)mn[j];
+        const uint16_t bits = (uint16_t)(__float_as_uint((float)mn[j]) >> 16);
+        mf[ol * 8 + j] = bits;
+        mf[(ol + 32) * 8 + j] = bits;
     }
 }
 

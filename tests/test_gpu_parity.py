@@ -168,6 +168,43 @@ def test_gemm_parity(ctx, wtype, n, od, id_):
     mmq.mmq_weight_free(w)
 
 
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+def test_gemm_degenerate_activation_rows(ctx, wtype):
+    """Rows the plane encodes at its edges: all zero (D = 0, S = 0), one
+    nonzero block among zero blocks, one nonzero value per block, and row
+    scales from 1e-20 to 1e20; n = 40 (a ragged token tile), od = 200."""
+    n, od, id_ = 40, 200, 1024
+    rng = synth.rng_for("test", n, f"degen{wtype}")
+    y = synth.activations(rng, n, id_)
+    y[0] = 0.0
+    y[1] = 0.0
+    y[1, 256:288] = y[2, 256:288]
+    y[3] = 0.0
+    y[3, ::32] = np.linspace(-5.0, 5.0, id_ // 32, dtype=np.float32)
+    y[4] *= np.float32(1e20)
+    y[5] *= np.float32(1e-20)
+    y[6, :512] = 0.0
+    y = np.ascontiguousarray(y, np.float32)
+    raw = synth.weights(wtype, synth.rng_for("test", od, f"degenw{wtype}"), od, id_)
+    w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw, mmq.MMQ_USE_GEMM)
+    a = dev_tensor(y)
+    out = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
+    (mmq.mmq_gemm_q4k if wtype == "q4_K" else mmq.mmq_gemm_q6k)(ctx, w, a, n, out)
+    torch.cuda.synchronize()
+    q, D, S = export_plane(ctx, a, n, id_)
+    assert_plane_equal((q, D, S), oracle.quantize(y), "degenerate rows plane")
+    got = out.cpu().numpy()
+    assert not got[0].any() and np.isfinite(got).all()
+    ref = oracle.gemm(wtype, q, D, S, raw, od, id_)
+    # rows 4 and 5 are checked relative to their own scale
+    for t in (4, 5):
+        sc = np.abs(ref[t]).max()
+        assert np.abs(got[t] - ref[t]).max() <= 1e-3 * sc, t
+    keep = [t for t in range(n) if t not in (4, 5)]
+    assert_gemm_close(got[keep], ref[keep], f"degenerate rows {wtype}")
+    mmq.mmq_weight_free(w)
+
+
 @pytest.mark.parametrize("wtype,n,od,id_", [("q4_K", 2, 1000, 5120), ("q6_K", 3, 300, 13824),
                                             ("q4_K", 5, 13824, 5120), ("q6_K", 8, 3584, 18944),
                                             ("q6_K", 4, 3584, 18944),
