@@ -70,7 +70,10 @@ def test_quant_f32_special_values(ctx):
     assert_plane_equal(export_plane(ctx, x, n, d), oracle.quantize(y), "special values")
 
 
-@pytest.mark.parametrize("n,d", [(37, 512), (128, 3584), (1, 5120), (3314, 3584)])
+# d 8192 and 16384 fill the 8- and 16-round register forms; 16640 and 18944
+# re-read x for the second pass
+@pytest.mark.parametrize("n,d", [(37, 512), (128, 3584), (1, 5120), (3314, 3584), (2, 8192),
+                                 (3, 16384), (2, 16640), (2, 18944)])
 def test_quant_rms_fused_and_cross_mode(ctx, n, d):
     rng = synth.rng_for("test", n, f"rms{d}")
     xh = synth.activations(rng, n, d)
@@ -312,6 +315,42 @@ def test_mmvq_q4k_parity(ctx, od, id_):
     q, D, S = export_plane(ctx, a, 1, id_)
     ref = oracle.gemm("q4_K", q, D, S, raw, od, id_)[0]
     assert_gemm_close(out.cpu().numpy(), ref, f"mmvq q4_K {od}x{id_}")
+    mmq.mmq_weight_free(w)
+
+
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("n", [1, 3])
+def test_gemv_degenerate_activation_rows(ctx, wtype, n):
+    """The one-token GEMV (n = 1) and the few-token GEMV (n = 3) on rows with
+    zero blocks, a block scaled by 1e20 and one by 1e-20, and (n = 3) an
+    all-zero row: outputs finite and within 1e-3 of the oracle relative to
+    each row's largest output."""
+    od, id_ = 300, 5120
+    y = synth.activations(synth.rng_for("test", n, f"gvdegen{wtype}"), n, id_)
+    y[0, :1024] = 0.0
+    y[0, 1024:1056] *= np.float32(1e20)
+    y[0, 2048:2080] *= np.float32(1e-20)
+    if n > 1:
+        y[1] = 0.0
+    y = np.ascontiguousarray(y, np.float32)
+    raw = synth.weights(wtype, synth.rng_for("test", od, f"gvdegenw{wtype}"), od, id_)
+    w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw, mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV)
+    a = dev_tensor(y)
+    out = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
+    before = mmq.mmq_stats(ctx)["small_n_gemv"]
+    (mmq.mmq_gemm_q4k if wtype == "q4_K" else mmq.mmq_gemm_q6k)(ctx, w, a, n, out)
+    torch.cuda.synchronize()
+    assert mmq.mmq_stats(ctx)["small_n_gemv"] == before + 1   # the GEMV path ran
+    q, D, S = export_plane(ctx, a, n, id_)
+    assert_plane_equal((q, D, S), oracle.quantize(y), "degenerate rows plane")
+    got = out.cpu().numpy()
+    ref = oracle.gemm(wtype, q, D, S, raw, od, id_)
+    assert np.isfinite(got).all()
+    for t in range(n):
+        sc = max(np.abs(ref[t]).max(), 1.0)
+        assert np.abs(got[t] - ref[t]).max() <= 1e-3 * sc, t
+    if n > 1:
+        assert not got[1].any()
     mmq.mmq_weight_free(w)
 
 
