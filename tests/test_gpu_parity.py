@@ -561,3 +561,45 @@ def test_auto_without_plane_memory_writes_y_only(kind):
         assert st["unfused_fallbacks"] == 1 and st["cache_entries"] == 0 and st["plane_bytes"] == 0
     finally:
         mmq.mmq_destroy(c)
+
+
+def test_side_stream_matches_default_stream(ctx):
+    """Every launch goes on the caller's stream: a producer -> matmul chain
+    (with a K split and the GEMV path) run on a side stream, with its inputs
+    written on that stream just before, equals the same chain on the default
+    stream bit for bit."""
+    n, d, od = 70, 1024, 512
+    xh = synth.activations(synth.rng_for("test", n, "side_x"), n, d)
+    wn = synth.rms_weight(synth.rng_for("test", n, "side_w"), d)
+    raw4 = synth.weights("q4_K", synth.rng_for("test", od, "side4"), od, d)
+    raw6 = synth.weights("q6_K", synth.rng_for("test", od, "side6"), od, d)
+    w4 = mmq.mmq_register_weight(ctx, WT["q4_K"], od, d, raw4, mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV)
+    w6 = mmq.mmq_register_weight(ctx, WT["q6_K"], od, d, raw6, mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV)
+    xs = torch.from_numpy(xh).cuda()
+    wt = torch.from_numpy(wn).cuda()
+
+    def chain(x):
+        y = torch.empty((n, d), dtype=torch.float32, device="cuda")
+        o4 = torch.empty((n, od), dtype=torch.float32, device="cuda")
+        o6 = torch.empty((n, od), dtype=torch.float32, device="cuda")
+        o1 = torch.empty((1, od), dtype=torch.float32, device="cuda")
+        mmq.mmq_quant_rms(ctx, x, wt, y, n, d, 1e-6, 0)
+        mmq.mmq_gemm_q4k(ctx, w4, y, n, o4)
+        mmq.mmq_gemm_q6k(ctx, w6, y, n, o6)
+        mmq.mmq_gemm_q6k(ctx, w6, x[:1], 1, o1)       # one token: the GEMV path
+        return o4, o6, o1
+
+    ref = [t.clone() for t in chain(xs)]
+    torch.cuda.synchronize()
+    mmq.mmq_cache_clear(ctx)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        x2 = torch.empty_like(xs)
+        x2.copy_(xs)                                   # written on the side stream
+        got = chain(x2)
+    side.synchronize()
+    mmq.mmq_cache_clear(ctx)
+    for r, g_ in zip(ref, got):
+        assert torch.equal(r, g_)
+    mmq.mmq_weight_free(w4)
+    mmq.mmq_weight_free(w6)
