@@ -260,7 +260,10 @@ hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, in
     const int rps = (rounds + segs - 1) / segs;
     segs = (rounds + rps - 1) / rps;
     const dim3 grid((unsigned)rows, (unsigned)segs), block(256);
-    if (KIND == kProdRms && per_wave <= 8) {
+    if (KIND == kProdRms && per_wave <= 4) {
+        hipLaunchKernelGGL((k_producer<KIND, WY, 4, QUANT>), grid, block, 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
+    } else if (KIND == kProdRms && per_wave <= 8) {
         hipLaunchKernelGGL((k_producer<KIND, WY, 8, QUANT>), grid, block, 0, s, a, b, y, (int)n,
                            (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
     } else if (KIND == kProdRms && per_wave <= 16) {
