@@ -10,21 +10,20 @@
 //
 // How it maps onto CDNA4.  The integer dots run on v_mfma_f32_32x32x16_f16 with
 // integer-valued f16 operands: the activation codes (|q| <= 127) and the
-// weight values -- for q4_K sc_j*q_w (<= 945), folded at registration; for
-// q6_K v = sc*(q_w-32) (|v| <= 4096, 13 bits), formed by each wave from the
-// stored code q_w-32 and its f16 sub-scale as hi = f16(v) and lo = v - hi
-// (one packed multiply and one packed fma per pair; |lo| <= 1) -- are exact
+// weight values.  For q4_K the weight value sc_j*q_w (<= 945) is folded at
+// registration.  For q6_K, v = sc*(q_w-32) needs 13 bits (|v| <= 4096), so
+// each wave forms it from the stored code q_w-32 and its f16 sub-scale as two
+// exact f16 parts, hi = f16(v) and lo = v - hi (|lo| <= 1), with one packed
+// multiply and one packed fma per pair; streaming the code rather than the two
+// parts halves the bytes each wave loads per weight.  All operands are exact
 // in f16, every product is exact in f32 and every partial sum of one block
 // stays below 2^24, so the MFMA returns the exact integer block dot as an f32.
-// (Streaming the q6_K code instead of the two parts halves the bytes each
-// wave loads per weight, and the vector-memory return path is what this
-// kernel's q6_K arm waits on.)  Folding the
-// weight's sub-scale into the operand leaves one FMA per output per block
-// (acc += D[t][b] * X) with D constant per lane, because tokens sit on the
-// MFMA's N axis (lane % 32) and outputs on its M axis (registers).  An int8
-// MFMA would return int32 and need a convert, a sub-scale multiply and the FMA
-// for every output of every block -- three VALU ops against the one here, and
-// the VALU, not the matrix core, is what bounds this kernel.
+// With the sub-scale inside the operand, the rescale is one FMA per output
+// per block (acc += D[t][b] * X), D constant per lane because tokens sit on
+// the MFMA's N axis (lane % 32) and outputs on its M axis (registers).  An
+// int8 MFMA would return int32 and need a convert, a sub-scale multiply and
+// the FMA for every output of every block: three VALU ops against one, on the
+// busier of the two arithmetic pipes here.
 // Per superblock the sum over its 8 blocks is scaled by d (one FMA per output);
 // the q4_K min term sum_j (D*S)[t][j] * m_j is two bf16 MFMAs per superblock
 // with m_j exact in bf16 and D*S split exactly into three bf16 parts (bf16
@@ -135,7 +134,7 @@ __device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint
 struct GemmArgs {
     const half8* wa;      // weight fragments
     const float* dmr;     // per (row group, superblock) scales
-    const half8* mfrag;   // q4_K mins
+    const half8* mfrag;   // q4_K mins (bf16) or q6_K sub-scales (f16)
     const int8_t* q;      // plane codes [plane_rows][id]
     const float* D;       // plane scales [plane_rows][id/32]
     const int32_t* S;     // plane sums  [plane_rows][id/32]
@@ -148,8 +147,7 @@ struct GemmArgs {
     int compact;          // 1: partials go to part[split][tile][128][128]
 };
 
-// The matmul kernel.  RA: depth of the weight-fragment register ring (the
-// prefetch distance is RA-1 blocks).
+// The matmul kernel (Q4K: q4_K weights, else q6_K).
 template <bool Q4K>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     constexpr int CH = 4;                   // 32-blocks per staged activation chunk
