@@ -236,7 +236,9 @@ int mmq_cache_invalidate(mmq_ctx* ctx, const void* key);
 /* Copy the plane recorded under (key, n, d) into caller device buffers in
  * the canonical row-major layout: q int8 [r][d], dq f32 [r][d/32],
  * s int32 [r][d/32], with r = n, or mmq_plane_rows(n) if include_pad.
- * Errors: MMQ_E_ARG (no such plane), MMQ_E_HIP, MMQ_E_DEVICE (dry run). */
+ * dq and s must be 4-byte aligned.
+ * Errors: MMQ_E_ARG (no such plane, null or misaligned buffer), MMQ_E_HIP,
+ * MMQ_E_DEVICE (dry run). */
 int mmq_plane_export(mmq_ctx* ctx, const void* key, int64_t n, int64_t d,
                      int include_pad, int8_t* q, float* dq, int32_t* s,
                      void* stream);

@@ -136,8 +136,7 @@ struct GemmArgs {
     const float* dmr;     // per (row group, superblock) scales
     const half8* mfrag;   // q4_K mins (bf16) or q6_K sub-scales (f16)
     const int8_t* q;      // plane codes [plane_rows][id]
-    const float* D;       // plane scales [plane_rows][id/32]
-    const int32_t* S;     // plane sums  [plane_rows][id/32]
+    const uint2* ds;      // plane (D, S) pairs [plane_rows][id/32]
     float* out;           // [n][od]
     uint32_t wa_bytes, dmr_bytes, mfrag_bytes, q_bytes, ds_bytes;
     int n, plane_rows, id, od, n_ttiles, n_otiles;
@@ -155,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     constexpr int NDM = Q4K ? 2 : 1;
     constexpr int RA = 4;                   // weight-fragment ring depth (divides 8)
     constexpr int PD = RA - 1;              // prefetch distance in blocks
-    constexpr int BPAD = 4, DPAD = 16;
+    constexpr int BPAD = 2, DPAD = 16;
     constexpr int NBUF = 3;
     constexpr int kBarAt = 1;               // the chunk step's barrier follows block 1
     static_assert(kBarAt < CH - 1, "the next chunk's first read must follow the barrier");
@@ -183,8 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
 
     const auto rA = rsrc(g.wa, g.wa_bytes);
     const auto rQ = rsrc(g.q, g.q_bytes);
-    const auto rD = rsrc(g.D, g.ds_bytes);
-    const auto rS = rsrc(g.S, g.ds_bytes);
+    const auto rDS = rsrc(g.ds, g.ds_bytes);
     const auto rM = rsrc(g.dmr, g.dmr_bytes);
     const auto rF = rsrc(g.mfrag, g.mfrag_bytes);
 
@@ -201,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     const int jb = tid & 3;
     const int rowb = t0 + tb;
     const uint32_t rowq = rowb < g.plane_rows ? (uint32_t)rowb * (uint32_t)id : 0x80000000u;
-    const uint32_t rowd = rowb < g.plane_rows ? (uint32_t)(rowb * nb + jb) * 4u : 0x80000000u;
+    const uint32_t rowd = rowb < g.plane_rows ? (uint32_t)(rowb * nb + jb) * 8u : 0x80000000u;
     // superblock scales: thread tid stages entry tid % DMN (threads past DMN
     // duplicate an entry into a spare half of sDM, so every thread stores)
     constexpr int DMN = 4 * NDM * 32;
@@ -219,8 +217,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
         const uint32_t sq = (uint32_t)(c * CH) * 32u;
         rb0 = bload<uint4>(rQ, rowq + (uint32_t)jb * 32u, sq);
         rb1 = bload<uint4>(rQ, rowq + (uint32_t)jb * 32u + 16u, sq);
-        rd = bload<float>(rD, rowd, (uint32_t)(c * CH) * 4u);
-        rs = Q4K ? bload<int32_t>(rS, rowd, (uint32_t)(c * CH) * 4u) : 0;
+        if constexpr (Q4K) {   // D and S in one load
+            const uint2 v = bload<uint2>(rDS, rowd, (uint32_t)(c * CH) * 8u);
+            rd = __uint_as_float(v.x);
+            rs = (int32_t)v.y;
+        } else {
+            rd = bload<float>(rDS, rowd, (uint32_t)(c * CH) * 8u);
+            rs = 0;
+        }
         if (first) rdm = bload<float>(rM, dm_off, (uint32_t)((c / SBCH) * (NDM * 32 * 4)));
     };
     // real == false: a clamped repeat of the last chunk; its min-term operands
@@ -577,14 +581,13 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.dmr = w.dmr;
     a.mfrag = (const half8*)w.mfrag;
     a.q = pl.q;
-    a.D = pl.D;
-    a.S = pl.S;
+    a.ds = pl.ds;
     const int64_t nsb = w.cols / kSuper, og = w.rows_pad / 32;
     a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * 2);
     a.dmr_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 64 : 32) * 4);
     a.mfrag_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 512 * 2 : 32 * 16 * 2));
     a.q_bytes = (uint32_t)(pl.rows * pl.d);
-    a.ds_bytes = (uint32_t)(pl.rows * (pl.d / kBlock) * 4);
+    a.ds_bytes = (uint32_t)(pl.rows * (pl.d / kBlock) * 8);
     a.n = (int)n;
     a.plane_rows = (int)pl.rows;
     a.id = (int)w.cols;

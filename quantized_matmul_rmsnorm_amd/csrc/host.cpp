@@ -64,14 +64,12 @@ struct DeadRange {
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-int64_t plane_bytes_for(int64_t n, int64_t d, int64_t* off_D, int64_t* off_S) {
+int64_t plane_bytes_for(int64_t n, int64_t d, int64_t* off_ds) {
     const int64_t rows = round_up(n, kPlaneRows);
     const int64_t nb = d / kBlock;
-    const int64_t oD = round_up(rows * d, 256);
-    const int64_t oS = oD + round_up(rows * nb * 4, 256);
-    if (off_D) *off_D = oD;
-    if (off_S) *off_S = oS;
-    return oS + round_up(rows * nb * 4, 256);
+    const int64_t o = round_up(rows * d, 256);
+    if (off_ds) *off_ds = o;
+    return o + round_up(rows * nb * 8, 256);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -211,7 +209,7 @@ int acquire_slot(mmq_ctx* c, const void* key, int64_t n, int64_t d, bool in_capt
                 if (c->entries[i].last < c->entries[idx].last) idx = i;
         }
     }
-    const int64_t need = plane_bytes_for(n, d, nullptr, nullptr);
+    const int64_t need = plane_bytes_for(n, d, nullptr);
     Slot& s = c->slots[idx];
     if (s.cap < need) {
         if (in_capture)
@@ -263,13 +261,12 @@ void commit_entry(mmq_ctx* c, int idx, const void* key, int64_t n, int64_t d, bo
 
 PlaneView view_of(const mmq_ctx* c, int idx) {
     const Entry& e = c->entries[idx];
-    int64_t oD, oS;
-    plane_bytes_for(e.n, e.d, &oD, &oS);
+    int64_t o;
+    plane_bytes_for(e.n, e.d, &o);
     char* base = (char*)c->slots[idx].mem;
     PlaneView v;
     v.q = (int8_t*)base;
-    v.D = (float*)(base + oD);
-    v.S = (int32_t*)(base + oS);
+    v.ds = (uint2*)(base + o);
     v.rows = round_up(e.n, kPlaneRows);
     v.d = e.d;
     return v;
@@ -721,6 +718,8 @@ int mmq_plane_export(mmq_ctx* c, const void* key, int64_t n, int64_t d, int incl
                      int8_t* q, float* dq, int32_t* s, void* stream) {
     const char* who = "mmq_plane_export";
     if (!c || !q || !dq || !s) return fail(MMQ_E_ARG, "%s: null argument", who);
+    if ((((uintptr_t)dq) | ((uintptr_t)s)) & 3u)
+        return fail(MMQ_E_ARG, "%s: dq and s must be 4-byte aligned", who);
     const int idx = find_entry(c, key, n, d);
     if (idx < 0) return fail(MMQ_E_ARG, "%s: no plane recorded for (%p, %lld, %lld)", who, key,
                              (long long)n, (long long)d);
@@ -732,10 +731,7 @@ int mmq_plane_export(mmq_ctx* c, const void* key, int64_t n, int64_t d, int incl
     const int64_t nb = d / kBlock;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(q, pl.q, (size_t)(rows * d), hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(dq, pl.D, (size_t)(rows * nb * 4), hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(s, pl.S, (size_t)(rows * nb * 4), hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = launch_plane_split(pl.ds, dq, s, rows * nb, st);
     return after_launch(c, e, st, who);
 }
 

@@ -8,16 +8,16 @@
 
 namespace mmq {
 
-// Plane of n tokens x d values: rows padded to kPlaneRows, three arrays in one
-// allocation: q int8 [rows][d], D f32 [rows][d/32], S int32 [rows][d/32].
+// Plane of n tokens x d values: rows padded to kPlaneRows, two arrays in one
+// allocation: q int8 [rows][d] and ds [rows][d/32] of (D f32 bits, S int32)
+// pairs, so that one 8-byte load fetches a block's scale and code sum.
 constexpr int kPlaneRows = 32;
 constexpr int kBlock = 32;     // activation block (one f32 scale, one int sum)
 constexpr int kSuper = 256;    // K-quant superblock
 
 struct PlaneView {
     int8_t* q;
-    float* D;
-    int32_t* S;
+    uint2* ds;      // .x = D (f32 bits), .y = S
     int64_t rows;   // padded row count
     int64_t d;
 };
@@ -50,6 +50,9 @@ enum ProducerKind { kProdRms = 0, kProdSwiglu = 1, kProdF32 = 2 };
 hipError_t launch_producer(ProducerKind kind, const float* a, const float* b, float* y,
                            int64_t n, int64_t d, float eps, bool write_y,
                            const PlaneView& pl, hipStream_t s);
+// Plane scales and sums into separate arrays (count blocks), for export.
+hipError_t launch_plane_split(const uint2* ds, float* D, int32_t* S, int64_t count,
+                              hipStream_t s);
 
 // ---- registration repack (repack.hip): raw superblocks already on device ----
 hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s);

@@ -56,8 +56,7 @@ struct MvArgs {
     const int16_t* sc;    // [od][nb] scales
     const float* dv;      // q6_K: [od][nsb] d; q4_K: [od][nsb][2] d, dmin
     const int8_t* Q;      // plane codes (row 0)
-    const float* Dp;      // plane scales
-    const int32_t* Sp;    // plane sums
+    const uint2* ds;      // plane (D, S) pairs
     int id, od;
     float* out;
 };
@@ -80,7 +79,7 @@ struct Q6 {
         const uint4* p = reinterpret_cast<const uint4*>(g.Q + (int64_t)b * kBlock);
         a.q0 = p[0];
         a.q1 = p[1];
-        a.D = g.Dp[b];
+        a.D = __uint_as_float(g.ds[b].x);
         const uint32_t ones = 0x01010101u;
         int s0 = dot4(a.q0.x, ones, 0); s0 = dot4(a.q0.y, ones, s0);
         s0 = dot4(a.q0.z, ones, s0);    s0 = dot4(a.q0.w, ones, s0);
@@ -137,8 +136,9 @@ struct Q4 {
         const uint4* p = reinterpret_cast<const uint4*>(g.Q + (int64_t)b * kBlock);
         a.q0 = p[0];
         a.q1 = p[1];
-        a.D = g.Dp[b];
-        a.S = g.Sp[b];
+        const uint2 v = g.ds[b];
+        a.D = __uint_as_float(v.x);
+        a.S = (int)v.y;
         return a;
     }
     static __device__ __forceinline__ W load(const MvArgs& g, int64_t o, int b, int nb, int nsb) {
@@ -305,7 +305,8 @@ __global__ __launch_bounds__(512) void k_mmvqn(const MvArgs g, int n, int t0) {
             const uint4* p = reinterpret_cast<const uint4*>(qrow + (int64_t)b * kBlock);
             r.q0 = p[0];
             r.q1 = p[1];
-            r.D = g.Dp[(int64_t)(t0 + t) * nb + b];
+            const uint2 v = g.ds[(int64_t)(t0 + t) * nb + b];
+            r.D = __uint_as_float(v.x);
             if constexpr (sizeof(typename F::Act) == sizeof(Q6::Act) &&
                           __is_same(F, Q6)) {
                 const uint32_t ones = 0x01010101u;
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(512) void k_mmvqn(const MvArgs g, int n, int t0) {
                 s1 = dot4(r.q1.z, ones, s1);    s1 = dot4(r.q1.w, ones, s1);
                 r.aux = (int)((uint32_t)(s0 & 0xFFFF) | ((uint32_t)s1 << 16));
             } else {
-                r.aux = g.Sp[(int64_t)(t0 + t) * nb + b];
+                r.aux = (int)v.y;
             }
         } else {
             r.q0 = make_uint4(0, 0, 0, 0);
@@ -393,8 +394,7 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     g.sc = w.gv_sc;
     g.dv = w.gv_d;
     g.Q = pl.q;
-    g.Dp = pl.D;
-    g.Sp = pl.S;
+    g.ds = pl.ds;
     g.id = (int)w.cols;
     g.od = (int)w.rows;
     g.out = out;
@@ -446,8 +446,7 @@ hipError_t launch_mmvqn(const WeightDev& w, const PlaneView& pl, int64_t n, floa
     g.sc = w.gv_sc;
     g.dv = w.gv_d;
     g.Q = pl.q;
-    g.Dp = pl.D;
-    g.Sp = pl.S;
+    g.ds = pl.ds;
     g.id = (int)w.cols;
     g.od = (int)w.rows;
     g.out = out;

@@ -83,9 +83,9 @@ __device__ __forceinline__ int code(float v, float dsc, float rcp) {
 }
 
 // Quantise the 4 values of this lane; lanes 8g..8g+7 form one 32-block.
-// Writes the 4 codes as one dword and, from the group's first lane, D and S.
-__device__ __forceinline__ void quant4(float4 v, int lane, uint32_t* qdst, float* Ddst,
-                                       int32_t* Sdst) {
+// Writes the 4 codes as one dword and, from the group's first lane, the
+// block's (D, S) pair as one 8-byte store.
+__device__ __forceinline__ void quant4(float4 v, int lane, uint32_t* qdst, uint2* dsdst) {
     float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     am = max8(am);
     const float dsc = am / 127.0f;
@@ -98,10 +98,7 @@ __device__ __forceinline__ void quant4(float4 v, int lane, uint32_t* qdst, float
     *qdst = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
             ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
     const int s = sum8((q0 + q1) + (q2 + q3));
-    if ((lane & 7) == 0) {
-        *Ddst = dsc;
-        *Sdst = s;
-    }
+    if ((lane & 7) == 0) *dsdst = make_uint2(__float_as_uint(dsc), (uint32_t)s);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -117,8 +114,7 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
                                                   const float* __restrict__ b,
                                                   float* __restrict__ y, int n, int d,
                                                   float eps, int8_t* __restrict__ q,
-                                                  float* __restrict__ D,
-                                                  int32_t* __restrict__ S, int rows,
+                                                  uint2* __restrict__ ds, int rows,
                                                   int rps) {
     constexpr int W = 4;   // waves per row segment
     constexpr int U = 8;   // rounds of one wave whose loads are in flight together
@@ -132,18 +128,14 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
     const int rcount = min(rps, d / kSuper - r0);
     const int my = (rcount - wave + W - 1) / W;   // rounds of this wave: r0 + wave + W*k, k < my
     uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (int64_t)row * d) + 64 * r0;
-    float* Dr = D + (int64_t)row * nb + 8 * r0;
-    int32_t* Sr = S + (int64_t)row * nb + 8 * r0;
+    uint2* dsr = ds + (int64_t)row * nb + 8 * r0;
     const int g = lane >> 3;
 
     if (QUANT && row >= n) {  // padded tail rows: deterministic zeros
         for (int k = 0; k < my; ++k) {
             const int r = wave + W * k;
             q4[64 * r + lane] = 0u;
-            if ((lane & 7) == 0) {
-                Dr[8 * r + g] = 0.0f;
-                Sr[8 * r + g] = 0;
-            }
+            if ((lane & 7) == 0) dsr[8 * r + g] = make_uint2(0u, 0u);
         }
         return;  // the whole workgroup takes this branch
     }
@@ -205,7 +197,7 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
             v = xin;
         }
         if constexpr (WRITE_Y) y4[64 * r + lane] = v;
-        if constexpr (QUANT) quant4(v, lane, q4 + 64 * r + lane, Dr + 8 * r + g, Sr + 8 * r + g);
+        if constexpr (QUANT) quant4(v, lane, q4 + 64 * r + lane, dsr + 8 * r + g);
     };
 
     if constexpr (MAXR > 0) {
@@ -262,21 +254,42 @@ hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, in
     const dim3 grid((unsigned)rows, (unsigned)segs), block(256);
     if (KIND == kProdRms && per_wave <= 4) {
         hipLaunchKernelGGL((k_producer<KIND, WY, 4, QUANT>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
+                           (int)d, eps, pl.q, pl.ds, (int)rows, rps);
     } else if (KIND == kProdRms && per_wave <= 8) {
         hipLaunchKernelGGL((k_producer<KIND, WY, 8, QUANT>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
+                           (int)d, eps, pl.q, pl.ds, (int)rows, rps);
     } else if (KIND == kProdRms && per_wave <= 16) {
         hipLaunchKernelGGL((k_producer<KIND, WY, 16, QUANT>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
+                           (int)d, eps, pl.q, pl.ds, (int)rows, rps);
     } else {
         hipLaunchKernelGGL((k_producer<KIND, WY, 0, QUANT>), grid, block, 0, s, a, b, y, (int)n,
-                           (int)d, eps, pl.q, pl.D, pl.S, (int)rows, rps);
+                           (int)d, eps, pl.q, pl.ds, (int)rows, rps);
     }
     return hipGetLastError();
 }
 
+// Export: the (D, S) pairs of `count` blocks into separate arrays.
+__global__ __launch_bounds__(256) void k_plane_split(const uint2* __restrict__ ds,
+                                                     float* __restrict__ D,
+                                                     int32_t* __restrict__ S, int64_t count) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        const uint2 v = ds[i];
+        D[i] = __uint_as_float(v.x);
+        S[i] = (int32_t)v.y;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_plane_split(const uint2* ds, float* D, int32_t* S, int64_t count,
+                              hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    const int64_t want = (count + 255) / 256;
+    const dim3 grid((unsigned)std::min<int64_t>(want, 4096));
+    hipLaunchKernelGGL(k_plane_split, grid, dim3(256), 0, s, ds, D, S, count);
+    return hipGetLastError();
+}
 
 hipError_t launch_producer(ProducerKind kind, const float* a, const float* b, float* y,
                            int64_t n, int64_t d, float eps, bool write_y,
