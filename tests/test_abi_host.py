@@ -241,9 +241,13 @@ def test_scratch_cap(ctx):
     assert _status(mmq.mmq_quant_f32, ctx, 0x200000, 1024, 512) == mmq.MMQ_OK
 
 
-def test_export_needs_a_plane_and_a_device(ctx):
-    assert _status(mmq.mmq_plane_export, ctx, 0x100000, 8, 256, 0, 0x1, 0x2, 0x3) == mmq.MMQ_E_ARG
+def test_export_needs_a_plane_aligned_buffers_and_a_device(ctx):
+    assert _status(mmq.mmq_plane_export, ctx, 0x100000, 8, 256, 0, 0x1000, 0x2000, 0x3000) == mmq.MMQ_E_ARG
     mmq.mmq_quant_f32(ctx, 0x100000, 8, 256)
+    # the scales and sums are written as 4-byte words
+    for dq, s in ((0x2002, 0x3000), (0x2000, 0x3001)):
+        rc = _lib.lib.mmq_plane_export(ctx, 0x100000, 8, 256, 0, 0x1000, dq, s, None)
+        assert rc == mmq.MMQ_E_ARG
     rc = _lib.lib.mmq_plane_export(ctx, 0x100000, 8, 256, 0, 0x1000, 0x2000, 0x3000, None)
     assert rc == mmq.MMQ_E_DEVICE
 
