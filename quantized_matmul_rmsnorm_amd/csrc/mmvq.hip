@@ -25,7 +25,8 @@
 // computed once per lane.  One f32 expression per block adds the block's
 // term; a wave-wide sum per row finishes the output.  For rows of up to 256
 // blocks the plane slice stays in registers and the weights of the wave's
-// next row are in flight while a row is reduced.
+// next row are in flight while a row is reduced; longer rows re-read the
+// slice (from L2) once per pair of rows.
 #include <algorithm>
 
 #include "mmq_internal.h"
@@ -187,7 +188,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // and the weights of the wave's next row are loaded block by block as soon as
 // the current row's registers for that block are consumed, so a row's loads
 // are in flight while the previous row is reduced.
-// MAXR == 0: blocks are re-read from the plane for every row (any length).
+// MAXR == 0: blocks are re-read from the plane for every pair of rows (any
+// length).
 template <class F, int MAXR>
 __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
     const int lane = threadIdx.x & 63;
@@ -224,21 +226,31 @@ __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
             if (lane == 0) g.out[o] = acc;
         }
     } else {
-        for (int o = wave; o < od; o += nwaves) {
-            float acc = 0.0f;
+        // two rows per pass (o and o + nwaves): each plane block read serves both
+        for (int o = wave; o < od; o += 2 * nwaves) {
+            const int o2 = o + nwaves;
+            float acc = 0.0f, acc2 = 0.0f;
             for (int r = 0; r < rounds; ++r) {
                 const int b = 64 * r + lane;
-                if (b < nb) acc += F::term(F::act(g, b), F::load(g, o, b, nb, nsb));
+                if (b < nb) {
+                    const typename F::Act a = F::act(g, b);
+                    acc += F::term(a, F::load(g, o, b, nb, nsb));
+                    if (o2 < od) acc2 += F::term(a, F::load(g, o2, b, nb, nsb));
+                }
             }
             acc = wave_sum(acc);
-            if (lane == 0) g.out[o] = acc;
+            acc2 = wave_sum(acc2);
+            if (lane == 0) {
+                g.out[o] = acc;
+                if (o2 < od) g.out[o2] = acc2;
+            }
         }
     }
 }
 
-// Workgroups of one launch: every row gets a wave when the rows fit in two
-// rounds of resident waves; larger matrices get exactly the resident waves
-// (each then walks rows grid-stride with its plane slice loaded once).
+// Workgroups of one launch: every row (MAXR == 0: every pair of rows) gets a
+// wave when they fit in two rounds of resident waves; larger matrices get
+// exactly the resident waves (each then walks rows grid-stride).
 template <class F, int MAXR>
 int64_t mmvq_grid(int64_t rows) {
     static int per_cu = -1, n_cu = 0;
@@ -253,7 +265,7 @@ int64_t mmvq_grid(int64_t rows) {
         if (n_cu <= 0) n_cu = 256;
     }
     const int64_t resident = (int64_t)per_cu * n_cu;
-    const int64_t want = (rows + 3) / 4;
+    const int64_t want = MAXR == 0 ? (rows + 7) / 8 : (rows + 3) / 4;
     return want <= 2 * resident ? want : resident;
 }
 
@@ -400,7 +412,9 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     g.out = out;
     // up to 4 blocks per lane and row: register arrays sized to exactly that
     // many (fewer registers, more resident waves); longer rows re-read the
-    // plane per row, which leaves room for 8 waves per SIMD, a wave per row
+    // plane per pair of rows, which leaves room for 8 waves per SIMD (one
+    // row per wave measured 4% slower on 5120 x 13824, four rows per wave
+    // 50% slower: too few waves in flight)
     const int64_t nb = w.cols / kBlock;
     switch ((nb + 63) / 64) {
     case 1: launch_rows<F, 1>(g, w.rows, s); break;
