@@ -1,4 +1,4 @@
-"""CPU oracle for the q8-plane producers and the q4_K / q6_K matmuls.
+"""CPU oracle for the q8-plane producers and the q4_K / q5_K / q6_K matmuls.
 
 TEST INFRASTRUCTURE ONLY: tests/, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package; the product
@@ -47,13 +47,16 @@ def _load():
         lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f32.restype = ctypes.c_float
         lib.oracle_q4k_fields.argtypes = [P, P, P, P, P, P]
+        lib.oracle_q5k_fields.argtypes = [P, P, P, P, P, P]
         lib.oracle_q6k_fields.argtypes = [P, P, P, P]
         lib.oracle_dequant_q4k.argtypes = [P, I64, I64, P]
+        lib.oracle_dequant_q5k.argtypes = [P, I64, I64, P]
         lib.oracle_dequant_q6k.argtypes = [P, I64, I64, P]
         lib.oracle_rmsnorm.argtypes = [P, P, I64, I64, ctypes.c_float, P]
         lib.oracle_swiglu.argtypes = [P, P, I64, I64, P]
         lib.oracle_quantize.argtypes = [P, I64, I64, P, P, P]
         lib.oracle_gemm_q4k.argtypes = [P, P, P, P, I64, P, I64, P, I64, P]
+        lib.oracle_gemm_q5k.argtypes = [P, P, P, P, I64, P, I64, P, I64, P]
         lib.oracle_gemm_q6k.argtypes = [P, P, P, I64, P, I64, P, I64, P]
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -88,6 +91,16 @@ def q4k_fields(block: np.ndarray):
     return float(d[0]), float(dm[0]), sc, mn, q
 
 
+def q5k_fields(block: np.ndarray):
+    """Decode one 176-byte q5_K superblock -> (d, dmin, sc[8], m[8], q[256] in [0,31])."""
+    b = np.ascontiguousarray(block, dtype=np.uint8)
+    assert b.size == 176
+    d = np.zeros(1, np.float32); dm = np.zeros(1, np.float32)
+    sc = np.zeros(8, np.uint8); mn = np.zeros(8, np.uint8); q = np.zeros(256, np.uint8)
+    _load().oracle_q5k_fields(_p(b), _p(d), _p(dm), _p(sc), _p(mn), _p(q))
+    return float(d[0]), float(dm[0]), sc, mn, q
+
+
 def q6k_fields(block: np.ndarray):
     """Decode one 210-byte q6_K superblock -> (d, sc[16] int8, q[256] in [0,63])."""
     b = np.ascontiguousarray(block, dtype=np.uint8)
@@ -101,7 +114,8 @@ def dequant(wtype: str, raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
     """f64 dequantised weight matrix [rows][cols]."""
     raw = np.ascontiguousarray(raw, dtype=np.uint8)
     w = np.zeros((rows, cols), np.float64)
-    fn = _load().oracle_dequant_q4k if wtype == "q4_K" else _load().oracle_dequant_q6k
+    fn = {"q4_K": _load().oracle_dequant_q4k, "q5_K": _load().oracle_dequant_q5k,
+          "q6_K": _load().oracle_dequant_q6k}[wtype]
     fn(_p(raw), rows, cols, _p(w))
     return w
 
@@ -152,13 +166,17 @@ def gemm(wtype: str, Q, D, S, raw, od: int, id_: int, tok=None, outs=None) -> np
     raw = np.ascontiguousarray(raw, np.uint8)
     n = Q.shape[0]
     assert Q.shape[1] == id_ and id_ % 256 == 0
-    bpb = 144 if wtype == "q4_K" else 210
+    bpb = {"q4_K": 144, "q5_K": 176, "q6_K": 210}[wtype]
     assert raw.size == od * (id_ // 256) * bpb
     tok = _idx(tok, n); outs = _idx(outs, od)
     out = np.zeros((tok.size, outs.size), np.float32)
     if wtype == "q4_K":
         S = np.ascontiguousarray(S, np.int32)
         _load().oracle_gemm_q4k(_p(Q), _p(D), _p(S), _p(raw), id_, _p(tok), tok.size,
+                                _p(outs), outs.size, _p(out))
+    elif wtype == "q5_K":
+        S = np.ascontiguousarray(S, np.int32)
+        _load().oracle_gemm_q5k(_p(Q), _p(D), _p(S), _p(raw), id_, _p(tok), tok.size,
                                 _p(outs), outs.size, _p(out))
     elif wtype == "q6_K":
         _load().oracle_gemm_q6k(_p(Q), _p(D), _p(raw), id_, _p(tok), tok.size,

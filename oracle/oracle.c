@@ -1,6 +1,6 @@
 /*
- * oracle.c -- the CPU oracle for the q8-plane producers and the q4_K / q6_K
- * integer-dot matmuls.
+ * oracle.c -- the CPU oracle for the q8-plane producers and the q4_K / q5_K /
+ * q6_K integer-dot matmuls.
  *
  * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
  * cpu_baseline leg of bench.py may load this library.  It shares no source,
@@ -16,12 +16,13 @@
  *   [r60]  "64 · r60 — flipping the verified gate set to default-on", 3.2
  *   [d37]  "72 · D3-7 — attn_v-q6K MMVQ routing ...", Excerpts A, A2, C
  * The K-quant superblock layouts are not on those pages; they follow the
- * public GGUF q4_K / q6_K definitions (256 weights per superblock).
+ * public GGUF q4_K / q5_K / q6_K definitions (256 weights per superblock).
+ * The pages name a q5_K one-token arm beside the q6_K one [d37 Excerpt B].
  *
  * Pinned by tests/test_oracle_pins.py: brute-force f64 dequantised matmul on
  * tiny shapes, the integer special case (unit scales -> exact int matmul),
  * quantiser invariants, the RMSNorm and SwiGLU closed forms, and an
- * independent field encoder for both superblock formats.
+ * independent field encoder for the three superblock formats.
  *
  * Parity unpinned: (1) bit-compatibility of the two superblock byte layouts
  * with real GGUF files (no such file is available; the layouts are this
@@ -36,6 +37,7 @@
 #define QK 32          /* activation block: 32 values, one f32 scale, one int sum */
 #define QKK 256        /* K-quant superblock */
 #define Q4K_BYTES 144
+#define Q5K_BYTES 176
 #define Q6K_BYTES 210
 
 /* IEEE half -> float, written out from the binary16 definition. */
@@ -86,6 +88,34 @@ void oracle_q4k_fields(const uint8_t* blk, float* d, float* dmin,
 }
 
 /*
+ * q5_K superblock (176 B): f16 d, f16 dmin, the same 12 B of packed 6-bit
+ * (scale, min) pairs as q4_K, 32 B of high bits, 128 B of low nibbles.
+ * Quants are 5-bit: element e = 64 g + i (g = 0..3) takes its low nibble
+ * from byte 32 g + (i % 32) of the nibbles (low half for i < 32, high half
+ * otherwise) and its fifth bit from bit 2 g + (i >= 32) of high-bit byte
+ * i % 32.  Weight value is d * scale_j * q_e - dmin * min_j, j = e / 32.
+ */
+void oracle_q5k_fields(const uint8_t* blk, float* d, float* dmin,
+                       uint8_t sc[8], uint8_t mn[8], uint8_t q[256])
+{
+    const uint8_t* qh = blk + 16;
+    const uint8_t* qs = blk + 48;
+    /* the header (d, dmin, scales) has the q4_K layout */
+    uint8_t head[144];
+    uint8_t unused[256];
+    memcpy(head, blk, 16);
+    memset(head + 16, 0, 128);
+    oracle_q4k_fields(head, d, dmin, sc, mn, unused);
+    for (int e = 0; e < 256; e++) {
+        int g = e / 64, i = e % 64;
+        uint8_t byte = qs[32 * g + (i % 32)];
+        int lo = (i < 32) ? (byte & 15) : (byte >> 4);
+        int hi = (qh[i % 32] >> (2 * g + (i >= 32))) & 1;
+        q[e] = (uint8_t)(lo + 16 * hi);
+    }
+}
+
+/*
  * q6_K superblock (210 B): ql[128] low nibbles, qh[64] high 2-bit pairs,
  * 16 int8 sub-scales (one per 16 elements), f16 d.  Weight value is
  * d * scale[e / 16] * (q_e - 32), q_e in [0, 63].
@@ -114,6 +144,19 @@ void oracle_dequant_q4k(const uint8_t* raw, int64_t rows, int64_t cols, double* 
         for (int64_t sb = 0; sb < nsb; sb++) {
             float d, dmin; uint8_t sc[8], mn[8], q[256];
             oracle_q4k_fields(raw + (o * nsb + sb) * Q4K_BYTES, &d, &dmin, sc, mn, q);
+            for (int e = 0; e < 256; e++)
+                w[o * cols + sb * 256 + e] =
+                    (double)d * sc[e / 32] * q[e] - (double)dmin * mn[e / 32];
+        }
+}
+
+void oracle_dequant_q5k(const uint8_t* raw, int64_t rows, int64_t cols, double* w)
+{
+    int64_t nsb = cols / QKK;
+    for (int64_t o = 0; o < rows; o++)
+        for (int64_t sb = 0; sb < nsb; sb++) {
+            float d, dmin; uint8_t sc[8], mn[8], q[256];
+            oracle_q5k_fields(raw + (o * nsb + sb) * Q5K_BYTES, &d, &dmin, sc, mn, q);
             for (int e = 0; e < 256; e++)
                 w[o * cols + sb * 256 + e] =
                     (double)d * sc[e / 32] * q[e] - (double)dmin * mn[e / 32];
@@ -232,6 +275,46 @@ void oracle_gemm_q4k(const int8_t* Q, const float* D, const int32_t* S,
             for (int64_t sb = 0; sb < nsb; sb++) {
                 float d, dmin; uint8_t sc[8], mn[8], qw[256];
                 oracle_q4k_fields(raw + (o * nsb + sb) * Q4K_BYTES, &d, &dmin, sc, mn, qw);
+                for (int j = 0; j < 8; j++) {
+                    int64_t b = sb * 8 + j;
+                    int32_t I = 0;
+                    for (int l = 0; l < QK; l++)
+                        I += (int32_t)qw[j * QK + l] * (int32_t)Q[t * id + b * QK + l];
+                    float Da = D[t * nb + b];
+                    float dsc = d * (float)sc[j];
+                    float dmn = dmin * (float)mn[j];
+                    float t1 = (Da * dsc) * (float)I;
+                    float t2 = (Da * (float)S[t * nb + b]) * dmn;
+                    acc += (double)(t1 - t2);
+                }
+            }
+            out[it * nout + jo] = (float)acc;
+        }
+    }
+}
+
+/*
+ * q5_K integer-dot matmul over a q8 plane: the q4_K expression with 5-bit
+ * quants (the one-token arm of d37 Excerpt B is this with ntok = 1):
+ *   I    = sum_{k in b} q_w[o][k] * Q[t][k]                (exact int32)
+ *   term = (D[t][b] * (d * sc_j)) * I  -  (D[t][b] * S[t][b]) * (dmin * m_j)
+ * each term in f32, summed over blocks in f64, stored as f32.
+ */
+void oracle_gemm_q5k(const int8_t* Q, const float* D, const int32_t* S,
+                     const uint8_t* raw, int64_t id,
+                     const int64_t* tok, int64_t ntok,
+                     const int64_t* outs, int64_t nout, float* out)
+{
+    int64_t nb = id / QK, nsb = id / QKK;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t jo = 0; jo < nout; jo++) {
+        int64_t o = outs[jo];
+        for (int64_t it = 0; it < ntok; it++) {
+            int64_t t = tok[it];
+            double acc = 0.0;
+            for (int64_t sb = 0; sb < nsb; sb++) {
+                float d, dmin; uint8_t sc[8], mn[8], qw[256];
+                oracle_q5k_fields(raw + (o * nsb + sb) * Q5K_BYTES, &d, &dmin, sc, mn, qw);
                 for (int j = 0; j < 8; j++) {
                     int64_t b = sb * 8 + j;
                     int32_t I = 0;

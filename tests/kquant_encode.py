@@ -1,4 +1,4 @@
-"""Test-side encoders for the q4_K / q6_K superblock formats.
+"""Test-side encoders for the q4_K / q5_K / q6_K superblock formats.
 
 Written independently of the oracle's decoders (the oracle decodes bytes into
 fields; this module packs fields into bytes) from the public GGUF K-quant
@@ -44,6 +44,30 @@ def q4k_encode(d_bits: int, dmin_bits: int, sc, mn, q) -> np.ndarray:
     return b
 
 
+def q5k_encode(d_bits: int, dmin_bits: int, sc, mn, q) -> np.ndarray:
+    """Pack one q5_K superblock (176 B).
+
+    sc, mn: eight 6-bit sub-block scales and mins; q: 256 5-bit quants.
+    Layout: d (f16) | dmin (f16) | 12 scale bytes (packed as in q4_K) |
+    32 high-bit bytes | 128 low-nibble bytes (arranged as the q4_K quants).
+    High-bit byte l holds, in bit 2*g, the fifth bit of element 64*g + l and,
+    in bit 2*g + 1, that of element 64*g + 32 + l.
+    """
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 32 for v in q)
+    head = q4k_encode(d_bits, dmin_bits, sc, mn, [v & 15 for v in q])
+    qh = np.zeros(32, np.int64)
+    for g in range(4):
+        for l in range(32):
+            qh[l] |= (q[64 * g + l] >> 4) << (2 * g)
+            qh[l] |= (q[64 * g + 32 + l] >> 4) << (2 * g + 1)
+    b = np.zeros(176, np.uint8)
+    b[0:16] = head[0:16]
+    b[16:48] = qh
+    b[48:176] = head[16:144]
+    return b
+
+
 def q6k_encode(d_bits: int, sc, q) -> np.ndarray:
     """Pack one q6_K superblock (210 B).
 
@@ -80,6 +104,21 @@ def random_q4k(rng, od: int, id_: int):
             d = np.float16(rng.uniform(1e-3, 1e-2)); dm = np.float16(rng.uniform(1e-3, 1e-2))
             sc = rng.integers(0, 64, 8); mn = rng.integers(0, 64, 8); q = rng.integers(0, 16, 256)
             raw[o, s * 144:(s + 1) * 144] = q4k_encode(f16_bits(d), f16_bits(dm), sc, mn, q)
+            j = np.arange(256) // 32
+            w[o, s * 256:(s + 1) * 256] = float(d) * sc[j] * q - float(dm) * mn[j]
+    return raw, w
+
+
+def random_q5k(rng, od: int, id_: int):
+    """Random q5_K matrix as (bytes [od, nsb*176], dequantised f64 [od, id])."""
+    nsb = id_ // 256
+    raw = np.zeros((od, nsb * 176), np.uint8)
+    w = np.zeros((od, id_), np.float64)
+    for o in range(od):
+        for s in range(nsb):
+            d = np.float16(rng.uniform(1e-3, 1e-2)); dm = np.float16(rng.uniform(1e-3, 1e-2))
+            sc = rng.integers(0, 64, 8); mn = rng.integers(0, 64, 8); q = rng.integers(0, 32, 256)
+            raw[o, s * 176:(s + 1) * 176] = q5k_encode(f16_bits(d), f16_bits(dm), sc, mn, q)
             j = np.arange(256) // 32
             w[o, s * 256:(s + 1) * 256] = float(d) * sc[j] * q - float(dm) * mn[j]
     return raw, w

@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.kquant_encode import f16_bits, q4k_encode, q6k_encode, random_q4k, random_q6k
+from tests.kquant_encode import (f16_bits, q4k_encode, q5k_encode, q6k_encode, random_q4k,
+                                 random_q5k, random_q6k)
 
 U24 = 2.0 ** -24
 
@@ -52,6 +53,17 @@ def test_q4k_field_roundtrip_random():
         assert np.array_equal(gsc, sc) and np.array_equal(gmn, mn) and np.array_equal(gq, q)
 
 
+def test_q5k_field_roundtrip_random():
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        sc = rng.integers(0, 64, 8); mn = rng.integers(0, 64, 8); q = rng.integers(0, 32, 256)
+        d = np.float16(rng.uniform(1e-3, 1e-2)); dm = np.float16(rng.uniform(1e-3, 1e-2))
+        blk = q5k_encode(f16_bits(d), f16_bits(dm), sc, mn, q)
+        gd, gdm, gsc, gmn, gq = oracle.q5k_fields(blk)
+        assert gd == float(d) and gdm == float(dm)
+        assert np.array_equal(gsc, sc) and np.array_equal(gmn, mn) and np.array_equal(gq, q)
+
+
 def test_q6k_field_roundtrip_random():
     rng = np.random.default_rng(2)
     for _ in range(50):
@@ -83,6 +95,32 @@ def test_q4k_hand_worked_block():
     assert w[0, 0] == 1.0 * 3 * 2 - 0.5 * 5          # sub-block 0
     assert w[0, 32] == 1.0 * sc[1] * 7 - 0.5 * mn[1]  # element 32 is sub-block 1
     assert w[0, 255] == 1.0 * sc[7] * 15 - 0.5 * mn[7]
+
+
+def test_q5k_hand_worked_block():
+    """A q5_K block written byte by byte: the header as in the q4_K block
+    above, then high bits and low nibbles whose quants are worked out by hand."""
+    blk = np.zeros(176, np.uint8)
+    blk[0:2] = [0x00, 0x3C]          # d = 1.0
+    blk[2:4] = [0x00, 0x38]          # dmin = 0.5
+    blk[4] = 0xC3                    # sc0 = 3; top bits 11 -> high bits of sc4
+    blk[8] = 0x45                    # m0 = 5; top bits 01 -> high bits of m4
+    blk[12] = 0x5A                   # sc4 = 0x3A, m4 = 0x15
+    blk[16] = 0b10000101             # byte 0: bit0 -> e0, bit2 -> e64, bit7 -> e224
+    blk[16 + 31] = 0b00000010        # byte 31: bit1 -> e63
+    blk[48] = 0x72                   # e0 low 2, e32 low 7
+    blk[48 + 32] = 0x3C              # e64 low 0xC, e96 low 3
+    blk[48 + 31] = 0x90              # e31 low 0, e63 low 9
+    blk[48 + 96] = 0x0E              # e192 low 0xE, e224 low 0
+    d, dm, sc, mn, q = oracle.q5k_fields(blk)
+    assert (d, dm) == (1.0, 0.5)
+    assert sc[0] == 3 and mn[0] == 5 and sc[4] == 0x3A and mn[4] == 0x15
+    assert q[0] == 2 + 16 and q[32] == 7 and q[64] == 12 + 16 and q[96] == 3
+    assert q[31] == 0 and q[63] == 9 + 16 and q[192] == 14 and q[224] == 16
+    assert q[1] == 0 and q[65] == 0
+    w = oracle.dequant("q5_K", blk, 1, 256)
+    assert w[0, 0] == 1.0 * 3 * 18 - 0.5 * 5
+    assert w[0, 224] == 1.0 * sc[7] * 16 - 0.5 * mn[7]
 
 
 def test_q6k_hand_worked_block():
@@ -308,6 +346,25 @@ def test_gemm_q6k_vs_bruteforce_f64(n, od, id_):
     assert np.all(np.abs(got - ref) <= 3 * U24 * mag + U24 * np.abs(ref) + 1e-30)
 
 
+@pytest.mark.parametrize("n,od,id_", [(1, 3, 256), (4, 6, 512), (8, 16, 256)])
+def test_gemm_q5k_vs_bruteforce_f64(n, od, id_):
+    rng = np.random.default_rng(300 + n)
+    raw, w = random_q5k(rng, od, id_)
+    Q, D, S = _plane(rng, n, id_)
+    a = Q.astype(np.float64) * np.repeat(D.astype(np.float64), 32, axis=1)
+    ref = a @ w.T
+    got = oracle.gemm("q5_K", Q, D, S, raw, od, id_)
+    nsb = id_ // 256
+    mag = np.zeros_like(ref)
+    for o in range(od):
+        for s in range(nsb):
+            d, dm, sc, mn, q = oracle.q5k_fields(raw[o, s * 176:(s + 1) * 176])
+            j = np.arange(256) // 32
+            mag[:, o] += np.abs(a[:, s * 256:(s + 1) * 256]) @ (d * sc[j] * q + dm * mn[j])
+    assert np.all(np.abs(got - ref) <= 4 * U24 * mag + U24 * np.abs(ref) + 1e-30)
+    assert np.abs(ref).max() > 1000 * (4 * U24 * mag.max())
+
+
 def _unit_plane(rng, n, id_):
     """Integer activations with D = 1 exactly: every block holds a +-127."""
     Q = rng.integers(-127, 128, (n, id_)).astype(np.int8)
@@ -335,6 +392,26 @@ def test_gemm_q4k_integer_special_case():
     assert np.array_equal(got.astype(np.int64), ref)
     # the output is [token][output]: a transposed result would not even match in shape
     assert got.shape == (n, od)
+
+
+def test_gemm_q5k_integer_special_case():
+    """d = dmin = 1, sc = 1: out = Q q^T - Q-block-sums . m exactly, with
+    5-bit quants (a dropped fifth bit would be off by 16 per set bit)."""
+    rng = np.random.default_rng(12)
+    n, od, id_ = 5, 7, 512
+    Q, D, S = _unit_plane(rng, n, id_)
+    nsb = id_ // 256
+    raw = np.zeros((od, nsb * 176), np.uint8)
+    qall = np.zeros((od, id_), np.int64); mall = np.zeros((od, id_ // 32), np.int64)
+    for o in range(od):
+        for s in range(nsb):
+            q = rng.integers(0, 32, 256); mn = rng.integers(0, 64, 8)
+            raw[o, s * 176:(s + 1) * 176] = q5k_encode(0x3C00, 0x3C00, [1] * 8, mn, q)
+            qall[o, s * 256:(s + 1) * 256] = q; mall[o, s * 8:(s + 1) * 8] = mn
+    ref = Q.astype(np.int64) @ qall.T - S.astype(np.int64) @ mall.T
+    got = oracle.gemm("q5_K", Q, D, S, raw, od, id_)
+    assert got.shape == (n, od)
+    assert np.array_equal(got.astype(np.int64), ref)
 
 
 def test_gemm_q6k_integer_special_case_and_halves():
