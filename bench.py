@@ -190,29 +190,32 @@ def decode_gemv(mmq, torch, synth):
                 mmq.mmq_weight_free(w)
         res["aggregate_GB_s"] = round(tot_b / (tot_t * 1e-6) / 1e9, 1)
         res["aggregate_frac_hbm"] = round(res["aggregate_GB_s"] / PEAK_HBM_GBS, 4)
-        # q4_K one-token GEMVs at the 14B shapes (ffn gate/up, attention q/output)
-        q4 = {}
-        for name, (od, id_, copies) in {"ffn_gate": (13824, 5120, 8),
-                                        "attn_q": (5120, 5120, 16)}.items():
-            raw = synth.q4k_weights(synth.rng_for("decode14b", 0, name), od, id_)
-            ws = [mmq.mmq_register_weight(ctx, mmq.MMQ_Q4_K, od, id_, raw, mmq.MMQ_USE_GEMV)
-                  for _ in range(copies)]
-            del raw
-            out = torch.empty((od,), dtype=torch.float32, device="cuda")
-            mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)
-            mmq.mmvq_q4k(ctx, ws[0], y5, out)
-            torch.cuda.synchronize()
-            ref = out.clone()
-            reps = max(2 * copies, 32)
-            t_us = _graph_time_us(torch, lambda i: mmq.mmvq_q4k(ctx, ws[i % copies], y5, out), reps)
-            if not torch.equal(out, ref):
-                raise RuntimeError(f"{name}: graph replay output differs from the eager launch")
-            nbytes = od * id_ / 256 * 144 + id_ * 1.25 + od * 4
-            q4[name] = {"od": od, "id": id_, "us": round(t_us, 3),
-                        "GB_s": round(nbytes / (t_us * 1e-6) / 1e9, 1)}
-            for w in ws:
-                mmq.mmq_weight_free(w)
-        res["q4_K"] = q4
+        # q4_K and q5_K one-token GEMVs at the 14B shapes (ffn gate/up, attention q/output)
+        arms = {"q4_K": (mmq.MMQ_Q4_K, synth.q4k_weights, mmq.mmvq_q4k, 144),
+                "q5_K": (mmq.MMQ_Q5_K, synth.q5k_weights, mmq.mmvq_q5k, 176)}
+        for wt, (code, gen, fn, bpb) in arms.items():
+            arm = {}
+            for name, (od, id_, copies) in {"ffn_gate": (13824, 5120, 8),
+                                            "attn_q": (5120, 5120, 16)}.items():
+                raw = gen(synth.rng_for("decode14b", 0, f"{name}/{wt}"), od, id_)
+                ws = [mmq.mmq_register_weight(ctx, code, od, id_, raw, mmq.MMQ_USE_GEMV)
+                      for _ in range(copies)]
+                del raw
+                out = torch.empty((od,), dtype=torch.float32, device="cuda")
+                mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)
+                fn(ctx, ws[0], y5, out)
+                torch.cuda.synchronize()
+                ref = out.clone()
+                reps = max(2 * copies, 32)
+                t_us = _graph_time_us(torch, lambda i: fn(ctx, ws[i % copies], y5, out), reps)
+                if not torch.equal(out, ref):
+                    raise RuntimeError(f"{wt} {name}: graph replay output differs from the eager launch")
+                nbytes = od * id_ / 256 * bpb + id_ * 1.25 + od * 4
+                arm[name] = {"od": od, "id": id_, "us": round(t_us, 3),
+                             "GB_s": round(nbytes / (t_us * 1e-6) / 1e9, 1)}
+                for w in ws:
+                    mmq.mmq_weight_free(w)
+            res[wt] = arm
         # decode producers (rms 5120, swiglu 13824) at n = 1
         for name, fn in (("rms_5120", lambda i: mmq.mmq_quant_rms(ctx, x, wn, y5, 1, 5120, 1e-6, 0)),
                          ("swiglu_13824", lambda i: mmq.mmq_quant_swiglu(ctx, g, u, y13, 1, 13824, 0))):

@@ -69,6 +69,7 @@ extern "C" {
 
 /* ---- weight types (values follow the GGUF type ids) ------------------ */
 #define MMQ_Q4_K 12           /* 144-byte superblocks of 256 weights         */
+#define MMQ_Q5_K 13           /* 176-byte superblocks of 256 weights (GEMV only) */
 #define MMQ_Q6_K 14           /* 210-byte superblocks of 256 weights         */
 
 /* ---- context flags --------------------------------------------------- */
@@ -79,12 +80,12 @@ extern "C" {
 
 /* ---- registration uses ------------------------------------------------ */
 #define MMQ_USE_GEMM 1u       /* prefill matmul (any n)                      */
-#define MMQ_USE_GEMV 2u       /* one-token GEMV (q6_K only)                  */
+#define MMQ_USE_GEMV 2u       /* one-token GEMV (and the few-token band)      */
 
-#define MMQ_PLANE_ROWS 32
+#define MMQ_PLANE_ROWS 32       /* plane rows are padded to this multiple     */
 #define MMQ_WRITE_AUTO (-1)     /* write_y: skip when allowed, degrade otherwise */
 #define MMQ_FOREIGN_F32 1       /* mmq_register_foreign_consumer kinds */
-#define MMQ_FOREIGN_QUANT 2     /* plane rows are padded to this multiple     */
+#define MMQ_FOREIGN_QUANT 2
 
 typedef struct mmq_ctx mmq_ctx;
 typedef struct mmq_weight mmq_weight;
@@ -106,6 +107,7 @@ typedef struct mmq_stats_t {
     int64_t degraded_writes;        /* skip-write requests that wrote y (mixed consumers) */
     int64_t unfused_fallbacks;      /* MMQ_WRITE_AUTO producers without plane memory      */
     int64_t small_n_gemv;           /* matmul calls served by the few-token GEMV path     */
+    int64_t launches_mmvq_q5k;
 } mmq_stats_t;
 
 /* ---- context ----------------------------------------------------------- */
@@ -135,11 +137,13 @@ int64_t mmq_plane_rows(int64_t n);
  * weight] ---------------------------------------------------------------- */
 
 /* Copy `rows` x `cols` weights of type `type` (raw superblocks, row-major
- * [rows][cols/256], 144 or 210 bytes each) from host memory and repack them
- * into device tiles for the consumers named in `uses` (MMQ_USE_*; 0 means
- * every consumer the type supports).  cols % 256 == 0.  raw_host may be
+ * [rows][cols/256], 144, 176 or 210 bytes each) from host memory and repack
+ * them into device tiles for the consumers named in `uses` (MMQ_USE_*; 0
+ * means every consumer the type supports).  cols % 256 == 0.  raw_host may be
  * freed on return.  Synchronises the device.
- * The default uses: q4_K MMQ_USE_GEMM, q6_K MMQ_USE_GEMM | MMQ_USE_GEMV.
+ * The default uses: q4_K MMQ_USE_GEMM, q6_K MMQ_USE_GEMM | MMQ_USE_GEMV,
+ * q5_K MMQ_USE_GEMV (q5_K has a decode arm only; MMQ_USE_GEMM with q5_K is
+ * MMQ_E_TYPE).
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE (unknown type), MMQ_E_OOM,
  * MMQ_E_HIP. */
 int mmq_register_weight(mmq_ctx* ctx, int type, int64_t rows, int64_t cols,
@@ -208,6 +212,15 @@ int mmvq_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
  * 32-block: D * (d*sc_j * sum(q_w * q) - dmin*m_j * S).  w must be
  * registered with MMQ_USE_GEMV. */
 int mmvq_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
+             void* stream);
+
+/* One-token q5_K GEMV, the third decode arm of the per-type routing
+ * [d37 Excerpt B: the Q5_K decode arm].  A q5_K superblock is the q4_K one
+ * plus a fifth bit per weight (codes 0..31); per 32-block the term is
+ * D * (d*sc_j * sum(q_w * q) - dmin*m_j * S), as for q4_K.  w must be a
+ * q5_K weight (registered with MMQ_USE_GEMV, the default for the type);
+ * a, out and the errors as for mmvq_q6k. */
+int mmvq_q5k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
              void* stream);
 
 /* ---- consumer set [r60 3.2-3.3: the registration-time nb_bt_only flag] -- */

@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "MMQ_OK", -1: "MMQ_E_ARG", -2: "MMQ_E_SHAPE", -3: "MMQ_E_TYPE
                 -4: "MMQ_E_OOM", -5: "MMQ_E_DEAD_WRITE", -6: "MMQ_E_HIP", -7: "MMQ_E_DEVICE"}
 
 MMQ_Q4_K = 12
+MMQ_Q5_K = 13
 MMQ_Q6_K = 14
 MMQ_CTX_SYNC_CHECK = 1
 MMQ_CTX_DRYRUN = 2
@@ -44,7 +45,7 @@ EXPORTS = [
     "mmq_create", "mmq_destroy", "mmq_last_error", "mmq_set_scratch_cap", "mmq_plane_rows",
     "mmq_register_weight", "mmq_weight_free", "mmq_weight_bytes",
     "mmq_quant_rms", "mmq_quant_swiglu", "mmq_quant_f32",
-    "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k", "mmvq_q4k",
+    "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k",
     "mmq_register_foreign_consumer", "mmq_plane_only",
     "mmq_cache_clear", "mmq_cache_invalidate", "mmq_plane_export", "mmq_stats",
 ]
@@ -62,7 +63,7 @@ class mmq_stats_t(ctypes.Structure):
         "launches_gemm_q4k", "launches_gemm_q6k", "launches_mmvq_q6k",
         "cache_hits", "cache_misses", "cache_refusals", "cache_entries",
         "plane_bytes", "weight_bytes", "launches_mmvq_q4k", "degraded_writes",
-        "unfused_fallbacks", "small_n_gemv")]
+        "unfused_fallbacks", "small_n_gemv", "launches_mmvq_q5k")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -100,6 +101,7 @@ def _load():
         "mmq_gemm_q6k": (I, [P, P, P, I64, P, P]),
         "mmvq_q6k": (I, [P, P, P, P, P]),
         "mmvq_q4k": (I, [P, P, P, P, P]),
+        "mmvq_q5k": (I, [P, P, P, P, P]),
         "mmq_register_foreign_consumer": (I, [P, I]),
         "mmq_plane_only": (I, [P]),
         "mmq_cache_clear": (None, [P]),
@@ -188,7 +190,7 @@ def mmq_register_weight(ctx, wtype: int, rows: int, cols: int, raw_host, uses: i
         arr = np.frombuffer(raw_host, dtype=np.uint8)
     else:
         arr = np.ascontiguousarray(raw_host, dtype=np.uint8)
-    bpb = {MMQ_Q4_K: 144, MMQ_Q6_K: 210}.get(wtype)
+    bpb = {MMQ_Q4_K: 144, MMQ_Q5_K: 176, MMQ_Q6_K: 210}.get(wtype)
     if bpb is not None and rows >= 1 and cols >= 256 and cols % 256 == 0 and \
             arr.size != rows * (cols // 256) * bpb:
         # the C call reads exactly that many bytes from the pointer it is given
@@ -243,6 +245,11 @@ def mmvq_q6k(ctx, w, a, out, stream=None):
 def mmvq_q4k(ctx, w, a, out, stream=None):
     f = _f32() if not isinstance(a, int) else None
     return _check(lib.mmvq_q4k(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
+
+
+def mmvq_q5k(ctx, w, a, out, stream=None):
+    f = _f32() if not isinstance(a, int) else None
+    return _check(lib.mmvq_q5k(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
 
 
 def mmq_register_foreign_consumer(ctx, kind: int) -> None:

@@ -443,7 +443,7 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     const char* who = "mmq_register_weight";
     if (!c || !raw_host || !out) return fail(MMQ_E_ARG, "%s: null argument", who);
     *out = nullptr;
-    if (type != MMQ_Q4_K && type != MMQ_Q6_K)
+    if (type != MMQ_Q4_K && type != MMQ_Q5_K && type != MMQ_Q6_K)
         return fail(MMQ_E_TYPE, "%s: unsupported weight type %d", who, type);
     if (rows < 1 || cols < kSuper || cols % kSuper != 0 || rows > ((int64_t)1 << 30) ||
         cols > ((int64_t)1 << 24))
@@ -451,7 +451,11 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
                     (long long)rows, (long long)cols);
     if (uses & ~(MMQ_USE_GEMM | MMQ_USE_GEMV))
         return fail(MMQ_E_ARG, "%s: unknown uses 0x%x", who, uses);
-    if (uses == 0) uses = type == MMQ_Q4_K ? MMQ_USE_GEMM : (MMQ_USE_GEMM | MMQ_USE_GEMV);
+    if (uses == 0)
+        uses = type == MMQ_Q4_K ? MMQ_USE_GEMM
+               : type == MMQ_Q5_K ? MMQ_USE_GEMV : (MMQ_USE_GEMM | MMQ_USE_GEMV);
+    if (type == MMQ_Q5_K && (uses & MMQ_USE_GEMM))
+        return fail(MMQ_E_TYPE, "%s: q5_K has a one-token GEMV arm only (uses=%u)", who, uses);
 
     mmq_weight* h = new mmq_weight();
     h->ctx = c;
@@ -463,7 +467,7 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     w.rows_pad = round_up(rows, kTileO);
     w.uses = uses;
     const int64_t nsb = cols / kSuper, nb = cols / kBlock, og = w.rows_pad / 32;
-    const int64_t bpb = type == MMQ_Q4_K ? 144 : 210;
+    const int64_t bpb = type == MMQ_Q4_K ? 144 : type == MMQ_Q5_K ? 176 : 210;
     const int64_t raw_bytes = rows * nsb * bpb;
     // matmul tiles: one f16 per weight (q4_K sc*q, q6_K q-32), superblock
     // scales, and per (row group, superblock) the q4_K mins or the q6_K
@@ -472,8 +476,10 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     const int64_t dmr_b = og * nsb * (type == MMQ_Q4_K ? 64 : 32) * 4;
     const int64_t mf_b = og * nsb * (type == MMQ_Q4_K ? 512 * 2 : 32 * 16 * 2);
     // one-token GEMV tiles: q6_K ql/qh/sc/d; q4_K nibbles (in ql), (sc, m)
-    // pairs (in sc) and (d, dmin) per superblock (in d), no qh
-    const int64_t ql_b = rows * nb * 16, qh_b = type == MMQ_Q6_K ? rows * nb * 8 : 0,
+    // pairs (in sc) and (d, dmin) per superblock (in d), no qh; q5_K as
+    // q4_K plus the fifth bits (4 B per 32 weights)
+    const int64_t ql_b = rows * nb * 16,
+                  qh_b = type == MMQ_Q6_K ? rows * nb * 8 : type == MMQ_Q5_K ? rows * nb * 4 : 0,
                   sc_b = rows * nb * 2, dv_b = rows * nsb * (type == MMQ_Q6_K ? 4 : 8);
     // the matmul addresses its tiles with 32-bit buffer offsets
     if ((uses & MMQ_USE_GEMM) && wa_b > (int64_t)0xFFFFFFFF) {
@@ -531,7 +537,9 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
             cleanup();
             return fail(MMQ_E_OOM, "%s: GEMV tiles", who);
         }
-        w.gv_ql = (uint4*)p1; w.gv_qh = (uint2*)p2; w.gv_sc = (int16_t*)p3; w.gv_d = (float*)p4;
+        w.gv_ql = (uint4*)p1; w.gv_sc = (int16_t*)p3; w.gv_d = (float*)p4;
+        if (type == MMQ_Q5_K) w.gv_h5 = (uint32_t*)p2;
+        else w.gv_qh = (uint2*)p2;
         e = launch_repack_gemv((const uint8_t*)raw_dev, w, nullptr);
         if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: repack"); }
     }
@@ -549,7 +557,8 @@ void mmq_weight_free(mmq_weight* h) {
     if (!h->dry) {
         (void)hipSetDevice(h->ctx->device);
         (void)hipDeviceSynchronize();
-        void* ps[] = {h->w.wa, h->w.dmr, h->w.mfrag, h->w.gv_ql, h->w.gv_qh, h->w.gv_sc, h->w.gv_d};
+        void* ps[] = {h->w.wa,    h->w.dmr,   h->w.mfrag, h->w.gv_ql,
+                      h->w.gv_qh, h->w.gv_h5, h->w.gv_sc, h->w.gv_d};
         for (void* p : ps)
             if (p) (void)hipFree(p);
     }
@@ -681,6 +690,19 @@ int mmvq_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
     return after_launch(c, launch_mmvq_q4k(w->w, pl, out, s), s, who);
+}
+
+int mmvq_q5k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* stream) {
+    const char* who = "mmvq_q5k";
+    int rc = consume_check(c, w, a, 1, out, MMQ_Q5_K, MMQ_USE_GEMV, who);
+    if (rc) return rc;
+    if ((rc = use_device(c))) return rc;
+    PlaneView pl;
+    if ((rc = plane_for(c, who, a, 1, w->w.cols, stream, &pl))) return rc;
+    c->st.launches_mmvq_q5k++;
+    if (c->dry) return MMQ_OK;
+    hipStream_t s = (hipStream_t)stream;
+    return after_launch(c, launch_mmvq_q5k(w->w, pl, out, s), s, who);
 }
 
 int mmq_register_foreign_consumer(mmq_ctx* c, int kind) {

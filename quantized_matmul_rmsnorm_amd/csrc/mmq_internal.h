@@ -28,7 +28,7 @@ constexpr int kTileO = 128;
 // Registered weight, device side.  Layouts are written by repack.hip and read
 // by gemm.hip / mmvq.hip; they are described there.
 struct WeightDev {
-    int type = 0;             // 12 = q4_K, 14 = q6_K
+    int type = 0;             // 12 = q4_K, 13 = q5_K (GEMV only), 14 = q6_K
     int64_t rows = 0, cols = 0, rows_pad = 0;
     unsigned uses = 0;
     // prefill matmul tiles
@@ -37,10 +37,11 @@ struct WeightDev {
     _Float16* mfrag = nullptr;// q4_K: 6-bit mins as f16, fragment order;
                               // q6_K: [row group][superblock][32 rows][16] f16 sub-scales
     // one-token GEMV
-    uint4* gv_ql = nullptr;   // [rows][cols/32] 4-bit codes (q6_K: their low nibbles)
+    uint4* gv_ql = nullptr;   // [rows][cols/32] 4-bit codes (q5_K, q6_K: their low nibbles)
     uint2* gv_qh = nullptr;   // q6_K: [rows][cols/32] high bit pairs
-    int16_t* gv_sc = nullptr; // [rows][cols/32] q6_K: two int8 sub-scales; q4_K: sc | m << 8
-    float* gv_d = nullptr;    // q6_K: [rows][cols/256] d; q4_K: [rows][cols/256][2] d, dmin
+    uint32_t* gv_h5 = nullptr;// q5_K: [rows][cols/32] fifth bits
+    int16_t* gv_sc = nullptr; // [rows][cols/32] q6_K: two int8 sub-scales; q4_K, q5_K: sc | m << 8
+    float* gv_d = nullptr;    // q6_K: [rows][cols/256] d; q4_K, q5_K: [rows][cols/256][2] d, dmin
     int64_t bytes = 0;
 };
 
@@ -79,6 +80,8 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
 hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
 hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,
+                           hipStream_t s);
+hipError_t launch_mmvq_q5k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
 // A few tokens at once over the GEMV tiles (out [n][rows]); used when the n
 // tokens' plane fits the LDS in one pass.

@@ -1,4 +1,4 @@
-// mmvq.hip -- one-token q6_K / q4_K GEMV over a q8 activation plane (gfx950).
+// mmvq.hip -- one-token q6_K / q4_K / q5_K GEMV over a q8 activation plane (gfx950).
 //
 // Method ("72 · D3-7 ...", section 2 and Excerpts A, A2, B): at one token the
 // matmul is a weight-streaming GEMV; the activation is quantised once into a
@@ -9,7 +9,9 @@
 //   q6_K: per 32-block, D * d * (sc0*I0 + sc1*I1), I0/I1 the dots of the
 //         16-value halves of (q_w - 32) with the codes;
 //   q4_K: per 32-block j of a superblock, D * (d*sc_j * I - dmin*m_j * S),
-//         I = sum(q_w * q), S the plane's code sum of the block.
+//         I = sum(q_w * q), S the plane's code sum of the block;
+//   q5_K: the q4_K term with 5-bit codes q_w (the low nibble plus a fifth
+//         bit stored apart; Excerpt B's q5_K arm).
 //
 // Design for CDNA4.  The kernel is bound by streaming the packed weights from
 // HBM, so the weights are read exactly once, with non-temporal loads, in
@@ -54,6 +56,7 @@ __device__ __forceinline__ uint2 nt_load(const uint2* p) {
 struct MvArgs {
     const uint4* ql;      // [od][nb] packed 4-bit codes
     const uint2* qh;      // q6_K: [od][nb] high bit pairs
+    const uint32_t* h5;   // q5_K: [od][nb] fifth bits
     const int16_t* sc;    // [od][nb] scales
     const float* dv;      // q6_K: [od][nsb] d; q4_K: [od][nsb][2] d, dmin
     const int8_t* Q;      // plane codes (row 0)
@@ -161,6 +164,44 @@ struct Q4 {
         i = dot4((L.z >> 4) & m4, a.q1.y, i);
         i = dot4(L.w & m4, a.q1.z, i);
         i = dot4((L.w >> 4) & m4, a.q1.w, i);
+        const float sc = (float)(w.s & 0xFF);
+        const float mn = (float)(((uint16_t)w.s >> 8) & 0xFF);
+        return a.D * ((w.dd.x * sc) * (float)i - (w.dd.y * mn) * (float)a.S);
+    }
+};
+
+// ---- q5_K arm: the q4_K block term with a fifth code bit ----
+struct Q5 {
+    using Act = Q4::Act;
+    struct W {
+        uint4 L;
+        uint32_t h;     // bit 8*i + g: fifth bit of the i-th weight of nibble group g
+        int16_t s;      // sc | m << 8
+        f2v dd;         // d, dmin
+    };
+    static __device__ __forceinline__ Act act(const MvArgs& g, int b) { return Q4::act(g, b); }
+    static __device__ __forceinline__ W load(const MvArgs& g, int64_t o, int b, int nb, int nsb) {
+        W w;
+        const int64_t i = o * nb + b;
+        w.L = nt_load(g.ql + i);
+        w.h = __builtin_nontemporal_load(g.h5 + i);
+        w.s = __builtin_nontemporal_load(g.sc + i);
+        w.dd = __builtin_nontemporal_load(reinterpret_cast<const f2v*>(g.dv) + o * nsb + (b >> 3));
+        return w;
+    }
+    static __device__ __forceinline__ float term(const Act& a, const W& w) {
+        const uint32_t m4 = 0x0F0F0F0Fu, m5 = 0x10101010u;
+        const uint4 L = w.L;
+        const uint32_t h = w.h;
+        // nibble group g takes bit g of each byte of h into bit 4
+        int i = dot4((L.x & m4) | ((h << 4) & m5), a.q0.x, 0);
+        i = dot4(((L.x >> 4) & m4) | ((h << 3) & m5), a.q0.y, i);
+        i = dot4((L.y & m4) | ((h << 2) & m5), a.q0.z, i);
+        i = dot4(((L.y >> 4) & m4) | ((h << 1) & m5), a.q0.w, i);
+        i = dot4((L.z & m4) | (h & m5), a.q1.x, i);
+        i = dot4(((L.z >> 4) & m4) | ((h >> 1) & m5), a.q1.y, i);
+        i = dot4((L.w & m4) | ((h >> 2) & m5), a.q1.z, i);
+        i = dot4(((L.w >> 4) & m4) | ((h >> 3) & m5), a.q1.w, i);
         const float sc = (float)(w.s & 0xFF);
         const float mn = (float)(((uint16_t)w.s >> 8) & 0xFF);
         return a.D * ((w.dd.x * sc) * (float)i - (w.dd.y * mn) * (float)a.S);
@@ -403,6 +444,7 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     MvArgs g;
     g.ql = w.gv_ql;
     g.qh = w.gv_qh;
+    g.h5 = w.gv_h5;
     g.sc = w.gv_sc;
     g.dv = w.gv_d;
     g.Q = pl.q;
@@ -457,6 +499,7 @@ hipError_t launch_mmvqn(const WeightDev& w, const PlaneView& pl, int64_t n, floa
     MvArgs g;
     g.ql = w.gv_ql;
     g.qh = w.gv_qh;
+    g.h5 = w.gv_h5;
     g.sc = w.gv_sc;
     g.dv = w.gv_d;
     g.Q = pl.q;
@@ -500,6 +543,11 @@ hipError_t launch_mmvq_q6k(const WeightDev& w, const PlaneView& pl, float* out,
 hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s) {
     return launch_mmvq<Q4>(w, pl, out, s);
+}
+
+hipError_t launch_mmvq_q5k(const WeightDev& w, const PlaneView& pl, float* out,
+                           hipStream_t s) {
+    return launch_mmvq<Q5>(w, pl, out, s);
 }
 
 }  // namespace mmq

@@ -10,6 +10,11 @@
 // Superblock formats (public GGUF K-quants, 256 weights each):
 //   q4_K, 144 B: f16 d | f16 dmin | 12 B packed 6-bit (scale, min) x 8 | 128 B
 //                4-bit quants; w = d*sc_j*q - dmin*m_j, j = sub-block of 32.
+//   q5_K, 176 B: f16 d | f16 dmin | 12 B scales (as q4_K) | qh[32] | qs[128]
+//                low nibbles (arranged as the q4_K quants); the fifth bit of
+//                element 64*g + l (l < 32) is bit 2g of qh[l], that of
+//                element 64*g + 32 + l bit 2g+1; w = d*sc_j*q - dmin*m_j,
+//                q in [0, 31];
 //   q6_K, 210 B: ql[128] | qh[64] | int8 scales[16] | f16 d;
 //                w = d*sc[e/16]*(q - 32), q in [0, 63].
 //
@@ -39,6 +44,11 @@
 //   ql[o][b]  uint4: the 4-bit codes, same byte order as the q6_K low nibbles
 //   sc[o][b]  int16: sc_j | m_j << 8
 //   d[o][sb]  f32 pair: d, dmin
+// One-token GEMV tiles (q5_K): ql, sc and d as for q4_K (ql holds the low
+// nibbles), plus
+//   h5[o][b]  uint32: bit 8*i + g = fifth bit of w_{4g+i} (g = 0..7,
+//             i = 0..3), so the bits of the 4 weights that one dot4 takes
+//             from a nibble group g sit at bit g of each byte
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -65,6 +75,14 @@ __device__ __forceinline__ void q4k_decode(const uint8_t* blk, float& d, float& 
 __device__ __forceinline__ int q4k_quant(const uint8_t* blk, int e) {
     const uint8_t byte = blk[16 + 32 * (e / 64) + (e % 32)];
     return (e % 64) < 32 ? (byte & 15) : (byte >> 4);
+}
+
+__device__ __forceinline__ int q5k_quant(const uint8_t* blk, int e) {
+    const int g = e / 64, i = e % 64;
+    const uint8_t byte = blk[48 + 32 * g + (i % 32)];
+    const int lo = i < 32 ? (byte & 15) : (byte >> 4);
+    const int hi = (blk[16 + (i % 32)] >> (2 * g + (i >= 32 ? 1 : 0))) & 1;
+    return lo | (hi << 4);
 }
 
 __device__ __forceinline__ int q6k_quant(const uint8_t* blk, int e) {
@@ -215,6 +233,40 @@ __global__ void k_repack_q4k_gemv(const uint8_t* __restrict__ raw, int64_t rows,
     }
 }
 
+__global__ void k_repack_q5k_gemv(const uint8_t* __restrict__ raw, int64_t rows, int64_t cols,
+                                  uint4* __restrict__ ql, uint32_t* __restrict__ h5,
+                                  int16_t* __restrict__ scv, float* __restrict__ dv) {
+    const int64_t nsb = cols / kSuper;
+    const int64_t nb = cols / kBlock;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nsb) return;
+    const int64_t o = idx / nsb, sb = idx % nsb;
+    const uint8_t* blk = raw + idx * 176;
+    float d, dmin;
+    int sc[8], mn[8];
+    q4k_decode(blk, d, dmin, sc, mn);   // the header has the q4_K layout
+    dv[2 * (o * nsb + sb)] = d;
+    dv[2 * (o * nsb + sb) + 1] = dmin;
+    for (int j = 0; j < 8; ++j) {
+        uint32_t L[4];
+        for (int u = 0; u < 4; ++u) {
+            uint32_t v = 0;
+            for (int i = 0; i < 4; ++i)
+                v |= (uint32_t)((q5k_quant(blk, 32 * j + 8 * u + i) & 15) |
+                                ((q5k_quant(blk, 32 * j + 8 * u + i + 4) & 15) << 4)) << (8 * i);
+            L[u] = v;
+        }
+        uint32_t H = 0;
+        for (int g = 0; g < 8; ++g)
+            for (int i = 0; i < 4; ++i)
+                H |= (uint32_t)(q5k_quant(blk, 32 * j + 4 * g + i) >> 4) << (8 * i + g);
+        const int64_t b = sb * 8 + j;
+        ql[o * nb + b] = make_uint4(L[0], L[1], L[2], L[3]);
+        h5[o * nb + b] = H;
+        scv[o * nb + b] = (int16_t)((uint16_t)sc[j] | ((uint16_t)mn[j] << 8));
+    }
+}
+
 }  // namespace
 
 hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s) {
@@ -235,6 +287,9 @@ hipError_t launch_repack_gemv(const uint8_t* raw_dev, const WeightDev& w, hipStr
     if (w.type == 12)
         hipLaunchKernelGGL(k_repack_q4k_gemv, grid, block, 0, s, raw_dev, w.rows, w.cols, w.gv_ql,
                            w.gv_sc, w.gv_d);
+    else if (w.type == 13)
+        hipLaunchKernelGGL(k_repack_q5k_gemv, grid, block, 0, s, raw_dev, w.rows, w.cols, w.gv_ql,
+                           w.gv_h5, w.gv_sc, w.gv_d);
     else
         hipLaunchKernelGGL(k_repack_q6k_gemv, grid, block, 0, s, raw_dev, w.rows, w.cols, w.gv_ql,
                            w.gv_qh, w.gv_sc, w.gv_d);

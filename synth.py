@@ -14,6 +14,8 @@ available):
     0..255 (so every 6-bit scale/min and 4-bit quant is uniform);
   * q6_K (210 B per 256 weights): the 128 ql bytes, 64 qh bytes and 16
     int8 sub-scales uniform over all byte values, f16 d from U(1e-3, 1e-2);
+  * q5_K (176 B per 256 weights): as q4_K, with the 32 fifth-bit bytes
+    uniform too (every 5-bit quant uniform);
   * activations ~ N(0, 1) f32; RMSNorm weight ~ U(0.5, 1.5); eps = 1e-6.
 """
 from __future__ import annotations
@@ -23,6 +25,7 @@ import zlib
 import numpy as np
 
 Q4K_BYTES = 144
+Q5K_BYTES = 176
 Q6K_BYTES = 210
 EPS = 1e-6
 
@@ -60,6 +63,16 @@ def q4k_weights(rng: np.random.Generator, od: int, id_: int) -> np.ndarray:
     return raw.reshape(od, (id_ // 256) * Q4K_BYTES)
 
 
+def q5k_weights(rng: np.random.Generator, od: int, id_: int) -> np.ndarray:
+    """Raw q5_K superblocks, row-major [od][id/256], returned as uint8 [od, id/256*176]."""
+    assert id_ % 256 == 0
+    nsb = od * (id_ // 256)
+    raw = _uniform_bytes(rng, nsb * Q5K_BYTES).reshape(nsb, Q5K_BYTES)
+    raw[:, 0:2] = _f16_bytes(rng, nsb)   # d
+    raw[:, 2:4] = _f16_bytes(rng, nsb)   # dmin
+    return raw.reshape(od, (id_ // 256) * Q5K_BYTES)
+
+
 def q6k_weights(rng: np.random.Generator, od: int, id_: int) -> np.ndarray:
     """Raw q6_K superblocks, row-major [od][id/256], returned as uint8 [od, id/256*210]."""
     assert id_ % 256 == 0
@@ -70,7 +83,7 @@ def q6k_weights(rng: np.random.Generator, od: int, id_: int) -> np.ndarray:
 
 
 def weights(wtype: str, rng: np.random.Generator, od: int, id_: int) -> np.ndarray:
-    return q4k_weights(rng, od, id_) if wtype == "q4_K" else q6k_weights(rng, od, id_)
+    return {"q4_K": q4k_weights, "q5_K": q5k_weights, "q6_K": q6k_weights}[wtype](rng, od, id_)
 
 
 def activations(rng: np.random.Generator, n: int, d: int) -> np.ndarray:

@@ -83,7 +83,7 @@ def ctx():
 
 
 def _w(ctx, wtype=mmq.MMQ_Q4_K, rows=512, cols=256, uses=0):
-    bpb = 144 if wtype == mmq.MMQ_Q4_K else 210
+    bpb = {mmq.MMQ_Q4_K: 144, mmq.MMQ_Q5_K: 176, mmq.MMQ_Q6_K: 210}[wtype]
     raw = np.zeros(rows * cols // 256 * bpb, np.uint8)
     return mmq.mmq_register_weight(ctx, wtype, rows, cols, raw, uses)
 
@@ -113,7 +113,7 @@ def test_shape_and_argument_validation(ctx):
 
 def test_registration_validation(ctx):
     raw = np.zeros(144 * 4, np.uint8)
-    assert _status(mmq.mmq_register_weight, ctx, 13, 4, 256, raw) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmq_register_weight, ctx, 11, 4, 256, raw) == mmq.MMQ_E_TYPE
     assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 300, raw) == mmq.MMQ_E_SHAPE
     assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 0, 256, raw) == mmq.MMQ_E_SHAPE
     assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw, 0x4) == mmq.MMQ_E_ARG
@@ -135,6 +135,34 @@ def test_registration_validation(ctx):
     mmq.mmq_weight_free(w4)
     assert mmq.mmq_stats(ctx)["weight_bytes"] == mmq.mmq_weight_bytes(w6)
     mmq.mmq_weight_free(w6)
+
+
+def test_q5k_is_a_decode_only_type(ctx):
+    raw = np.zeros(176 * 4, np.uint8)
+    # no matmul tiles for q5_K: asking for them is a type error, before any allocation
+    for uses in (mmq.MMQ_USE_GEMM, mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV):
+        assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q5_K, 4, 256, raw, uses) == mmq.MMQ_E_TYPE
+    assert mmq.mmq_stats(ctx)["weight_bytes"] == 0
+    # default uses = the GEMV: 16 B of low nibbles + 4 B of fifth bits + 2 B (sc, m) per 32
+    # weights, (d, dmin) per 256
+    w5 = _w(ctx, mmq.MMQ_Q5_K, 300, 512)
+    assert mmq.mmq_weight_bytes(w5) == 300 * 16 * (16 + 4 + 2) + 300 * 2 * 8
+    w4 = _w(ctx, mmq.MMQ_Q4_K, 64, 512, mmq.MMQ_USE_GEMV)
+    A, O = 0x100000, 0x200000
+    assert _status(mmq.mmq_gemm_q4k, ctx, w5, A, 8, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmq_gemm_q6k, ctx, w5, A, 8, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmvq_q4k, ctx, w5, A, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmvq_q6k, ctx, w5, A, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmvq_q5k, ctx, w4, A, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmvq_q5k, ctx, w5, A + 4, O) == mmq.MMQ_E_ARG
+    assert _status(mmq.mmvq_q5k, ctx, w5, A, O) == mmq.MMQ_OK
+    st = mmq.mmq_stats(ctx)
+    assert st["launches_mmvq_q5k"] == 1 and st["launches_mmvq_q4k"] == 0
+    assert st["cache_misses"] == 1      # the activation was quantised standalone
+    with pytest.raises(ValueError):     # the binding checks 176 B per superblock
+        mmq.mmq_register_weight(ctx, mmq.MMQ_Q5_K, 4, 256, np.zeros(144 * 4, np.uint8))
+    mmq.mmq_weight_free(w5)
+    mmq.mmq_weight_free(w4)
 
 
 def test_consumer_type_checks(ctx):

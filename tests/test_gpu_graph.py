@@ -93,7 +93,7 @@ def test_chain_graph_replays_equal_eager():
         assert census == {"launches_quant_rms": 2 * LAYERS, "launches_quant_swiglu": LAYERS,
                           "launches_quant_f32": LAYERS, "launches_gemm_q4k": 5 * LAYERS,
                           "launches_gemm_q6k": 2 * LAYERS, "launches_mmvq_q6k": 0,
-                          "launches_mmvq_q4k": 0}, census
+                          "launches_mmvq_q4k": 0, "launches_mmvq_q5k": 0}, census
         assert st1["cache_hits"] - st0["cache_hits"] == 7 * LAYERS
         assert st1["cache_misses"] - st0["cache_misses"] == 0
         for rep in range(1, 4):

@@ -318,6 +318,42 @@ def test_mmvq_q4k_parity(ctx, od, id_):
     mmq.mmq_weight_free(w)
 
 
+@pytest.mark.parametrize("od,id_", GEMV_SHAPES + [(5120, 13824), (13824, 5120)])
+def test_mmvq_q5k_parity(ctx, od, id_):
+    rng = synth.rng_for("test", od, f"mmvq5{id_}")
+    raw = synth.q5k_weights(rng, od, id_)
+    w = mmq.mmq_register_weight(ctx, mmq.MMQ_Q5_K, od, id_, raw, 0)
+    ah = _act("mmvq5", 1, id_)
+    a = dev_tensor(ah)
+    out = torch.full((od,), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmvq_q5k(ctx, w, a, out)
+    q, D, S = export_plane(ctx, a, 1, id_)
+    ref = oracle.gemm("q5_K", q, D, S, raw, od, id_)[0]
+    assert_gemm_close(out.cpu().numpy(), ref, f"mmvq q5_K {od}x{id_}")
+    assert mmq.mmq_stats(ctx)["launches_mmvq_q5k"] >= 1
+    mmq.mmq_weight_free(w)
+
+
+def test_mmvq_q5k_extreme_codes(ctx):
+    """Every code at 31 (all fifth bits set) and at 0, with sub-scales and mins
+    at 63: the fifth bit carries weight 16 in every nibble group."""
+    od, id_ = 96, 1024
+    raw = synth.q5k_weights(synth.rng_for("test", od, "mmvq5x"), od, id_).reshape(od, -1, 176)
+    raw[:, :, 4:16] = 0xFF                      # every 6-bit scale and min = 63
+    raw[: od // 2, :, 16:176] = 0xFF            # rows 0..47: every code 31
+    raw[od // 2:, :, 16:176] = 0x00             # rows 48..95: every code 0
+    raw = np.ascontiguousarray(raw.reshape(od, -1))
+    w = mmq.mmq_register_weight(ctx, mmq.MMQ_Q5_K, od, id_, raw, 0)
+    ah = _act("mmvq5x", 1, id_)
+    a = dev_tensor(ah)
+    out = torch.full((od,), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmvq_q5k(ctx, w, a, out)
+    q, D, S = export_plane(ctx, a, 1, id_)
+    ref = oracle.gemm("q5_K", q, D, S, raw, od, id_)[0]
+    assert_gemm_close(out.cpu().numpy(), ref, "mmvq q5_K extreme codes")
+    mmq.mmq_weight_free(w)
+
+
 @pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
 @pytest.mark.parametrize("n", [1, 3])
 def test_gemv_degenerate_activation_rows(ctx, wtype, n):
