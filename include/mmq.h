@@ -1,6 +1,6 @@
 /*
- * mmq.h -- C ABI of libmmq: q8-plane producers and q4_K / q6_K integer-dot
- * matmuls for gfx950 (MI355X).
+ * mmq.h -- C ABI of libmmq: q8-plane producers, q4_K / q6_K integer-dot
+ * matmuls and q4_K / q5_K / q6_K one-token GEMVs for gfx950 (MI355X).
  *
  * The operations follow three pages of the "minfer" CUDA optimisation log:
  *   [r52] "55 · r52 — skip-write mode 2: skipping the f32 intermediate write-out"
