@@ -382,9 +382,12 @@ def cpu_baseline(seconds: float):
 def measured_peaks(torch):
     """Ceilings measured on this device, beside the published peaks: the
     matrix pipe's rate for the f16 and int8 32x32 MFMA instructions (a
-    benchmark kernel of independent MFMA chains, libmmq_peak.so), a read-only
-    stream over 2 GiB (the same library) and the device-to-device copy rate
-    of a 1 GiB buffer (read + write bytes)."""
+    benchmark kernel of independent MFMA chains, libmmq_peak.so); the
+    matmul's per-block MFMA + rescale-FMA mix with no memory traffic (MFMAs
+    alone, FMAs alone and both; hidden_frac is the share of the shorter of
+    the two that running both together hides); a read-only stream over 2 GiB
+    (the same library) and the device-to-device copy rate of a 1 GiB buffer
+    (read + write bytes)."""
     import ctypes
     from quantized_matmul_rmsnorm_amd import build as _b
     lib = ctypes.CDLL(_b.LIB_PEAK)
@@ -411,6 +414,34 @@ def measured_peaks(torch):
         torch.cuda.synchronize()
         ops = 3 * blocks * 4 * iters * chains * ops_per_mfma
         res[name] = round(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    # the matmul's per-block mix (4 MFMAs + 32 rescale FMAs per wave, 2 waves
+    # per SIMD) without memory: MFMAs alone, FMAs alone, both
+    lib.mmq_peak_mix.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    lib.mmq_peak_mix.restype = ctypes.c_int
+    mblocks, miters = n_cu, 2048
+    mout = torch.empty(mblocks * 512, dtype=torch.float32, device="cuda")
+    mix_ms = []
+    for mode in (0, 1, 2):
+        if lib.mmq_peak_mix(mout.data_ptr(), mblocks, miters, mode, stream.cuda_stream) != 0:
+            raise RuntimeError("instruction mix: launch failed")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            if lib.mmq_peak_mix(mout.data_ptr(), mblocks, miters, mode, stream.cuda_stream) != 0:
+                raise RuntimeError("instruction mix: launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        mix_ms.append(e0.elapsed_time(e1) / 3)
+    mix_ops = mblocks * 8 * miters * 8 * (2 * 32 * 32 * 16)
+    t_m, t_v, t_b = mix_ms
+    res["matmul_mix"] = {"mfma_only_ms": round(t_m, 4), "fma_only_ms": round(t_v, 4),
+                         "both_ms": round(t_b, 4),
+                         "both_TFLOPs": round(mix_ops / (t_b * 1e-3) / 1e12, 1),
+                         "both_frac_of_f16_peak": round(mix_ops / (t_b * 1e-3) / 1e12 / PEAK_F16_TOPS, 4),
+                         "hidden_frac": round((t_m + t_v - t_b) / min(t_m, t_v), 3)}
+    del mout
     lib.mmq_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_void_p]
     lib.mmq_peak_read.restype = ctypes.c_int

@@ -35,6 +35,19 @@ int mmq_peak_chains(void);
 int mmq_peak_mfma_f16(float* out, int blocks, int iters, hipStream_t stream);
 int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t stream);
 
+/* The matmul's per-block instruction mix with no memory traffic, in its
+ * launch shape (workgroups of 512 threads, 2 waves per SIMD): per 32-block
+ * each wave issues 4 f16 32x32x16 MFMAs (two output tiles, two K-steps) and
+ * the 32 FMAs of the previous block's rescale.  mode 0 issues the MFMAs only,
+ * 1 the FMAs only, 2 both in the matmul's order; comparing the three times
+ * shows how far the matrix pipe and the VALU overlap on this device.  A
+ * launch runs blocks * 8 * iters * 2 blocks of that mix: mode 0 and 2 perform
+ * blocks * 8 * iters * 8 * (2*32*32*16) f16 operations.  out: caller-owned
+ * device buffer of blocks * 512 floats; blocks >= 1, 1 <= iters <= 2^20.
+ * Returns 0, -1 for an invalid argument (nothing launched), or the HIP error
+ * code of the launch. */
+int mmq_peak_mix(float* out, int blocks, int iters, int mode, hipStream_t stream);
+
 /* Read-only HBM stream: reads `bytes` (a multiple of 16, > 0) of the device
  * buffer `src` once with 16-byte non-temporal loads, `blocks` workgroups of
  * 256 threads walking it grid-stride, and writes one folded value per thread

@@ -1,6 +1,7 @@
-// peak.hip -- measured ceilings on this device (matrix-core rates and a
-// read-only HBM stream), for the benchmark's roofline (a measurement aid; no
-// part of the matmul path).
+// peak.hip -- measured ceilings on this device (matrix-core rates, the
+// matmul's MFMA + rescale instruction mix without memory, and a read-only HBM
+// stream), for the benchmark's roofline (a measurement aid; no part of the
+// matmul path).
 //
 // Each wave keeps 8 independent accumulator chains and issues `iters` rounds
 // of one MFMA per chain, back to back, on operands held in registers: the
@@ -73,6 +74,66 @@ __global__ __launch_bounds__(256) void k_peak_i8(int* __restrict__ out, int iter
     out[(int64_t)blockIdx.x * blockDim.x + t] = s;
 }
 
+// The matmul's per-block instruction mix without memory traffic, in its
+// launch shape (512 threads: 2 waves per SIMD).  Per block each wave issues 4
+// MFMAs (two output tiles, two K-steps of 16, the first with C = 0 as the
+// matmul's block dot) into one X buffer and 32 FMAs (acc += s * X, the
+// per-block rescale) reading the X buffer of the previous block; the buffers
+// alternate.  MODE 0: MFMAs only; 1: FMAs only; 2: both, in the matmul's
+// order (the MFMAs of a block, then the FMAs of the one before).  The
+// operands change every round so nothing is hoisted.
+template <int MODE>
+__global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int iters, float s) {
+    const int t = threadIdx.x;
+    half8 a0, b0, a1, b1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a0[i] = (_Float16)((t + i) & 7);
+        b0[i] = (_Float16)((t * 3 + i) & 7);
+        a1[i] = (_Float16)((t + 2 * i) & 7);
+        b1[i] = (_Float16)((t * 5 + i) & 7);
+    }
+    f32x16 XA[2], XB[2], acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            XA[i][r] = (float)(r + i);
+            XB[i][r] = (float)(r - i);
+            acc[i][r] = 0.0f;
+        }
+    auto block = [&](f32x16* Xw, const f32x16* Xr) {
+        if constexpr (MODE != 1) {
+            Xw[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Xw[0], 0, 0, 0);
+            Xw[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Xw[1], 0, 0, 0);
+            Xw[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, a0, Xw[0], 0, 0, 0);
+            Xw[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, a1, Xw[1], 0, 0, 0);
+        }
+        if constexpr (MODE != 0) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(s, Xr[i][r], acc[i][r]);
+        }
+        if constexpr (MODE == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // the block's MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);   // then the rescale FMAs
+        }
+    };
+    for (int it = 0; it < iters; ++it) {
+        block(XA, XB);
+        block(XB, XA);
+        if constexpr (MODE == 1) {   // the FMAs' inputs change every round
+            XA[0][0] += 1.0f;
+            XB[1][0] -= 1.0f;
+        }
+    }
+    float v = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v += XA[0][r] + XA[1][r] + XB[0][r] + XB[1][r] + acc[0][r] + acc[1][r];
+    out[(int64_t)blockIdx.x * blockDim.x + t] = v;
+}
+
 // Read-only stream: each thread walks the buffer grid-stride in 16 B
 // non-temporal loads (4 in flight) and writes one folded value at the end.
 __global__ __launch_bounds__(256) void k_peak_read(const uint4* __restrict__ src, int64_t n16,
@@ -116,6 +177,18 @@ int mmq_peak_mfma_f16(float* out, int blocks, int iters, hipStream_t s) {
 int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t s) {
     if (out == nullptr || blocks < 1 || iters < 1 || iters > (1 << 20)) return -1;
     hipLaunchKernelGGL(k_peak_i8, dim3((unsigned)blocks), dim3(256), 0, s, out, iters);
+    return (int)hipGetLastError();
+}
+
+// out: device buffer of blocks * 512 floats; blocks >= 1, 1 <= iters <=
+// 1 << 20; mode 0, 1 or 2.  Returns 0, -1 for bad arguments, or the HIP error.
+int mmq_peak_mix(float* out, int blocks, int iters, int mode, hipStream_t s) {
+    if (out == nullptr || blocks < 1 || iters < 1 || iters > (1 << 20) || mode < 0 || mode > 2)
+        return -1;
+    const dim3 g((unsigned)blocks), b(512);
+    if (mode == 0) hipLaunchKernelGGL(k_peak_mix<0>, g, b, 0, s, out, iters, 0.999f);
+    else if (mode == 1) hipLaunchKernelGGL(k_peak_mix<1>, g, b, 0, s, out, iters, 0.999f);
+    else hipLaunchKernelGGL(k_peak_mix<2>, g, b, 0, s, out, iters, 0.999f);
     return (int)hipGetLastError();
 }
 

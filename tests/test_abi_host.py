@@ -44,7 +44,8 @@ def test_peak_library_exports_its_header():
     from quantized_matmul_rmsnorm_amd import build as _b
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mmq_peak.h")).read(), flags=re.S)
     declared = sorted(set(re.findall(r"\b(mmq\w+)\s*\(", text)))
-    assert declared == ["mmq_peak_chains", "mmq_peak_mfma_f16", "mmq_peak_mfma_i8", "mmq_peak_read"]
+    assert declared == ["mmq_peak_chains", "mmq_peak_mfma_f16", "mmq_peak_mfma_i8", "mmq_peak_mix",
+                        "mmq_peak_read"]
     out = subprocess.run(["nm", "-D", "--defined-only", _b.LIB_PEAK], capture_output=True,
                          text=True, check=True).stdout
     dyn = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -57,6 +58,14 @@ def test_peak_library_exports_its_header():
         assert fn(ctypes.c_void_p(0x1000), 0, 1, None) == -1
         assert fn(ctypes.c_void_p(0x1000), 1, 0, None) == -1
         assert fn(ctypes.c_void_p(0x1000), 1, (1 << 20) + 1, None) == -1
+    mix = lib.mmq_peak_mix
+    mix.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert mix(None, 1, 1, 0, None) == -1
+    assert mix(ctypes.c_void_p(0x1000), 0, 1, 0, None) == -1
+    assert mix(ctypes.c_void_p(0x1000), 1, 0, 0, None) == -1
+    assert mix(ctypes.c_void_p(0x1000), 1, (1 << 20) + 1, 0, None) == -1
+    assert mix(ctypes.c_void_p(0x1000), 1, 1, 3, None) == -1
+    assert mix(ctypes.c_void_p(0x1000), 1, 1, -1, None) == -1
     rd = lib.mmq_peak_read
     rd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     assert rd(None, 16, ctypes.c_void_p(0x1000), 1, None) == -1
