@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--small-n", action="store_true", help="add the small-n band sweep (us per call)")
+    p.add_argument("--decode-crossover", action="store_true",
+                   help="add the q6_K decode arm's path sweep over od x id (us per call)")
     p.add_argument("--f16-reference", action="store_true",
                    help="add a dense f16 GEMM of the gate shape through torch.matmul (context)")
     # one untimed device copy of this many MiB before the chain: the plain copy
@@ -255,6 +257,52 @@ def small_n_sweep(mmq, torch, synth):
             for w in ws:
                 mmq.mmq_weight_free(w)
     finally:
+        mmq.mmq_destroy(ctx)
+    return res
+
+
+def decode_crossover_sweep(mmq, torch, synth):
+    """The q6_K decode arm's two paths across od x id at one token: the
+    quantised GEMV from a written activation with no plane yet (standalone
+    quantise + GEMV, as the routed arm would run it), the same GEMV with the
+    plane already recorded, and the f32-activation GEMV (one launch, no
+    quantise).  us per call, captured-graph replays over rotated weight
+    copies; the f32 gate is the smallest od*id where the quantised route is
+    no slower."""
+    ctx = mmq.mmq_create(0, 0)
+    res = {}
+    try:
+        for id_ in (3584, 5120):
+            x = torch.from_numpy(synth.activations(synth.rng_for("crossover", id_, "x"), 1, id_)[0]).cuda()
+            for od in (256, 512, 1024, 2048, 4096, 8192, 16384):
+                raw = synth.q6k_weights(synth.rng_for("crossover", od, str(id_)), od, id_)
+                copies = max(2, min(128, int(400e6 // (od * id_ * 0.83))))
+                ws = [mmq.mmq_register_weight(ctx, mmq.MMQ_Q6_K, od, id_, raw, mmq.MMQ_USE_GEMV)
+                      for _ in range(copies)]
+                out = torch.empty((od,), dtype=torch.float32, device="cuda")
+                reps = 2 * copies
+
+                def miss(i):
+                    mmq.mmq_cache_clear(ctx)   # host bookkeeping only: every call quantises x
+                    mmq.mmvq_q6k(ctx, ws[i % copies], x, out)
+
+                miss(0)
+                torch.cuda.synchronize()
+                t_miss = _graph_time_us(torch, miss, reps)
+                mmq.mmq_cache_clear(ctx)
+                mmq.mmq_quant_f32(ctx, x, 1, id_)
+                t_hit = _graph_time_us(torch, lambda i: mmq.mmvq_q6k(ctx, ws[i % copies], x, out), reps)
+                mmq.mmq_cache_clear(ctx)
+                mmq.mmq_gemv_q6k_f32(ctx, ws[0], x, out)
+                torch.cuda.synchronize()
+                t_f32 = _graph_time_us(torch, lambda i: mmq.mmq_gemv_q6k_f32(ctx, ws[i % copies], x, out),
+                                       reps)
+                res[f"{od}x{id_}"] = {"od_id": od * id_, "quantise+gemv": round(t_miss, 2),
+                                      "gemv_on_plane": round(t_hit, 2), "f32_gemv": round(t_f32, 2)}
+                for w in ws:
+                    mmq.mmq_weight_free(w)
+    finally:
+        mmq.mmq_cache_clear(ctx)
         mmq.mmq_destroy(ctx)
     return res
 
@@ -629,6 +677,7 @@ def main():
         decode["aggregate_frac_measured_copy"] = round(decode["aggregate_GB_s"] / peaks["hbm_copy_GB_s"], 4)
         decode["aggregate_frac_measured_read"] = round(decode["aggregate_GB_s"] / peaks["hbm_read_GB_s"], 4)
     small = small_n_sweep(mmq, torch, synth) if args.small_n else None
+    crossover = decode_crossover_sweep(mmq, torch, synth) if args.decode_crossover else None
     f16ref = f16_reference(torch) if args.f16_reference else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
@@ -668,6 +717,7 @@ def main():
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
         "decode_gemv": decode,
         "small_n_us": small,
+        "decode_crossover_us": crossover,
         "f16_gemm_reference": f16ref,
         "cpu_baseline": cpu,
     }

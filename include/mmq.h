@@ -108,6 +108,7 @@ typedef struct mmq_stats_t {
     int64_t unfused_fallbacks;      /* MMQ_WRITE_AUTO producers without plane memory      */
     int64_t small_n_gemv;           /* matmul calls served by the few-token GEMV path     */
     int64_t launches_mmvq_q5k;
+    int64_t launches_gemv_f32;      /* q6_K GEMVs on an f32 activation (no plane) */
 } mmq_stats_t;
 
 /* ---- context ----------------------------------------------------------- */
@@ -222,6 +223,32 @@ int mmvq_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
  * a, out and the errors as for mmvq_q6k. */
 int mmvq_q5k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
              void* stream);
+
+/* One-token q6_K GEMV on the f32 activation itself, with no plane
+ * [d37 2b and Excerpt A: below an od*id gate the q6_K decode arm runs a
+ * kernel on the f32 activation; above it, the quantised GEMV].
+ * out[o] = sum_k w[o][k] * x[k] for o < rows, w the dequantised weight, in
+ * f32 arithmetic (the activation is not rounded to q8).  x: f32 [cols],
+ * written (a dead key is refused with MMQ_E_DEAD_WRITE); it is neither
+ * quantised nor recorded in the cache.  w must be q6_K registered with
+ * MMQ_USE_GEMV; cols <= 16384 (MMQ_E_SHAPE otherwise).  Errors as for
+ * mmvq_q6k. */
+int mmq_gemv_q6k_f32(mmq_ctx* ctx, const mmq_weight* w, const float* x, float* out,
+                     void* stream);
+
+/* The routed one-token q6_K decode arm [d37 Excerpt A]: the f32-activation
+ * GEMV when rows * cols < MMQ_DECODE_F32_GATE, cols <= 16384, x has no
+ * recorded plane and is not a dead key; otherwise mmvq_q6k (which consults
+ * the cache and quantises x on a miss).  The gate is the crossover measured
+ * on MI355X between the f32 GEMV and a standalone quantise + quantised GEMV
+ * (the pages' constants, 24M then 4M, were fitted on their GPU; the 4M also
+ * counts on a second consumer sharing the quantise).  A caller whose
+ * activation feeds further quantised consumers can call mmvq_q6k directly so
+ * that the plane is recorded and shared.  Counted under launches_gemv_f32 or
+ * launches_mmvq_q6k. */
+#define MMQ_DECODE_F32_GATE 20000000LL
+int mmq_decode_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* x, float* out,
+                   void* stream);
 
 /* ---- consumer set [r60 3.2-3.3: the registration-time nb_bt_only flag] -- */
 

@@ -1,4 +1,5 @@
-"""CPU oracle for the q8-plane producers and the q4_K / q5_K / q6_K matmuls.
+"""CPU oracle for the q8-plane producers, the q4_K / q5_K / q6_K matmuls and
+the f32-activation q6_K GEMV.
 
 TEST INFRASTRUCTURE ONLY: tests/, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package; the product
@@ -118,6 +119,17 @@ def dequant(wtype: str, raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
           "q6_K": _load().oracle_dequant_q6k}[wtype]
     fn(_p(raw), rows, cols, _p(w))
     return w
+
+
+def gemv_f32(wtype: str, raw: np.ndarray, rows: int, cols: int, x: np.ndarray) -> np.ndarray:
+    """out[o] = sum_k w[o][k] * x[k] in f64, w the dequantised weight and x the
+    f32 activation as given (not quantised): what the decode arm computes on
+    its f32-activation path below the shape gate ("72 · D3-7 ...", section 2,
+    Excerpt A).  The plain definition: the f64 dequantisation above, then one
+    matrix-vector product."""
+    x = np.ascontiguousarray(x, np.float32).astype(np.float64)
+    assert x.shape == (cols,)
+    return dequant(wtype, raw, rows, cols) @ x
 
 
 def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:

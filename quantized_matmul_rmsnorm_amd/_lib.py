@@ -46,6 +46,7 @@ EXPORTS = [
     "mmq_register_weight", "mmq_weight_free", "mmq_weight_bytes",
     "mmq_quant_rms", "mmq_quant_swiglu", "mmq_quant_f32",
     "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k",
+    "mmq_gemv_q6k_f32", "mmq_decode_q6k",
     "mmq_register_foreign_consumer", "mmq_plane_only",
     "mmq_cache_clear", "mmq_cache_invalidate", "mmq_plane_export", "mmq_stats",
 ]
@@ -63,7 +64,7 @@ class mmq_stats_t(ctypes.Structure):
         "launches_gemm_q4k", "launches_gemm_q6k", "launches_mmvq_q6k",
         "cache_hits", "cache_misses", "cache_refusals", "cache_entries",
         "plane_bytes", "weight_bytes", "launches_mmvq_q4k", "degraded_writes",
-        "unfused_fallbacks", "small_n_gemv", "launches_mmvq_q5k")]
+        "unfused_fallbacks", "small_n_gemv", "launches_mmvq_q5k", "launches_gemv_f32")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -102,6 +103,8 @@ def _load():
         "mmvq_q6k": (I, [P, P, P, P, P]),
         "mmvq_q4k": (I, [P, P, P, P, P]),
         "mmvq_q5k": (I, [P, P, P, P, P]),
+        "mmq_gemv_q6k_f32": (I, [P, P, P, P, P]),
+        "mmq_decode_q6k": (I, [P, P, P, P, P]),
         "mmq_register_foreign_consumer": (I, [P, I]),
         "mmq_plane_only": (I, [P]),
         "mmq_cache_clear": (None, [P]),
@@ -245,6 +248,19 @@ def mmvq_q6k(ctx, w, a, out, stream=None):
 def mmvq_q4k(ctx, w, a, out, stream=None):
     f = _f32() if not isinstance(a, int) else None
     return _check(lib.mmvq_q4k(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
+
+
+def mmq_gemv_q6k_f32(ctx, w, x, out, stream=None):
+    f = _f32() if not isinstance(x, int) else None
+    return _check(lib.mmq_gemv_q6k_f32(ctx, w, _ptr(x, f), _ptr(out, f), _stream(stream)))
+
+
+def mmq_decode_q6k(ctx, w, x, out, stream=None):
+    f = _f32() if not isinstance(x, int) else None
+    return _check(lib.mmq_decode_q6k(ctx, w, _ptr(x, f), _ptr(out, f), _stream(stream)))
+
+
+MMQ_DECODE_F32_GATE = 20_000_000
 
 
 def mmvq_q5k(ctx, w, a, out, stream=None):

@@ -692,6 +692,37 @@ int mmvq_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     return after_launch(c, launch_mmvq_q4k(w->w, pl, out, s), s, who);
 }
 
+int mmq_gemv_q6k_f32(mmq_ctx* c, const mmq_weight* w, const float* x, float* out,
+                     void* stream) {
+    const char* who = "mmq_gemv_q6k_f32";
+    int rc = consume_check(c, w, x, 1, out, MMQ_Q6_K, MMQ_USE_GEMV, who);
+    if (rc) return rc;
+    if (w->w.cols > kGemvF32MaxCols)
+        return fail(MMQ_E_SHAPE, "%s: cols=%lld exceeds %lld (x is staged whole in LDS)", who,
+                    (long long)w->w.cols, (long long)kGemvF32MaxCols);
+    // the kernel reads x itself: a buffer a skip-write producer never wrote is refused
+    if (overlaps_dead(c, x, w->w.cols * 4)) return refuse_dead(c, who, x);
+    if ((rc = use_device(c))) return rc;
+    c->st.launches_gemv_f32++;
+    if (c->dry) return MMQ_OK;
+    hipStream_t s = (hipStream_t)stream;
+    return after_launch(c, launch_gemv_f32_q6k(w->w, x, out, s), s, who);
+}
+
+int mmq_decode_q6k(mmq_ctx* c, const mmq_weight* w, const float* x, float* out, void* stream) {
+    const char* who = "mmq_decode_q6k";
+    int rc = consume_check(c, w, x, 1, out, MMQ_Q6_K, MMQ_USE_GEMV, who);
+    if (rc) return rc;
+    // The f32 path only where it is cheaper (small od*id) and possible: x was
+    // written (not a dead key) and has no plane yet (a recorded plane makes
+    // the GEMV free of its quantise).
+    const int64_t od = w->w.rows, id = w->w.cols;
+    if (od * id < MMQ_DECODE_F32_GATE && id <= kGemvF32MaxCols && find_entry(c, x, 1, id) < 0 &&
+        !overlaps_dead(c, x, id * 4))
+        return mmq_gemv_q6k_f32(c, w, x, out, stream);
+    return mmvq_q6k(c, w, x, out, stream);
+}
+
 int mmvq_q5k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* stream) {
     const char* who = "mmvq_q5k";
     int rc = consume_check(c, w, a, 1, out, MMQ_Q5_K, MMQ_USE_GEMV, who);

@@ -83,6 +83,9 @@ hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
 hipError_t launch_mmvq_q5k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s);
+// q6_K GEMV on the f32 activation x [cols] (no plane): out [rows].
+constexpr int64_t kGemvF32MaxCols = 16384;   // x is staged whole in 64 KiB of LDS
+hipError_t launch_gemv_f32_q6k(const WeightDev& w, const float* x, float* out, hipStream_t s);
 // A few tokens at once over the GEMV tiles (out [n][rows]); used when the n
 // tokens' plane fits the LDS in one pass.
 int mmvqn_supported(int64_t cols, int64_t n);

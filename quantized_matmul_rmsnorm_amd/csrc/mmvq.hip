@@ -1,4 +1,5 @@
-// mmvq.hip -- one-token q6_K / q4_K / q5_K GEMV over a q8 activation plane (gfx950).
+// mmvq.hip -- one-token q6_K / q4_K / q5_K GEMV over a q8 activation plane, and
+// the q6_K GEMV on an f32 activation for small shapes (gfx950).
 //
 // Method ("72 · D3-7 ...", section 2 and Excerpts A, A2, B): at one token the
 // matmul is a weight-streaming GEMV; the activation is quantised once into a
@@ -518,6 +519,59 @@ hipError_t launch_mmvqn(const WeightDev& w, const PlaneView& pl, int64_t n, floa
     return hipSuccess;
 }
 
+// ---- f32-activation q6_K GEMV: the decode arm's path for small shapes ----
+// ("72 · D3-7 ...", section 2 and Excerpt A: below an od*id gate the q6_K
+// decode arm runs a kernel on the f32 activation instead of quantising it.)
+// out[o] = sum_k w[o][k] * x[k] with w dequantised in f32 from the GEMV tiles:
+// per 32-block and 16-value half h, (d * sc_h) * sum (q - 32) * x.  Every
+// (q - 32) and d * sc_h is exact in f32, so only the products and sums round.
+// x (id floats) is staged once per workgroup in LDS; each wave takes rows
+// grid-stride and lane l owns 32-blocks l, l + 64, ...
+__global__ __launch_bounds__(256) void k_gemv_f32_q6(const MvArgs g, const float* __restrict__ x) {
+    extern __shared__ float4 sx[];   // [id / 4]
+    const int id = g.id, od = g.od;
+    const int nb = id / kBlock, nsb = id / kSuper;
+    for (int i = threadIdx.x; i < id / 4; i += blockDim.x)
+        sx[i] = reinterpret_cast<const float4*>(x)[i];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * 4;
+    const uint32_t m4 = 0x0F0F0F0Fu, m2 = 0x30303030u;
+    for (int o = wave; o < od; o += nwaves) {
+        float acc = 0.0f;
+        for (int b = lane; b < nb; b += 64) {
+            const int64_t i = (int64_t)o * nb + b;
+            const uint4 L = nt_load(g.ql + i);
+            const uint2 H = nt_load(g.qh + i);
+            const int16_t sc = __builtin_nontemporal_load(g.sc + i);
+            const float d = __builtin_nontemporal_load(g.dv + (int64_t)o * nsb + (b >> 3));
+            // word w holds the 6-bit codes of values 4w .. 4w+3, one per byte
+            const uint32_t c[8] = {(L.x & m4) | ((H.x << 4) & m2), ((L.x >> 4) & m4) | ((H.x << 2) & m2),
+                                   (L.y & m4) | (H.x & m2),        ((L.y >> 4) & m4) | ((H.x >> 2) & m2),
+                                   (L.z & m4) | ((H.y << 4) & m2), ((L.z >> 4) & m4) | ((H.y << 2) & m2),
+                                   (L.w & m4) | (H.y & m2),        ((L.w >> 4) & m4) | ((H.y >> 2) & m2)};
+            const float4* xb = sx + (int64_t)b * 8;
+            float h[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const float4 xv = xb[w];
+                float& hs = h[w >> 2];
+                hs = fmaf((float)(c[w] & 0xFF) - 32.0f, xv.x, hs);
+                hs = fmaf((float)((c[w] >> 8) & 0xFF) - 32.0f, xv.y, hs);
+                hs = fmaf((float)((c[w] >> 16) & 0xFF) - 32.0f, xv.z, hs);
+                hs = fmaf((float)(c[w] >> 24) - 32.0f, xv.w, hs);
+            }
+            const float s0 = d * (float)(int)(int8_t)(sc & 0xFF);
+            const float s1 = d * (float)(int)(int8_t)((uint16_t)sc >> 8);
+            acc = fmaf(s0, h[0], acc);
+            acc = fmaf(s1, h[1], acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) g.out[o] = acc;
+    }
+}
+
 }  // namespace
 
 // The GEMV path pays off while one pass holds all n tokens (each further
@@ -548,6 +602,42 @@ hipError_t launch_mmvq_q4k(const WeightDev& w, const PlaneView& pl, float* out,
 hipError_t launch_mmvq_q5k(const WeightDev& w, const PlaneView& pl, float* out,
                            hipStream_t s) {
     return launch_mmvq<Q5>(w, pl, out, s);
+}
+
+// The f32-activation q6_K GEMV: one launch, x read once per workgroup into
+// LDS (cols <= kGemvF32MaxCols, so it fits the default 64 KiB).  Grid: a wave
+// per row while the rows fit two rounds of resident waves, else exactly the
+// resident waves.
+hipError_t launch_gemv_f32_q6k(const WeightDev& w, const float* x, float* out, hipStream_t s) {
+    if (w.cols > kGemvF32MaxCols || w.cols % kSuper != 0) return hipErrorInvalidValue;
+    MvArgs g{};
+    g.ql = w.gv_ql;
+    g.qh = w.gv_qh;
+    g.sc = w.gv_sc;
+    g.dv = w.gv_d;
+    g.id = (int)w.cols;
+    g.od = (int)w.rows;
+    g.out = out;
+    const size_t lds = (size_t)w.cols * 4;
+    static int per_cu = -1, n_cu = 0;
+    if (per_cu < 0) {
+        int dev = 0, blk = 0;
+        (void)hipFuncSetAttribute((const void*)k_gemv_f32_q6,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(kGemvF32MaxCols * 4));
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_gemv_f32_q6, 256,
+                                                         (size_t)kGemvF32MaxCols * 4) != hipSuccess)
+            blk = 1;
+        per_cu = blk > 0 ? blk : 1;
+        if (n_cu <= 0) n_cu = 256;
+    }
+    const int64_t resident = (int64_t)per_cu * n_cu;
+    const int64_t want = (w.rows + 3) / 4;
+    const int64_t grid = want <= 2 * resident ? want : resident;
+    hipLaunchKernelGGL(k_gemv_f32_q6, dim3((unsigned)grid), dim3(256), lds, s, g, x);
+    return hipGetLastError();
 }
 
 }  // namespace mmq

@@ -174,6 +174,65 @@ def test_q5k_is_a_decode_only_type(ctx):
     mmq.mmq_weight_free(w4)
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    for name in ("MMQ_Q4_K", "MMQ_Q5_K", "MMQ_Q6_K", "MMQ_USE_GEMM", "MMQ_USE_GEMV",
+                 "MMQ_DECODE_F32_GATE", "MMQ_PLANE_ROWS"):
+        m = re.search(rf"#define {name}\s+\(?(-?\d+)", text)
+        assert m, name
+        assert int(m.group(1)) == getattr(mmq, name), name
+
+
+def test_decode_q6k_routing(ctx):
+    """The routed q6_K decode arm takes the f32-activation GEMV only below the
+    od*id gate, for a written activation with no recorded plane; otherwise
+    the quantised GEMV (which quantises on a miss and hits a recorded plane)."""
+    gv = mmq.MMQ_USE_GEMV
+    small = _w(ctx, mmq.MMQ_Q6_K, 512, 3584, gv)          # 1.8M < gate
+    big = _w(ctx, mmq.MMQ_Q6_K, 8192, 5120, gv)           # 41.9M >= gate
+    wide = _w(ctx, mmq.MMQ_Q6_K, 16, 16640, gv)           # small, but x too wide for LDS
+    assert 512 * 3584 < mmq.MMQ_DECODE_F32_GATE <= 8192 * 5120
+    X, X2, X3, Y, W, O = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+
+    def delta(fn, *a):
+        before = mmq.mmq_stats(ctx)
+        fn(*a)
+        after = mmq.mmq_stats(ctx)
+        return {k: after[k] - before[k] for k in ("launches_gemv_f32", "launches_mmvq_q6k",
+                                                 "launches_quant_f32", "cache_hits", "cache_misses")}
+
+    # small, written, no plane: the f32 path, nothing quantised or recorded
+    d = delta(mmq.mmq_decode_q6k, ctx, small, X, O)
+    assert d == {"launches_gemv_f32": 1, "launches_mmvq_q6k": 0, "launches_quant_f32": 0,
+                 "cache_hits": 0, "cache_misses": 0}
+    # large: the quantised GEMV, quantising x on the miss
+    d = delta(mmq.mmq_decode_q6k, ctx, big, X2, O)
+    assert d["launches_mmvq_q6k"] == 1 and d["cache_misses"] == 1 and d["launches_gemv_f32"] == 0
+    # small, but x2 (id 5120) now has no plane of width 3584; x3 gets one first
+    mmq.mmq_quant_f32(ctx, X3, 1, 3584)
+    d = delta(mmq.mmq_decode_q6k, ctx, small, X3, O)
+    assert d["launches_mmvq_q6k"] == 1 and d["cache_hits"] == 1 and d["launches_gemv_f32"] == 0
+    # a skip-write producer's output: never read as f32, served from its plane
+    mmq.mmq_quant_rms(ctx, X, W, Y, 1, 3584, 1e-6, 0)
+    d = delta(mmq.mmq_decode_q6k, ctx, small, Y, O)
+    assert d["launches_mmvq_q6k"] == 1 and d["cache_hits"] == 1 and d["launches_gemv_f32"] == 0
+    # the explicit f32 path refuses it (and launches nothing)
+    assert _status(mmq.mmq_gemv_q6k_f32, ctx, small, Y, O) == mmq.MMQ_E_DEAD_WRITE
+    # too wide for the staged activation: explicit call refused, routed call quantises
+    assert _status(mmq.mmq_gemv_q6k_f32, ctx, wide, X, O) == mmq.MMQ_E_SHAPE
+    d = delta(mmq.mmq_decode_q6k, ctx, wide, X, O)
+    assert d["launches_mmvq_q6k"] == 1 and d["launches_gemv_f32"] == 0
+    # type and registration checks
+    w4 = _w(ctx, mmq.MMQ_Q4_K, 64, 256, gv)
+    w6g = _w(ctx, mmq.MMQ_Q6_K, 64, 256, mmq.MMQ_USE_GEMM)
+    for fn in (mmq.mmq_gemv_q6k_f32, mmq.mmq_decode_q6k):
+        assert _status(fn, ctx, w4, X, O) == mmq.MMQ_E_TYPE
+        assert _status(fn, ctx, w6g, X, O) == mmq.MMQ_E_TYPE
+        assert _status(fn, ctx, small, X + 4, O) == mmq.MMQ_E_ARG
+    for w in (small, big, wide, w4, w6g):
+        mmq.mmq_weight_free(w)
+
+
 def test_consumer_type_checks(ctx):
     w4 = _w(ctx, mmq.MMQ_Q4_K, 512, 256)
     w6g = _w(ctx, mmq.MMQ_Q6_K, 64, 256, mmq.MMQ_USE_GEMM)

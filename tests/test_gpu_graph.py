@@ -90,10 +90,11 @@ def test_chain_graph_replays_equal_eager():
         st1 = mmq.mmq_stats(ch.ctx)
         mmq.mmq_cache_clear(ch.ctx)
         census = {k: st1[k] - st0[k] for k in st1 if k.startswith("launches_")}
-        assert census == {"launches_quant_rms": 2 * LAYERS, "launches_quant_swiglu": LAYERS,
-                          "launches_quant_f32": LAYERS, "launches_gemm_q4k": 5 * LAYERS,
-                          "launches_gemm_q6k": 2 * LAYERS, "launches_mmvq_q6k": 0,
-                          "launches_mmvq_q4k": 0, "launches_mmvq_q5k": 0}, census
+        expect = {"launches_quant_rms": 2 * LAYERS, "launches_quant_swiglu": LAYERS,
+                  "launches_quant_f32": LAYERS, "launches_gemm_q4k": 5 * LAYERS,
+                  "launches_gemm_q6k": 2 * LAYERS}
+        # every other launch counter (the GEMVs) stays at zero
+        assert census == {k: expect.get(k, 0) for k in census}, census
         assert st1["cache_hits"] - st0["cache_hits"] == 7 * LAYERS
         assert st1["cache_misses"] - st0["cache_misses"] == 0
         for rep in range(1, 4):

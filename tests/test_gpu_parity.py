@@ -334,6 +334,70 @@ def test_mmvq_q5k_parity(ctx, od, id_):
     mmq.mmq_weight_free(w)
 
 
+# the f32-activation q6_K GEMV: register-sized rows, ragged row counts, the
+# widest staged activation (16384) and the decode shapes below the gate
+GEMV_F32_SHAPES = [(1, 256), (64, 256), (37, 1024), (512, 3584), (1000, 5120), (1024, 5120),
+                   (3, 16384), (4100, 4096), (20000, 768)]
+
+
+def _assert_f32_gemv_close(got, raw, od, id_, x, what):
+    ref = oracle.gemv_f32("q6_K", raw, od, id_, x)
+    scale = np.abs(oracle.dequant("q6_K", raw, od, id_)) @ np.abs(x.astype(np.float64))
+    err = np.abs(got.astype(np.float64) - ref)
+    # f32 products and sums of exact weights: well inside 2^-14 of the absolute sum
+    assert np.all(err <= 2.0 ** -14 * scale + 1e-30), (what, float((err / (scale + 1e-30)).max()))
+    assert_gemm_close(got, ref.astype(np.float32), what)
+
+
+@pytest.mark.parametrize("od,id_", GEMV_F32_SHAPES)
+def test_gemv_f32_parity(ctx, od, id_):
+    raw = synth.q6k_weights(synth.rng_for("test", od, f"gemvf32{id_}"), od, id_)
+    w = mmq.mmq_register_weight(ctx, mmq.MMQ_Q6_K, od, id_, raw, mmq.MMQ_USE_GEMV)
+    xh = _act("gemvf32", 1, id_)[0]
+    x = dev_tensor(xh)
+    out = torch.full((od,), float("nan"), dtype=torch.float32, device="cuda")
+    st0 = mmq.mmq_stats(ctx)
+    mmq.mmq_gemv_q6k_f32(ctx, w, x, out)
+    st1 = mmq.mmq_stats(ctx)
+    assert st1["launches_gemv_f32"] - st0["launches_gemv_f32"] == 1
+    assert st1["launches_quant_f32"] == st0["launches_quant_f32"]     # nothing quantised
+    _assert_f32_gemv_close(out.cpu().numpy(), raw, od, id_, xh, f"gemv f32 {od}x{id_}")
+    mmq.mmq_weight_free(w)
+
+
+def test_decode_q6k_routes_bit_identically(ctx):
+    """The routed decode arm returns exactly what the path it takes returns:
+    the f32 GEMV below the gate, the quantised GEMV above it or when the
+    activation already has a plane."""
+    for od, id_ in ((512, 3584), (1024, 5120), (8192, 3584)):
+        raw = synth.q6k_weights(synth.rng_for("test", od, f"route{id_}"), od, id_)
+        w = mmq.mmq_register_weight(ctx, mmq.MMQ_Q6_K, od, id_, raw, mmq.MMQ_USE_GEMV)
+        xh = _act("route", 1, id_)[0]
+        x = dev_tensor(xh)
+        routed = torch.empty((od,), dtype=torch.float32, device="cuda")
+        direct = torch.empty_like(routed)
+        mmq.mmq_cache_clear(ctx)
+        mmq.mmq_decode_q6k(ctx, w, x, routed)
+        small = od * id_ < mmq.MMQ_DECODE_F32_GATE
+        assert small == (od != 8192)
+        if small:
+            mmq.mmq_gemv_q6k_f32(ctx, w, x, direct)
+        else:
+            mmq.mmvq_q6k(ctx, w, x, direct)
+        torch.cuda.synchronize()
+        assert torch.equal(routed, direct), (od, id_)
+        if small:
+            _assert_f32_gemv_close(routed.cpu().numpy(), raw, od, id_, xh, "routed f32")
+            # with a plane recorded for x, the same call takes the quantised GEMV
+            mmq.mmq_quant_f32(ctx, x, 1, id_)
+            mmq.mmq_decode_q6k(ctx, w, x, routed)
+            mmq.mmvq_q6k(ctx, w, x, direct)
+            torch.cuda.synchronize()
+            assert torch.equal(routed, direct)
+        mmq.mmq_cache_clear(ctx)
+        mmq.mmq_weight_free(w)
+
+
 def test_mmvq_q5k_extreme_codes(ctx):
     """Every code at 31 (all fifth bits set) and at 0, with sub-scales and mins
     at 63: the fifth bit carries weight 16 in every nibble group."""

@@ -448,3 +448,36 @@ def test_gemm_sampled_equals_full():
     tok = np.array([8, 0, 3]); outs = np.array([11, 2])
     part = oracle.gemm("q4_K", Q, D, S, raw, 12, 256, tok=tok, outs=outs)
     assert np.array_equal(part, full[np.ix_(tok, outs)])
+
+
+# ---------------------------------------------------------------- f32-activation GEMV
+def test_gemv_f32_closed_forms():
+    """Single q6_K superblock rows with every code 33 (weight d*sc*1) or 31
+    (weight -d*sc), d = 1 and sub-scales s_h: out = sum_h s_h * sum_{e in h} x_e."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(256).astype(np.float32)
+    sc = [int(v) for v in rng.integers(-128, 128, 16)]
+    rows = [q6k_encode(0x3C00, sc, [33] * 256), q6k_encode(0x3C00, sc, [31] * 256)]
+    raw = np.stack(rows)
+    got = oracle.gemv_f32("q6_K", raw, 2, 256, x)
+    halves = [float(np.sum(x[16 * h:16 * h + 16].astype(np.float64))) for h in range(16)]
+    want = sum(s * v for s, v in zip(sc, halves))
+    assert abs(got[0] - want) <= 1e-9 * (1 + abs(want))
+    assert abs(got[1] + want) <= 1e-9 * (1 + abs(want))
+
+
+def test_gemv_f32_equals_the_integer_dot_path_on_exact_planes():
+    """With integer activations whose every 32-block holds +-127, the q8 plane
+    is exact (D = 1, q = x), so the integer-dot matmul (its own decode, block
+    dots and rescale) and the f32-activation GEMV compute the same sum."""
+    rng = np.random.default_rng(12)
+    od, id_ = 7, 512
+    raw, _ = random_q6k(rng, od, id_)
+    x = rng.integers(-127, 128, id_).astype(np.float32)
+    x[::32] = 127.0
+    Q, D, S = oracle.quantize(x[None, :])
+    assert np.all(D == 1.0) and np.array_equal(Q[0].astype(np.float32), x)
+    dot = oracle.gemm("q6_K", Q, D, S, raw, od, id_)[0]
+    ref = oracle.gemv_f32("q6_K", raw, od, id_, x)
+    scale = np.abs(oracle.dequant("q6_K", raw, od, id_)) @ np.abs(x.astype(np.float64))
+    assert np.all(np.abs(dot - ref) <= 1e-6 * scale + 1e-30)
