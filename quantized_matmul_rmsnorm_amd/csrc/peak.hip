@@ -76,12 +76,13 @@ __global__ __launch_bounds__(256) void k_peak_i8(int* __restrict__ out, int iter
 
 // The matmul's per-block instruction mix without memory traffic, in its
 // launch shape (512 threads: 2 waves per SIMD).  Per block each wave issues 4
-// MFMAs (two output tiles, two K-steps of 16, the first with C = 0 as the
-// matmul's block dot) into one X buffer and 32 FMAs (acc += s * X, the
-// per-block rescale) reading the X buffer of the previous block; the buffers
-// alternate.  MODE 0: MFMAs only; 1: FMAs only; 2: both, in the matmul's
-// order (the MFMAs of a block, then the FMAs of the one before).  The
-// operands change every round so nothing is hoisted.
+// MFMAs (two output tiles, two K-steps of 16) into one X buffer and 32 FMAs
+// (acc += s * X, the per-block rescale) reading the X buffer of the previous
+// block; the buffers alternate.  The first K-step accumulates onto the
+// buffer's old contents (the matmul starts each block from zero; a zero start
+// with fixed operands would be hoisted out of the loop).  MODE 0: MFMAs only;
+// 1: FMAs only; 2: both, in the matmul's order (the MFMAs of a block, then
+// the FMAs of the one before).
 template <int MODE>
 __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int iters, float s) {
     const int t = threadIdx.x;
