@@ -470,7 +470,7 @@ def measured_peaks(torch):
     mblocks, miters = n_cu, 2048
     mout = torch.empty(mblocks * 512, dtype=torch.float32, device="cuda")
     mix_ms = []
-    for mode in (0, 1, 2):
+    for mode in (0, 1, 2, 3):
         if lib.mmq_peak_mix(mout.data_ptr(), mblocks, miters, mode, stream.cuda_stream) != 0:
             raise RuntimeError("instruction mix: launch failed")
         e0 = torch.cuda.Event(enable_timing=True)
@@ -483,12 +483,14 @@ def measured_peaks(torch):
         torch.cuda.synchronize()
         mix_ms.append(e0.elapsed_time(e1) / 3)
     mix_ops = mblocks * 8 * miters * 8 * (2 * 32 * 32 * 16)
-    t_m, t_v, t_b = mix_ms
+    t_m, t_v, t_b, t_i8 = mix_ms
     res["matmul_mix"] = {"mfma_only_ms": round(t_m, 4), "fma_only_ms": round(t_v, 4),
                          "both_ms": round(t_b, 4),
                          "both_TFLOPs": round(mix_ops / (t_b * 1e-3) / 1e12, 1),
                          "both_frac_of_f16_peak": round(mix_ops / (t_b * 1e-3) / 1e12 / PEAK_F16_TOPS, 4),
-                         "hidden_frac": round((t_m + t_v - t_b) / min(t_m, t_v), 3)}
+                         "hidden_frac": round((t_m + t_v - t_b) / min(t_m, t_v), 3),
+                         "int8_mfma_with_rescale_ms": round(t_i8, 4),
+                         "int8_mfma_with_rescale_TOPs": round(mix_ops / (t_i8 * 1e-3) / 1e12, 1)}
     del mout
     lib.mmq_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_void_p]

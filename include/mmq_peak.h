@@ -40,9 +40,11 @@ int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t stream);
  * each wave issues 4 f16 32x32x16 MFMAs (two output tiles, two K-steps) and
  * the 32 FMAs of the previous block's rescale.  mode 0 issues the MFMAs only,
  * 1 the FMAs only, 2 both in the matmul's order; comparing the three times
- * shows how far the matrix pipe and the VALU overlap on this device.  A
- * launch runs blocks * 8 * iters * 2 blocks of that mix: mode 0 and 2 perform
- * blocks * 8 * iters * 8 * (2*32*32*16) f16 operations.  out: caller-owned
+ * shows how far the matrix pipe and the VALU overlap on this device.  mode 3
+ * runs the same per-block work on int8 MFMA: 2 v_mfma_i32_32x32x32_i8 per
+ * block and wave and 3 VALU operations per output (convert, weight scale,
+ * token-scale FMA).  A launch runs blocks * 8 * iters * 2 blocks of that mix:
+ * mode 0, 2 and 3 perform blocks * 8 * iters * 8 * (2*32*32*16) operations.  out: caller-owned
  * device buffer of blocks * 512 floats; blocks >= 1, 1 <= iters <= 2^20.
  * Returns 0, -1 for an invalid argument (nothing launched), or the HIP error
  * code of the launch. */

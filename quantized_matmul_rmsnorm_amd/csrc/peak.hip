@@ -82,7 +82,11 @@ __global__ __launch_bounds__(256) void k_peak_i8(int* __restrict__ out, int iter
 // buffer's old contents (the matmul starts each block from zero; a zero start
 // with fixed operands would be hoisted out of the loop).  MODE 0: MFMAs only;
 // 1: FMAs only; 2: both, in the matmul's order (the MFMAs of a block, then
-// the FMAs of the one before).
+// the FMAs of the one before).  MODE 3 is the same per-block work on int8
+// MFMA: one v_mfma_i32_32x32x32_i8 per output tile and block (the whole
+// 32-block in one instruction) and, per output, the three VALU operations an
+// int32 block dot needs (convert, times the row's weight scale, FMA with the
+// token scale).
 template <int MODE>
 __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int iters, float s) {
     const int t = threadIdx.x;
@@ -103,6 +107,34 @@ __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int i
             XB[i][r] = (float)(r - i);
             acc[i][r] = 0.0f;
         }
+    i32x4 ia0, ia1, ib0, ib1;
+    i32x16 IA[2], IB[2];
+    float wsc[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ia0[i] = 0x01010101 * ((t + i) & 7);
+        ib0[i] = 0x01010101 * ((t * 3 + i) & 7);
+        ia1[i] = 0x01010101 * ((t + 2 * i) & 7);
+        ib1[i] = 0x01010101 * ((t * 5 + i) & 7);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        IA[0][r] = r; IA[1][r] = r + 1; IB[0][r] = r + 2; IB[1][r] = r + 3;
+        wsc[r] = 1.0f + 0.125f * (float)r;
+    }
+    float dtok[2] = {s, 1.0f - s};   // the two tiles' token scales, a new value per block
+    auto block_i8 = [&](i32x16* Iw, const i32x16* Ir) {
+        Iw[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ia0, ib0, Iw[0], 0, 0, 0);
+        Iw[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ia1, ib1, Iw[1], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            dtok[i] *= 0.999f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(dtok[i] * wsc[r], (float)Ir[i][r], acc[i][r]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // the block's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x002, 98, 0);   // then its rescale
+    };
     auto block = [&](f32x16* Xw, const f32x16* Xr) {
         if constexpr (MODE != 1) {
             Xw[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Xw[0], 0, 0, 0);
@@ -122,6 +154,11 @@ __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int i
         }
     };
     for (int it = 0; it < iters; ++it) {
+        if constexpr (MODE == 3) {
+            block_i8(IA, IB);
+            block_i8(IB, IA);
+            continue;
+        }
         block(XA, XB);
         block(XB, XA);
         if constexpr (MODE == 1) {   // the FMAs' inputs change every round
@@ -131,7 +168,10 @@ __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int i
     }
     float v = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v += XA[0][r] + XA[1][r] + XB[0][r] + XB[1][r] + acc[0][r] + acc[1][r];
+    for (int r = 0; r < 16; ++r) {
+        v += XA[0][r] + XA[1][r] + XB[0][r] + XB[1][r] + acc[0][r] + acc[1][r];
+        if constexpr (MODE == 3) v += (float)(IA[0][r] ^ IA[1][r] ^ IB[0][r] ^ IB[1][r]);
+    }
     out[(int64_t)blockIdx.x * blockDim.x + t] = v;
 }
 
@@ -182,14 +222,15 @@ int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t s) {
 }
 
 // out: device buffer of blocks * 512 floats; blocks >= 1, 1 <= iters <=
-// 1 << 20; mode 0, 1 or 2.  Returns 0, -1 for bad arguments, or the HIP error.
+// 1 << 20; mode 0 .. 3.  Returns 0, -1 for bad arguments, or the HIP error.
 int mmq_peak_mix(float* out, int blocks, int iters, int mode, hipStream_t s) {
-    if (out == nullptr || blocks < 1 || iters < 1 || iters > (1 << 20) || mode < 0 || mode > 2)
+    if (out == nullptr || blocks < 1 || iters < 1 || iters > (1 << 20) || mode < 0 || mode > 3)
         return -1;
     const dim3 g((unsigned)blocks), b(512);
     if (mode == 0) hipLaunchKernelGGL(k_peak_mix<0>, g, b, 0, s, out, iters, 0.999f);
     else if (mode == 1) hipLaunchKernelGGL(k_peak_mix<1>, g, b, 0, s, out, iters, 0.999f);
-    else hipLaunchKernelGGL(k_peak_mix<2>, g, b, 0, s, out, iters, 0.999f);
+    else if (mode == 2) hipLaunchKernelGGL(k_peak_mix<2>, g, b, 0, s, out, iters, 0.999f);
+    else hipLaunchKernelGGL(k_peak_mix<3>, g, b, 0, s, out, iters, 0.999f);
     return (int)hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ def test_peak_library_exports_its_header():
     assert mix(ctypes.c_void_p(0x1000), 0, 1, 0, None) == -1
     assert mix(ctypes.c_void_p(0x1000), 1, 0, 0, None) == -1
     assert mix(ctypes.c_void_p(0x1000), 1, (1 << 20) + 1, 0, None) == -1
-    assert mix(ctypes.c_void_p(0x1000), 1, 1, 3, None) == -1
+    assert mix(ctypes.c_void_p(0x1000), 1, 1, 4, None) == -1
     assert mix(ctypes.c_void_p(0x1000), 1, 1, -1, None) == -1
     rd = lib.mmq_peak_read
     rd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
