@@ -215,7 +215,12 @@ void oracle_swiglu(const float* g, const float* u, int64_t n, int64_t d, float* 
  * Block-32 quantisation [r52 2.2, 3.2; d37 Excerpt C]: per block of 32
  * values, amax = max |y|, scale D = amax / 127 (f32 IEEE divide), codes
  * q = clamp(rint(y / D), -127, 127) with round-half-even and the IEEE
- * quotient, S = sum q (int).  An all-zero block has D = 0, q = 0, S = 0.
+ * quotient, S = sum q (int).  A block whose scale is zero has q = 0 and
+ * S = 0: the all-zero block, and also a block of deep subnormals whose
+ * quotient amax / 127 rounds to zero (amax <= 63 * 2^-149).  With D = 0 the
+ * block's values D * q are zero whatever the codes, so the zero codes of the
+ * all-zero block (and of a padded row) are the reading that keeps D, q and S
+ * consistent; it also keeps y / 0 out of the arithmetic.
  * q: [n][d] int8, D and S: [n][d/32].
  */
 void oracle_quantize(const float* y, int64_t n, int64_t d,
@@ -235,7 +240,7 @@ void oracle_quantize(const float* y, int64_t n, int64_t d,
             int32_t sum = 0;
             for (int i = 0; i < QK; i++) {
                 int v = 0;
-                if (amax != 0.0f) {
+                if (dsc != 0.0f) {
                     float r = rintf(yb[i] / dsc);
                     if (r > 127.0f) r = 127.0f;
                     if (r < -127.0f) r = -127.0f;

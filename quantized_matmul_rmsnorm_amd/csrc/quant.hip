@@ -7,7 +7,9 @@
 //   SwiGLU  : y = (g / (1 + exp(-g))) * u
 //   F32     : y = x                      (standalone quantise)
 // then per 32-block: amax = max|y|, D = amax / 127, q = clamp(rint(y / D),
-// -127, 127), S = sum(q); an all-zero block has D = 0, q = 0, S = 0.
+// -127, 127), S = sum(q); a block whose scale is zero (all zeros, or deep
+// subnormals with amax <= 63 * 2^-149, where amax / 127 rounds to zero) has
+// q = 0 and S = 0.
 //
 // Geometry.  One workgroup of 4 waves per row (per row segment for SwiGLU and
 // the standalone quantise, whose rows need no row-wide reduction); the row is
@@ -90,7 +92,7 @@ __device__ __forceinline__ void quant4(float4 v, int lane, uint32_t* qdst, uint2
     am = max8(am);
     const float dsc = am / 127.0f;
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    if (am > 0.0f) {
+    if (dsc > 0.0f) {   // a zero scale (amax 0, or amax / 127 underflowing) leaves zero codes
         const float rcp = __builtin_amdgcn_rcpf(dsc);
         q0 = code(v.x, dsc, rcp); q1 = code(v.y, dsc, rcp);
         q2 = code(v.z, dsc, rcp); q3 = code(v.w, dsc, rcp);

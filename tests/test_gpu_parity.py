@@ -56,7 +56,7 @@ def test_quant_f32_bit_exact(ctx, n, d):
 
 
 def test_quant_f32_special_values(ctx):
-    n, d = 4, 256
+    n, d = 5, 256
     y = np.zeros((n, d), np.float32)
     y[0, :32] = 1e-40                     # subnormal block
     y[0, 32:64] = np.linspace(-3e-39, 3e-39, 32)
@@ -65,6 +65,11 @@ def test_quant_f32_special_values(ctx):
     y[2, ::2] = 2.5                       # ties around the code grid
     y[2, 1::2] = 127.0
     y[3] = np.float32(7.0) / np.float32(3.0)
+    tiny = np.float32(2.0 ** -149)            # scale underflow: amax / 127 rounds to 0
+    y[4, 0], y[4, 5] = 10 * tiny, -3 * tiny
+    y[4, 32], y[4, 33] = 63 * tiny, -63 * tiny
+    y[4, 64], y[4, 65], y[4, 66] = 190 * tiny, 64 * tiny, -3 * tiny   # D = 2^-149, clamped code
+    y[4, 96:128] = -tiny
     x = dev_tensor(y)
     mmq.mmq_quant_f32(ctx, x, n, d)
     assert_plane_equal(export_plane(ctx, x, n, d), oracle.quantize(y), "special values")

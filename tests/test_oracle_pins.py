@@ -233,6 +233,32 @@ def test_quantize_zero_and_single_nonzero_blocks():
     assert D[1, 1] == np.float32(np.float32(0.123) / np.float32(127.0))
 
 
+def test_quantize_scale_underflow_is_a_zero_block():
+    """Deep subnormal blocks: where the IEEE quotient amax / 127 rounds to
+    zero (numpy's own float32 division decides it), the block is the all-zero
+    block (q = 0, S = 0); one step above, the scale is the smallest subnormal
+    and the codes are the clamped quotients."""
+    tiny = np.float32(2.0 ** -149)
+    y = np.zeros((3, 32), np.float32)
+    y[0, 0] = 10 * tiny; y[0, 5] = -3 * tiny             # amax 10 * 2^-149
+    y[1, 0] = 63 * tiny; y[1, 1] = -63 * tiny             # the largest amax that underflows
+    y[2, 0] = 190 * tiny; y[2, 1] = 64 * tiny; y[2, 2] = -3 * tiny
+    amax = np.abs(y).max(-1)
+    Dn = amax / np.float32(127.0)
+    assert Dn.dtype == np.float32
+    assert Dn[0] == 0 and Dn[1] == 0 and Dn[2] == tiny    # 190/127 rounds to one step
+    q, D, S = _blocks(y)
+    assert np.array_equal(D[:, 0].view(np.uint32), Dn.view(np.uint32))
+    assert np.all(q[:2] == 0) and np.all(S[:2, 0] == 0)
+    # D = 2^-149: y / D is the integer multiple itself; 190 clamps to 127
+    assert list(q[2, :3]) == [127, 64, -3] and np.count_nonzero(q[2]) == 3
+    assert S[2, 0] == 127 + 64 - 3
+    # a larger value in the same block lifts the whole block out of underflow
+    y2 = y[:1].copy(); y2[0, 31] = np.float32(1e-30)
+    q2, D2, S2 = _blocks(y2)
+    assert D2[0, 0] > 0 and q2[0, 31] == 127 and np.count_nonzero(q2) == 1
+
+
 def test_quantize_uses_quotient_not_reciprocal():
     """Find values where rint(y * (1/D)) != rint(y / D) and check the oracle
     follows the quotient (the reading of the plain 'y / scale')."""
