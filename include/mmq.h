@@ -19,8 +19,14 @@
  *                 skip-write producer, the buffer it would have written);
  *                 consumers look planes up by (pointer, n, d) [r52 3.1, d37 A2].
  *   dead key   -- a skip-write producer's output buffer: it was never
- *                 written, so quantising it again would read garbage; any
- *                 request that would do so is refused [r52 3.1-3.2].
+ *                 written, so quantising it again, or feeding it to a
+ *                 producer as an input, would read garbage; any request that
+ *                 would do so is refused [r52 3.1-3.2].  Bytes stay dead
+ *                 until the library writes them (a producer's y, a
+ *                 consumer's out, an export) or the window ends.
+ *   stale key  -- every write the library makes to caller memory drops the
+ *                 cached planes whose key bytes it overwrites, so a later
+ *                 lookup of those bytes misses and re-quantises.
  *
  * Conventions for every call.
  *   * Pointers named x, w, y, gate, up, a, out are DEVICE pointers on the
@@ -168,8 +174,10 @@ int64_t mmq_weight_bytes(const mmq_weight* w);
  * memory), falls back to writing y alone with no plane recorded (counted in
  * unfused_fallbacks; returns MMQ_OK) -- every tier is correct, a lower one
  * only costs time.
+ * An input that overlaps a dead key (x or w for RMSNorm, gate or up for
+ * SwiGLU) is refused with MMQ_E_DEAD_WRITE before any launch.
  * Preconditions: d % 256 == 0, n >= 1; x/gate/up/y 16-byte aligned.
- * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_OOM, MMQ_E_HIP. */
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_OOM, MMQ_E_DEAD_WRITE, MMQ_E_HIP. */
 
 /* RMSNorm: y[t][i] = (x[t][i] * s_t) * w[i], s_t = 1/sqrt(mean_i x[t][i]^2 + eps). */
 int mmq_quant_rms(mmq_ctx* ctx, const float* x, const float* w, float* y,
@@ -190,6 +198,8 @@ int mmq_quant_f32(mmq_ctx* ctx, const float* x, int64_t n, int64_t d, void* stre
  * overlaps a dead key, in which case it returns MMQ_E_DEAD_WRITE.
  * out[t][o] = sum_k D[t][k/32] q[t][k] * w[o][k] for t < n, o < rows,
  * row-major [n][rows] f32, caller-owned; w is the dequantised weight.
+ * Writing out drops cached planes keyed in its bytes and revives dead bytes
+ * there (the same holds for every consumer below).
  * The small-n band [r60 3.2: the matmul is tuned for n >= 16; d37 2]: for
  * n <= 8 on a weight also registered with MMQ_USE_GEMV the call runs on the
  * dot4 GEMV path (one launch per pass of up to 8 tokens); otherwise the
@@ -269,8 +279,11 @@ int mmq_plane_only(const mmq_ctx* ctx);
  * for reuse. */
 void mmq_cache_clear(mmq_ctx* ctx);
 
-/* Drop the entry and dead marks of `key` (for a buffer about to be reused
- * with new contents inside a window).  MMQ_OK even if absent. */
+/* Drop the entries recorded under `key` and the dead range a skip-write
+ * producer recorded for `key` (all of it that no later write revived), for a
+ * buffer about to be reused with new contents inside a window.  Writes to
+ * caller memory that the caller makes itself are invisible to the library:
+ * call this before re-using a key buffer.  MMQ_OK even if absent. */
 int mmq_cache_invalidate(mmq_ctx* ctx, const void* key);
 
 /* Copy the plane recorded under (key, n, d) into caller device buffers in

@@ -6,10 +6,14 @@
 // produced (or, with write_y = 0, the buffer they were promised but never
 // wrote); consumers look the plane up by (pointer, n, d) and on a miss
 // quantise the buffer themselves and record it.  A skip-write producer marks
-// its output range dead: any later request that would quantise bytes of a
-// dead range refuses loudly (status MMQ_E_DEAD_WRITE plus one stderr line)
-// instead of reading memory that was never written.  mmq_cache_clear is the
-// execution-window boundary: it drops every entry and every dead range.
+// its output range dead: any later request that would read bytes of a dead
+// range -- a quantise, or a producer taking it as an input -- refuses loudly
+// (status MMQ_E_DEAD_WRITE plus one stderr line) instead of reading memory
+// that was never written.  Every write the library makes to caller memory (a
+// producer's y, a consumer's out, an export) drops the cached planes whose
+// key bytes it overwrites and revives the dead bytes it defines.
+// mmq_cache_clear is the execution-window boundary: it drops every entry and
+// every dead range.
 //
 // The table has kSlots entries, each owning one grow-only device plane slot;
 // when all are in use the least recently used entry is evicted and its slot
@@ -60,6 +64,7 @@ struct Slot {
 
 struct DeadRange {
     uintptr_t lo, hi;  // [lo, hi)
+    uintptr_t key;     // the skip-write producer output it was recorded for
 };
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -170,10 +175,17 @@ void revive(mmq_ctx* c, const void* p, int64_t bytes) {
             keep.push_back(r);
             continue;
         }
-        if (r.lo < lo) keep.push_back({r.lo, lo});
-        if (hi < r.hi) keep.push_back({hi, r.hi});
+        if (r.lo < lo) keep.push_back({r.lo, lo, r.key});
+        if (hi < r.hi) keep.push_back({hi, r.hi, r.key});
     }
     c->dead.swap(keep);
+}
+
+// [p, p + bytes) becomes a dead range recorded for key p (overlapping older
+// ranges give up those bytes first, so the list stays disjoint).
+void mark_dead(mmq_ctx* c, const void* p, int64_t bytes) {
+    revive(c, p, bytes);
+    c->dead.push_back({(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes, (uintptr_t)p});
 }
 
 int find_entry(const mmq_ctx* c, const void* key, int64_t n, int64_t d) {
@@ -193,6 +205,13 @@ void drop_overlapping(mmq_ctx* c, const void* p, int64_t bytes) {
         const uintptr_t elo = (uintptr_t)e.key, ehi = elo + (uintptr_t)(e.n * e.d * 4);
         if (lo < ehi && elo < hi) e.used = false;
     }
+}
+
+// The library is about to write [p, p + bytes) of caller memory: planes keyed
+// by those bytes describe old contents, and dead bytes become written.
+void written(mmq_ctx* c, const void* p, int64_t bytes) {
+    drop_overlapping(c, p, bytes);
+    revive(c, p, bytes);
 }
 
 // Pick an entry for (key, n, d), growing its slot if needed.  The entry is
@@ -294,6 +313,12 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
         return fail(MMQ_E_ARG, "%s: null or non-16-byte-aligned pointer", who);
     if (kind != kProdF32 && write_y != 0 && write_y != 1 && write_y != MMQ_WRITE_AUTO)
         return fail(MMQ_E_ARG, "%s: write_y=%d (0, 1 or MMQ_WRITE_AUTO)", who, write_y);
+    const int64_t bytes = n * d * 4;
+    // every f32 input the kernel reads must have been written: x (or gate),
+    // and the RMSNorm weight [d] or the SwiGLU up [n][d]
+    if (overlaps_dead(c, a, bytes)) return refuse_dead(c, who, a);
+    if (kind == kProdRms && overlaps_dead(c, b, d * 4)) return refuse_dead(c, who, b);
+    if (kind == kProdSwiglu && overlaps_dead(c, b, bytes)) return refuse_dead(c, who, b);
     // The degradation ladder: skip-write (y never written) only while every
     // consumer reads planes; otherwise write y and the plane.
     const int auto_mode = write_y == MMQ_WRITE_AUTO;
@@ -301,9 +326,7 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
     const bool skip = want_skip && c->plane_only;
     if (want_skip && !skip) c->st.degraded_writes++;
     write_y = kind == kProdF32 ? 0 : (skip ? 0 : 1);
-    const int64_t bytes = n * d * 4;
     const void* key = kind == kProdF32 ? (const void*)a : (const void*)y;
-    if (kind == kProdF32 && overlaps_dead(c, a, bytes)) return refuse_dead(c, who, a);
     if ((rc = use_device(c))) return rc;
     int idx;
     // The producer replaces whatever was cached for bytes it (re)defines.
@@ -329,7 +352,7 @@ int produce(mmq_ctx* c, ProducerKind kind, const char* who, const float* a, cons
     if (kind != kProdF32 && write_y) revive(c, y, bytes);  // a real write makes these bytes valid
     const bool dead = kind != kProdF32 && !write_y;
     commit_entry(c, idx, key, n, d, dead);
-    if (dead) c->dead.push_back({(uintptr_t)y, (uintptr_t)y + (uintptr_t)bytes});
+    if (dead) mark_dead(c, y, bytes);
     if (kind == kProdRms) c->st.launches_quant_rms++;
     else if (kind == kProdSwiglu) c->st.launches_quant_swiglu++;
     else c->st.launches_quant_f32++;
@@ -630,6 +653,7 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
     if (small) {
         PlaneView pl;
         if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;
+        written(c, out, n * w->w.rows * 4);
         if (type == MMQ_Q4_K) c->st.launches_gemm_q4k++;
         else c->st.launches_gemm_q6k++;
         c->st.small_n_gemv++;
@@ -649,6 +673,7 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
         return rc;
     PlaneView pl;
     if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;
+    written(c, out, n * w->w.rows * 4);
     if (type == MMQ_Q4_K) c->st.launches_gemm_q4k++;
     else c->st.launches_gemm_q6k++;
     if (c->dry) return MMQ_OK;
@@ -673,6 +698,7 @@ int mmvq_q6k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     if ((rc = use_device(c))) return rc;
     PlaneView pl;
     if ((rc = plane_for(c, who, a, 1, w->w.cols, stream, &pl))) return rc;
+    written(c, out, w->w.rows * 4);
     c->st.launches_mmvq_q6k++;
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -686,6 +712,7 @@ int mmvq_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     if ((rc = use_device(c))) return rc;
     PlaneView pl;
     if ((rc = plane_for(c, who, a, 1, w->w.cols, stream, &pl))) return rc;
+    written(c, out, w->w.rows * 4);
     c->st.launches_mmvq_q4k++;
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -703,6 +730,7 @@ int mmq_gemv_q6k_f32(mmq_ctx* c, const mmq_weight* w, const float* x, float* out
     // the kernel reads x itself: a buffer a skip-write producer never wrote is refused
     if (overlaps_dead(c, x, w->w.cols * 4)) return refuse_dead(c, who, x);
     if ((rc = use_device(c))) return rc;
+    written(c, out, w->w.rows * 4);
     c->st.launches_gemv_f32++;
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -730,6 +758,7 @@ int mmvq_q5k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     if ((rc = use_device(c))) return rc;
     PlaneView pl;
     if ((rc = plane_for(c, who, a, 1, w->w.cols, stream, &pl))) return rc;
+    written(c, out, w->w.rows * 4);
     c->st.launches_mmvq_q5k++;
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -761,8 +790,10 @@ int mmq_cache_invalidate(mmq_ctx* c, const void* key) {
     if (!c) return fail(MMQ_E_ARG, "mmq_cache_invalidate: null context");
     for (Entry& e : c->entries)
         if (e.used && e.key == key) e.used = false;
+    // every piece of the dead range recorded for key, also the pieces a later
+    // partial write left of it
     c->dead.erase(std::remove_if(c->dead.begin(), c->dead.end(),
-                                 [&](const DeadRange& r) { return r.lo == (uintptr_t)key; }),
+                                 [&](const DeadRange& r) { return r.key == (uintptr_t)key; }),
                   c->dead.end());
     return MMQ_OK;
 }
@@ -782,6 +813,9 @@ int mmq_plane_export(mmq_ctx* c, const void* key, int64_t n, int64_t d, int incl
     const PlaneView pl = view_of(c, idx);
     const int64_t rows = include_pad ? pl.rows : n;
     const int64_t nb = d / kBlock;
+    written(c, q, rows * d);
+    written(c, dq, rows * nb * 4);
+    written(c, s, rows * nb * 4);
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(q, pl.q, (size_t)(rows * d), hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = launch_plane_split(pl.ds, dq, s, rows * nb, st);

@@ -327,6 +327,67 @@ def test_producer_replaces_stale_overlapping_entries(ctx):
     assert mmq.mmq_stats(ctx)["cache_misses"] == m0 + 1
 
 
+def test_consumer_output_drops_stale_planes_and_revives_dead_bytes(ctx):
+    """A matmul's out that overwrites a key buffer: the old plane no longer
+    serves (a miss re-quantises), and dead bytes it writes become readable."""
+    w = _w(ctx, mmq.MMQ_Q4_K, 256, 256)          # out rows: n x 256 floats = n x 1 KiB
+    K, n, d = 0x1000000, 8, 256
+    mmq.mmq_quant_f32(ctx, K, n, d)               # plane of K recorded (live)
+    mmq.mmq_gemm_q4k(ctx, w, 0x2000000, n, K)     # out = K: its contents change
+    m0, h0 = mmq.mmq_stats(ctx)["cache_misses"], mmq.mmq_stats(ctx)["cache_hits"]
+    mmq.mmq_gemm_q4k(ctx, w, K, n, 0x3000000)     # must not reuse K's old plane
+    st = mmq.mmq_stats(ctx)
+    assert (st["cache_misses"], st["cache_hits"]) == (m0 + 1, h0)
+    # a dead key that a matmul has since written is readable again, exactly there
+    Y = 0x5000000
+    mmq.mmq_quant_rms(ctx, 0x10000, 0x20000, Y, 2 * n, d, 1e-6, 0)   # dead [Y, Y + 16 KiB)
+    assert _status(mmq.mmq_quant_f32, ctx, Y, n, d) == mmq.MMQ_E_DEAD_WRITE
+    mmq.mmq_gemm_q4k(ctx, w, 0x2000000, n, Y)     # writes [Y, Y + 8 KiB)
+    assert _status(mmq.mmq_quant_f32, ctx, Y, n, d) == mmq.MMQ_OK
+    assert _status(mmq.mmq_quant_f32, ctx, Y + n * d * 4, n, d) == mmq.MMQ_E_DEAD_WRITE
+    # the one-token GEMV's output counts as a write too
+    wv = _w(ctx, mmq.MMQ_Q6_K, 256, 256)
+    Z = 0x7000000
+    mmq.mmq_quant_swiglu(ctx, 0x10000, 0x30000, Z, 1, d, 0)         # dead [Z, Z + 1 KiB)
+    mmq.mmvq_q6k(ctx, wv, 0x2000000, Z)
+    assert _status(mmq.mmq_quant_f32, ctx, Z, 1, d) == mmq.MMQ_OK
+
+
+def test_producers_refuse_dead_inputs(ctx, capfd):
+    """RMSNorm and SwiGLU read their f32 inputs: a skip-write buffer (never
+    written) as x, w, gate or up is refused before any launch."""
+    Y, n, d = 0x1000000, 4, 256
+    mmq.mmq_quant_swiglu(ctx, 0x10000, 0x20000, Y, n, d, 0)         # dead [Y, Y + 4 KiB)
+    before = mmq.mmq_stats(ctx)
+    for call in ((mmq.mmq_quant_rms, ctx, Y, 0x30000, 0x40000, n, d, 1e-6, 1),
+                 (mmq.mmq_quant_rms, ctx, 0x30000, Y + 512, 0x40000, n, d, 1e-6, 1),
+                 (mmq.mmq_quant_swiglu, ctx, Y, 0x30000, 0x40000, n, d, 1),
+                 (mmq.mmq_quant_swiglu, ctx, 0x30000, Y + 1024, 0x40000, 1, d, 0)):
+        assert _status(*call) == mmq.MMQ_E_DEAD_WRITE
+    after = mmq.mmq_stats(ctx)
+    assert after["cache_refusals"] == before["cache_refusals"] + 4
+    for k in ("launches_quant_rms", "launches_quant_swiglu", "degraded_writes"):
+        assert after[k] == before[k]
+    assert "refused" in capfd.readouterr().err
+    # inputs next to the dead range are fine
+    mmq.mmq_quant_rms(ctx, Y + n * d * 4, 0x30000, 0x40000, n, d, 1e-6, 1)
+
+
+def test_invalidate_drops_every_piece_of_the_dead_range(ctx):
+    """After a partial write splits a dead range, invalidating its key drops
+    the pieces on both sides; other producers' dead ranges stay."""
+    w = _w(ctx, mmq.MMQ_Q4_K, 256, 256)
+    Y, V, d = 0x1000000, 0x4000000, 256
+    mmq.mmq_quant_rms(ctx, 0x10000, 0x20000, Y, 16, d, 1e-6, 0)     # dead [Y, Y + 16 KiB)
+    mmq.mmq_quant_rms(ctx, 0x10000, 0x20000, V, 4, d, 1e-6, 0)      # another dead key
+    mmq.mmq_gemm_q4k(ctx, w, 0x2000000, 4, Y + 4096)                # writes 4 KiB in the middle
+    assert _status(mmq.mmq_quant_f32, ctx, Y + 12288, 4, d) == mmq.MMQ_E_DEAD_WRITE
+    mmq.mmq_cache_invalidate(ctx, Y)
+    assert _status(mmq.mmq_quant_f32, ctx, Y, 4, d) == mmq.MMQ_OK
+    assert _status(mmq.mmq_quant_f32, ctx, Y + 12288, 4, d) == mmq.MMQ_OK
+    assert _status(mmq.mmq_quant_f32, ctx, V, 4, d) == mmq.MMQ_E_DEAD_WRITE
+
+
 def test_scratch_cap(ctx):
     mmq.mmq_set_scratch_cap(ctx, 64 * 1024)
     assert _status(mmq.mmq_quant_f32, ctx, 0x100000, 32, 512) == mmq.MMQ_OK     # ~21 KB

@@ -1,9 +1,12 @@
 """Randomised check of the plane cache against a small Python model of its
 contract (include/mmq.h): producers record planes under their output buffer
 (dead when write_y == 0), consumers hit on (key, n, d) or quantise on a miss,
-anything that would re-quantise bytes of a dead buffer is refused, a real
-write revives its bytes, eight entries with least-recently-used reuse, and
-clear / invalidate.  Runs on dry-run contexts (host bookkeeping only).
+anything that would read bytes of a dead buffer (a quantise, a producer's
+inputs) is refused, every library write to caller memory (a producer's y, a
+consumer's out) drops the planes keyed in those bytes and revives them, eight
+entries with least-recently-used reuse, and clear / invalidate (which drops
+every piece of the dead range recorded for the key).  Runs on dry-run
+contexts (host bookkeeping only).
 """
 import random
 
@@ -17,12 +20,12 @@ SLOTS = 8
 class Model:
     def __init__(self):
         self.entries = [None] * SLOTS          # dict(key, n, d, last)
-        self.dead = []                         # [lo, hi)
+        self.dead = []                         # [lo, hi, key of the recording producer]
         self.tick = 0
         self.st = dict(hits=0, misses=0, refusals=0, rms=0, swiglu=0, f32=0, gemm=0)
 
     def _overlaps_dead(self, lo, hi):
-        return any(lo < h and l < hi for l, h in self.dead)
+        return any(lo < h and l < hi for l, h, _ in self.dead)
 
     def _drop_overlapping(self, lo, hi):
         for i, e in enumerate(self.entries):
@@ -31,15 +34,19 @@ class Model:
 
     def _revive(self, lo, hi):
         keep = []
-        for l, h in self.dead:
+        for l, h, k in self.dead:
             if hi <= l or h <= lo:
-                keep.append((l, h))
+                keep.append((l, h, k))
                 continue
             if l < lo:
-                keep.append((l, lo))
+                keep.append((l, lo, k))
             if hi < h:
-                keep.append((hi, h))
+                keep.append((hi, h, k))
         self.dead = keep
+
+    def _written(self, lo, hi):
+        self._drop_overlapping(lo, hi)
+        self._revive(lo, hi)
 
     def _find(self, key, n, d):
         for i, e in enumerate(self.entries):
@@ -60,8 +67,13 @@ class Model:
         self.tick += 1
         self.entries[i] = dict(key=key, n=n, d=d, last=self.tick)
 
-    def produce(self, kind, a, y, n, d, write_y):
+    def produce(self, kind, a, y, n, d, write_y, b=None):
         bytes_ = n * d * 4
+        b_bytes = d * 4 if kind == "rms" else bytes_
+        if kind != "f32" and (self._overlaps_dead(a, a + bytes_) or
+                              self._overlaps_dead(b, b + b_bytes)):
+            self.st["refusals"] += 1
+            return mmq.MMQ_E_DEAD_WRITE
         if kind == "f32":
             if self._overlaps_dead(a, a + bytes_):
                 self.st["refusals"] += 1
@@ -76,17 +88,19 @@ class Model:
             self._revive(y, y + bytes_)
         self._commit(i, y, n, d)
         if not write_y:
-            self.dead.append((y, y + bytes_))
+            self._revive(y, y + bytes_)
+            self.dead.append((y, y + bytes_, y))
         self.st[kind] += 1
         return mmq.MMQ_OK
 
-    def consume(self, a, n, d):
+    def consume(self, a, n, d, out, od):
         i = self._find(a, n, d)
         if i >= 0:
             self.st["hits"] += 1
             self.tick += 1
             self.entries[i]["last"] = self.tick
             self.st["gemm"] += 1
+            self._written(out, out + n * od * 4)
             return mmq.MMQ_OK
         if self._overlaps_dead(a, a + n * d * 4):
             self.st["refusals"] += 1
@@ -95,6 +109,7 @@ class Model:
         rc = self.produce("f32", a, None, n, d, 0)
         if rc == mmq.MMQ_OK:
             self.st["gemm"] += 1
+            self._written(out, out + n * od * 4)
         return rc
 
     def clear(self):
@@ -105,7 +120,7 @@ class Model:
         for i, e in enumerate(self.entries):
             if e and e["key"] == key:
                 self.entries[i] = None
-        self.dead = [(l, h) for l, h in self.dead if l != key]
+        self.dead = [(l, h, k) for l, h, k in self.dead if k != key]
 
 
 def _status(fn, *a):
@@ -140,17 +155,22 @@ def test_cache_matches_model(seed):
             if op in ("rms", "swiglu"):
                 y = rng.choice(addrs)
                 wy = rng.random() < 0.4
+                # the second input: the RMSNorm weight (never a key), or the
+                # SwiGLU up buffer, sometimes a key buffer
+                b = W if (op == "rms" or rng.random() < 0.5) else rng.choice(addrs)
                 if op == "rms":
-                    got = _status(mmq.mmq_quant_rms, ctx, a, W, y, n, d, 1e-6, int(wy))
+                    got = _status(mmq.mmq_quant_rms, ctx, a, b, y, n, d, 1e-6, int(wy))
                 else:
-                    got = _status(mmq.mmq_quant_swiglu, ctx, a, W, y, n, d, int(wy))
-                want = model.produce(op, a, y, n, d, wy)
+                    got = _status(mmq.mmq_quant_swiglu, ctx, a, b, y, n, d, int(wy))
+                want = model.produce(op, a, y, n, d, wy, b)
             elif op == "f32":
                 got = _status(mmq.mmq_quant_f32, ctx, a, n, d)
                 want = model.produce("f32", a, None, n, d, 0)
             elif op == "gemm":
-                got = _status(mmq.mmq_gemm_q4k, ctx, ws[d], a, n, O)
-                want = model.consume(a, n, d)
+                # the output lands on a key buffer half of the time
+                out = O if rng.random() < 0.5 else rng.choice(addrs)
+                got = _status(mmq.mmq_gemm_q4k, ctx, ws[d], a, n, out)
+                want = model.consume(a, n, d, out, 64)
             elif op == "clear":
                 mmq.mmq_cache_clear(ctx)
                 model.clear()
