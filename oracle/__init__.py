@@ -56,9 +56,9 @@ def _load():
         lib.oracle_rmsnorm.argtypes = [P, P, I64, I64, ctypes.c_float, P]
         lib.oracle_swiglu.argtypes = [P, P, I64, I64, P]
         lib.oracle_quantize.argtypes = [P, I64, I64, P, P, P]
-        lib.oracle_gemm_q4k.argtypes = [P, P, P, P, I64, P, I64, P, I64, P]
-        lib.oracle_gemm_q5k.argtypes = [P, P, P, P, I64, P, I64, P, I64, P]
-        lib.oracle_gemm_q6k.argtypes = [P, P, P, I64, P, I64, P, I64, P]
+        lib.oracle_gemm_q4k.argtypes = [P, P, P, P, I64, P, I64, P, I64, P, P]
+        lib.oracle_gemm_q5k.argtypes = [P, P, P, P, I64, P, I64, P, I64, P, P]
+        lib.oracle_gemm_q6k.argtypes = [P, P, P, I64, P, I64, P, I64, P, P]
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -168,8 +168,13 @@ def _idx(v, limit):
     return v
 
 
-def gemm(wtype: str, Q, D, S, raw, od: int, id_: int, tok=None, outs=None) -> np.ndarray:
-    """out[i][j] for t = tok[i], o = outs[j] (all tokens / outputs when None).
+def gemm(wtype: str, Q, D, S, raw, od: int, id_: int, tok=None, outs=None,
+         with_mag: bool = False):
+    """out[i][j] for t = tok[i], o = outs[j] (all tokens / outputs when None):
+    the plane's values D * q times the dequantised weight, with f64 block terms
+    and an f64 sum, stored as f32.  With with_mag, also returns mag [i][j] =
+    sum over blocks of |block term| (f64), the magnitude that any f32
+    evaluation of the per-block rescale rounds against.
 
     Q/D/S: the q8 plane (int8 [n][id], f32 [n][id/32], int32 [n][id/32]);
     raw: the [od][id/256] superblocks as bytes.
@@ -182,17 +187,19 @@ def gemm(wtype: str, Q, D, S, raw, od: int, id_: int, tok=None, outs=None) -> np
     assert raw.size == od * (id_ // 256) * bpb
     tok = _idx(tok, n); outs = _idx(outs, od)
     out = np.zeros((tok.size, outs.size), np.float32)
+    mag = np.zeros((tok.size, outs.size), np.float64) if with_mag else None
+    mp = _p(mag) if with_mag else None
     if wtype == "q4_K":
         S = np.ascontiguousarray(S, np.int32)
         _load().oracle_gemm_q4k(_p(Q), _p(D), _p(S), _p(raw), id_, _p(tok), tok.size,
-                                _p(outs), outs.size, _p(out))
+                                _p(outs), outs.size, _p(out), mp)
     elif wtype == "q5_K":
         S = np.ascontiguousarray(S, np.int32)
         _load().oracle_gemm_q5k(_p(Q), _p(D), _p(S), _p(raw), id_, _p(tok), tok.size,
-                                _p(outs), outs.size, _p(out))
+                                _p(outs), outs.size, _p(out), mp)
     elif wtype == "q6_K":
         _load().oracle_gemm_q6k(_p(Q), _p(D), _p(raw), id_, _p(tok), tok.size,
-                                _p(outs), outs.size, _p(out))
+                                _p(outs), outs.size, _p(out), mp)
     else:
         raise ValueError(wtype)
-    return out
+    return (out, mag) if with_mag else out

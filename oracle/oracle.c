@@ -259,16 +259,22 @@ void oracle_quantize(const float* y, int64_t n, int64_t d,
  * plane, k32 chunks].  For output (t, o) and 32-block b in superblock sb
  * with sub-block j:
  *   I    = sum_{k in b} q_w[o][k] * Q[t][k]                (exact int32)
- *   term = (D[t][b] * (d * sc_j)) * I  -  (D[t][b] * S[t][b]) * (dmin * m_j)
- * each term evaluated in f32, summed over blocks in f64, stored as f32.
- * (d*sc_j and dmin*m_j are exact in f32: 11-bit times 6-bit.)
- * Computes out[i][j] for t = tok[i], o = outs[j]; out is [ntok][nout].
- * Q: [*][id] int8 row-major, D/S: [*][id/32]; raw: [od][id/256] superblocks.
+ *   term = D[t][b] * (d * sc_j) * I  -  D[t][b] * S[t][b] * (dmin * m_j)
+ * The factoring per block is exact, so the result is, up to rounding, the
+ * product of the plane's values D * q with the dequantised weight; the oracle
+ * evaluates that plain definition with every term in f64 (d*sc_j, dmin*m_j and
+ * D*d*sc_j are exact; the product with I rounds once, at 2^-53), sums the
+ * terms over blocks in f64 and stores the sum as f32.  mag (may be NULL)
+ * receives, per output, the sum over blocks of |first part| + |second part|:
+ * the magnitude any f32 evaluation of the per-block rescale rounds against.
+ * Computes out[i][j] for t = tok[i], o = outs[j]; out and mag are
+ * [ntok][nout].  Q: [*][id] int8 row-major, D/S: [*][id/32]; raw: [od][id/256]
+ * superblocks.
  */
 void oracle_gemm_q4k(const int8_t* Q, const float* D, const int32_t* S,
                      const uint8_t* raw, int64_t id,
                      const int64_t* tok, int64_t ntok,
-                     const int64_t* outs, int64_t nout, float* out)
+                     const int64_t* outs, int64_t nout, float* out, double* mag)
 {
     int64_t nb = id / QK, nsb = id / QKK;
     #pragma omp parallel for schedule(dynamic, 1)
@@ -276,7 +282,7 @@ void oracle_gemm_q4k(const int8_t* Q, const float* D, const int32_t* S,
         int64_t o = outs[jo];
         for (int64_t it = 0; it < ntok; it++) {
             int64_t t = tok[it];
-            double acc = 0.0;
+            double acc = 0.0, sabs = 0.0;
             for (int64_t sb = 0; sb < nsb; sb++) {
                 float d, dmin; uint8_t sc[8], mn[8], qw[256];
                 oracle_q4k_fields(raw + (o * nsb + sb) * Q4K_BYTES, &d, &dmin, sc, mn, qw);
@@ -285,15 +291,17 @@ void oracle_gemm_q4k(const int8_t* Q, const float* D, const int32_t* S,
                     int32_t I = 0;
                     for (int l = 0; l < QK; l++)
                         I += (int32_t)qw[j * QK + l] * (int32_t)Q[t * id + b * QK + l];
-                    float Da = D[t * nb + b];
-                    float dsc = d * (float)sc[j];
-                    float dmn = dmin * (float)mn[j];
-                    float t1 = (Da * dsc) * (float)I;
-                    float t2 = (Da * (float)S[t * nb + b]) * dmn;
-                    acc += (double)(t1 - t2);
+                    double Da = (double)D[t * nb + b];
+                    double dsc = (double)d * (double)sc[j];
+                    double dmn = (double)dmin * (double)mn[j];
+                    double t1 = Da * dsc * (double)I;
+                    double t2 = Da * (double)S[t * nb + b] * dmn;
+                    acc += t1 - t2;
+                    sabs += fabs(t1) + fabs(t2);
                 }
             }
             out[it * nout + jo] = (float)acc;
+            if (mag) mag[it * nout + jo] = sabs;
         }
     }
 }
@@ -302,13 +310,13 @@ void oracle_gemm_q4k(const int8_t* Q, const float* D, const int32_t* S,
  * q5_K integer-dot matmul over a q8 plane: the q4_K expression with 5-bit
  * quants (the one-token arm of d37 Excerpt B is this with ntok = 1):
  *   I    = sum_{k in b} q_w[o][k] * Q[t][k]                (exact int32)
- *   term = (D[t][b] * (d * sc_j)) * I  -  (D[t][b] * S[t][b]) * (dmin * m_j)
- * each term in f32, summed over blocks in f64, stored as f32.
+ *   term = D[t][b] * (d * sc_j) * I  -  D[t][b] * S[t][b] * (dmin * m_j)
+ * evaluated as for q4_K (f64 terms, f64 sum, f32 result; mag as there).
  */
 void oracle_gemm_q5k(const int8_t* Q, const float* D, const int32_t* S,
                      const uint8_t* raw, int64_t id,
                      const int64_t* tok, int64_t ntok,
-                     const int64_t* outs, int64_t nout, float* out)
+                     const int64_t* outs, int64_t nout, float* out, double* mag)
 {
     int64_t nb = id / QK, nsb = id / QKK;
     #pragma omp parallel for schedule(dynamic, 1)
@@ -316,7 +324,7 @@ void oracle_gemm_q5k(const int8_t* Q, const float* D, const int32_t* S,
         int64_t o = outs[jo];
         for (int64_t it = 0; it < ntok; it++) {
             int64_t t = tok[it];
-            double acc = 0.0;
+            double acc = 0.0, sabs = 0.0;
             for (int64_t sb = 0; sb < nsb; sb++) {
                 float d, dmin; uint8_t sc[8], mn[8], qw[256];
                 oracle_q5k_fields(raw + (o * nsb + sb) * Q5K_BYTES, &d, &dmin, sc, mn, qw);
@@ -325,15 +333,17 @@ void oracle_gemm_q5k(const int8_t* Q, const float* D, const int32_t* S,
                     int32_t I = 0;
                     for (int l = 0; l < QK; l++)
                         I += (int32_t)qw[j * QK + l] * (int32_t)Q[t * id + b * QK + l];
-                    float Da = D[t * nb + b];
-                    float dsc = d * (float)sc[j];
-                    float dmn = dmin * (float)mn[j];
-                    float t1 = (Da * dsc) * (float)I;
-                    float t2 = (Da * (float)S[t * nb + b]) * dmn;
-                    acc += (double)(t1 - t2);
+                    double Da = (double)D[t * nb + b];
+                    double dsc = (double)d * (double)sc[j];
+                    double dmn = (double)dmin * (double)mn[j];
+                    double t1 = Da * dsc * (double)I;
+                    double t2 = Da * (double)S[t * nb + b] * dmn;
+                    acc += t1 - t2;
+                    sabs += fabs(t1) + fabs(t2);
                 }
             }
             out[it * nout + jo] = (float)acc;
+            if (mag) mag[it * nout + jo] = sabs;
         }
     }
 }
@@ -344,14 +354,16 @@ void oracle_gemm_q5k(const int8_t* Q, const float* D, const int32_t* S,
  * own int8 scales sc0, sc1:
  *   I0, I1 = 16-element int dots of (q_w - 32) with Q     (exact int32)
  *   Ic     = sc0 * I0 + sc1 * I1                          (exact int32)
- *   term   = (D[t][b] * d) * Ic                           (f32)
- * summed over blocks in f64, stored as f32.  The one-token GEMV is this
- * function with ntok = 1 [d37 Excerpt A].
+ *   term   = D[t][b] * d * Ic
+ * in f64 (D*d exact, the product with Ic rounded once at 2^-53), summed over
+ * blocks in f64, stored as f32: the plain dequantised product, as for q4_K.
+ * mag (may be NULL) receives the sum of |term| per output.  The one-token
+ * GEMV is this function with ntok = 1 [d37 Excerpt A].
  */
 void oracle_gemm_q6k(const int8_t* Q, const float* D,
                      const uint8_t* raw, int64_t id,
                      const int64_t* tok, int64_t ntok,
-                     const int64_t* outs, int64_t nout, float* out)
+                     const int64_t* outs, int64_t nout, float* out, double* mag)
 {
     int64_t nb = id / QK, nsb = id / QKK;
     #pragma omp parallel for schedule(dynamic, 1)
@@ -359,7 +371,7 @@ void oracle_gemm_q6k(const int8_t* Q, const float* D,
         int64_t o = outs[jo];
         for (int64_t it = 0; it < ntok; it++) {
             int64_t t = tok[it];
-            double acc = 0.0;
+            double acc = 0.0, sabs = 0.0;
             for (int64_t sb = 0; sb < nsb; sb++) {
                 float d; int8_t sc[16]; uint8_t qw[256];
                 oracle_q6k_fields(raw + (o * nsb + sb) * Q6K_BYTES, &d, sc, qw);
@@ -371,11 +383,13 @@ void oracle_gemm_q6k(const int8_t* Q, const float* D,
                     for (int l = 16; l < 32; l++)
                         I1 += ((int32_t)qw[j * QK + l] - 32) * (int32_t)Q[t * id + b * QK + l];
                     int32_t Ic = (int32_t)sc[2 * j] * I0 + (int32_t)sc[2 * j + 1] * I1;
-                    float term = (D[t * nb + b] * d) * (float)Ic;
-                    acc += (double)term;
+                    double term = (double)D[t * nb + b] * (double)d * (double)Ic;
+                    acc += term;
+                    sabs += fabs(term);
                 }
             }
             out[it * nout + jo] = (float)acc;
+            if (mag) mag[it * nout + jo] = sabs;
         }
     }
 }

@@ -4,15 +4,22 @@ The chain of two layers (RMSNorm -> plane -> q, k, v; standalone quantise ->
 o; RMSNorm -> plane -> gate, up; SwiGLU -> plane -> down) is captured once and
 replayed several times.  Between replays the inputs are rewritten in place and
 the same chain is run eagerly; every replay must equal the eager run bit for
-bit (same kernels, same inputs).  The launch census of the capture comes from
-mmq_stats.  Capture rules tested: nothing is allocated during a capture (a
-plane that would need a bigger slot is refused before anything is recorded).
+bit (same kernels, same inputs), and the last replay's final layer is checked
+against the CPU oracle: the o projection on the oracle's own quantisation of
+its input, every matmul on the exported plane, and the SwiGLU plane against
+the oracle's SwiGLU of the replayed gate/up outputs.  The launch census of the
+capture comes from mmq_stats.  Capture rules tested: nothing is allocated
+during a capture (a plane that would need a bigger slot is refused before
+anything is recorded).
 """
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import quantized_matmul_rmsnorm_amd as mmq
 import synth
+from tests.gpu_util import assert_fused_close, assert_gemm_close, export_plane, gemm_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +51,13 @@ class Chain:
         self.out = [{name: e(N, od) for name, _, od, _ in GEMMS} for _ in range(LAYERS)]
 
     def set_inputs(self, seed):
+        self.host = []
         for l, L in enumerate(self.layers):
+            h = {}
             for t in ("x_attn", "attn_out", "x_ffn"):
-                a = synth.activations(synth.rng_for(f"graph{seed}", l, t), N, HID)
-                L[t].copy_(torch.from_numpy(a))
+                h[t] = synth.activations(synth.rng_for(f"graph{seed}", l, t), N, HID)
+                L[t].copy_(torch.from_numpy(h[t]))
+            self.host.append(h)
         torch.cuda.synchronize()
 
     def step(self):
@@ -112,6 +122,29 @@ def test_chain_graph_replays_equal_eager():
                     assert torch.isfinite(ref[l][name]).all()
             # the inputs changed, so the outputs must have too
             assert not torch.equal(got[0]["q"], ch.out[0]["q"].new_zeros(ch.out[0]["q"].shape))
+        # the last replay's final layer against the oracle; its planes come from
+        # one more eager run on the same inputs (the outputs were just found
+        # equal bit for bit), left in the cache for the export
+        ch.step()
+        torch.cuda.synchronize()
+        l = LAYERS - 1
+        rep_out = {k: v.cpu().numpy() for k, v in got[l].items()}
+        raws = {name: synth.weights(wt, synth.rng_for("graph", l, name), od, id_)
+                for name, wt, od, id_ in GEMMS}
+        planes = {"attn": export_plane(ch.ctx, ch.y_attn, N, HID),
+                  "o": export_plane(ch.ctx, ch.layers[l]["attn_out"], N, HID),
+                  "ffn": export_plane(ch.ctx, ch.y_ffn, N, HID),
+                  "sw": export_plane(ch.ctx, ch.y_sw, N, FFN)}
+        src = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "ffn", "up": "ffn",
+               "down": "sw"}
+        for name, wt, od, id_ in GEMMS:
+            ref = gemm_ref(wt, *planes[src[name]], raws[name], od, id_)
+            assert_gemm_close(rep_out[name], ref, f"replayed {name}")
+        own = oracle.quantize(ch.host[l]["attn_out"])    # no GPU plane involved
+        assert_gemm_close(rep_out["o"], gemm_ref("q4_K", *own, raws["o"], HID, HID),
+                          "replayed o on the oracle plane")
+        assert_fused_close(planes["sw"], oracle.quantize(oracle.swiglu(rep_out["gate"], rep_out["up"])),
+                           what="replayed swiglu plane")
         del g
     finally:
         ch.close()

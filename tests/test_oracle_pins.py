@@ -346,8 +346,7 @@ def test_gemm_q4k_vs_bruteforce_f64(n, od, id_):
     Q, D, S = _plane(rng, n, id_)
     a = Q.astype(np.float64) * np.repeat(D.astype(np.float64), 32, axis=1)
     ref = a @ w.T
-    got = oracle.gemm("q4_K", Q, D, S, raw, od, id_)
-    # bound: each per-block term takes <= 3 f32 roundings, the f32 store one more
+    got, gmag = oracle.gemm("q4_K", Q, D, S, raw, od, id_, with_mag=True)
     nsb = id_ // 256
     mag = np.zeros_like(ref)
     for o in range(od):
@@ -355,7 +354,10 @@ def test_gemm_q4k_vs_bruteforce_f64(n, od, id_):
             d, dm, sc, mn, q = oracle.q4k_fields(raw[o, s * 144:(s + 1) * 144])
             j = np.arange(256) // 32
             mag[:, o] += np.abs(a[:, s * 256:(s + 1) * 256]) @ (d * sc[j] * q + dm * mn[j])
-    assert np.all(np.abs(got - ref) <= 4 * U24 * mag + U24 * np.abs(ref) + 1e-30)
+    # the plain product up to its one f32 rounding (f64 terms round at 2^-53)
+    assert np.all(np.abs(got - ref) <= U24 * np.abs(ref) + 2.0 ** -50 * mag + 1e-30)
+    # sum |block term| lies between |sum| and the sum of |element products|
+    assert np.all(gmag >= np.abs(ref) * (1 - 1e-12)) and np.all(gmag <= mag * (1 + 1e-12))
     # a dropped min term or sign flip would be far outside that bound
     assert np.abs(ref).max() > 1000 * (4 * U24 * mag.max())
 
@@ -367,9 +369,10 @@ def test_gemm_q6k_vs_bruteforce_f64(n, od, id_):
     Q, D, S = _plane(rng, n, id_)
     a = Q.astype(np.float64) * np.repeat(D.astype(np.float64), 32, axis=1)
     ref = a @ w.T
-    got = oracle.gemm("q6_K", Q, D, S, raw, od, id_)
+    got, gmag = oracle.gemm("q6_K", Q, D, S, raw, od, id_, with_mag=True)
     mag = np.abs(a) @ np.abs(w).T
-    assert np.all(np.abs(got - ref) <= 3 * U24 * mag + U24 * np.abs(ref) + 1e-30)
+    assert np.all(np.abs(got - ref) <= U24 * np.abs(ref) + 2.0 ** -50 * mag + 1e-30)
+    assert np.all(gmag >= np.abs(ref) * (1 - 1e-12)) and np.all(gmag <= mag * (1 + 1e-12))
 
 
 @pytest.mark.parametrize("n,od,id_", [(1, 3, 256), (4, 6, 512), (8, 16, 256)])
@@ -379,7 +382,7 @@ def test_gemm_q5k_vs_bruteforce_f64(n, od, id_):
     Q, D, S = _plane(rng, n, id_)
     a = Q.astype(np.float64) * np.repeat(D.astype(np.float64), 32, axis=1)
     ref = a @ w.T
-    got = oracle.gemm("q5_K", Q, D, S, raw, od, id_)
+    got, gmag = oracle.gemm("q5_K", Q, D, S, raw, od, id_, with_mag=True)
     nsb = id_ // 256
     mag = np.zeros_like(ref)
     for o in range(od):
@@ -387,7 +390,8 @@ def test_gemm_q5k_vs_bruteforce_f64(n, od, id_):
             d, dm, sc, mn, q = oracle.q5k_fields(raw[o, s * 176:(s + 1) * 176])
             j = np.arange(256) // 32
             mag[:, o] += np.abs(a[:, s * 256:(s + 1) * 256]) @ (d * sc[j] * q + dm * mn[j])
-    assert np.all(np.abs(got - ref) <= 4 * U24 * mag + U24 * np.abs(ref) + 1e-30)
+    assert np.all(np.abs(got - ref) <= U24 * np.abs(ref) + 2.0 ** -50 * mag + 1e-30)
+    assert np.all(gmag >= np.abs(ref) * (1 - 1e-12)) and np.all(gmag <= mag * (1 + 1e-12))
     assert np.abs(ref).max() > 1000 * (4 * U24 * mag.max())
 
 
