@@ -66,12 +66,18 @@ def log(msg):
 
 
 class Chain:
-    def __init__(self, mmq, torch, synth, layers):
+    """The 7B chain on one context: per layer its registered weights, inputs
+    and RMSNorm weights (seeded by the layer index), shared producer output
+    buffers (the plane keys) and matmul outputs.  `layer_ids` picks which
+    layers of the 28 are built (all of them for the timed step)."""
+
+    def __init__(self, mmq, torch, synth, layers, layer_ids=None):
         self.mmq, self.torch = mmq, torch
         self.ctx = mmq.mmq_create(0, 0)
         self.layers = []
         dev = "cuda"
-        for l in range(layers):
+        self.layer_ids = list(range(layers)) if layer_ids is None else list(layer_ids)
+        for l in self.layer_ids:
             L = {}
             for name, wt, od, id_, _ in LAYER_GEMMS:
                 raw = synth.weights(wt, synth.rng_for("chain7b", l, name), od, id_)
@@ -84,8 +90,8 @@ class Chain:
             for t in ("norm_attn", "norm_ffn"):
                 L[t] = torch.from_numpy(synth.rms_weight(synth.rng_for("chain7b", l, t), HIDDEN)).to(dev)
             self.layers.append(L)
-            if l % 7 == 6:
-                log(f"registered layer {l + 1}/{layers}")
+            if len(self.layers) % 7 == 0:
+                log(f"registered {len(self.layers)}/{len(self.layer_ids)} layers")
         e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
         # producer output buffers: allocated (they are the plane keys) but never written
         self.y_attn, self.y_ffn, self.y_sw = e(TOKENS, HIDDEN), e(TOKENS, HIDDEN), e(TOKENS, FFN)
@@ -108,23 +114,33 @@ class Chain:
             end.record()
 
     def step(self):
-        m, c, n = self.mmq, self.ctx, TOKENS
         for L in self.layers:
-            self._run("quant_rms", m.mmq_quant_rms, c, L["x_attn"], L["norm_attn"], self.y_attn, n,
-                      HIDDEN, 1e-6, 0)
-            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["q"], self.y_attn, n, self.out["q"])
-            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["k"], self.y_attn, n, self.out["k"])
-            self._run("gemm_q6k", m.mmq_gemm_q6k, c, L["v"], self.y_attn, n, self.out["v"])
-            self._run("quant_f32", m.mmq_quant_f32, c, L["attn_out"], n, HIDDEN)
-            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["o"], L["attn_out"], n, self.out["o"])
-            self._run("quant_rms", m.mmq_quant_rms, c, L["x_ffn"], L["norm_ffn"], self.y_ffn, n,
-                      HIDDEN, 1e-6, 0)
-            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["gate"], self.y_ffn, n, self.out["gate"])
-            self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["up"], self.y_ffn, n, self.out["up"])
-            self._run("quant_swiglu", m.mmq_quant_swiglu, c, self.out["gate"], self.out["up"],
-                      self.y_sw, n, FFN, 0)
-            self._run("gemm_q6k", m.mmq_gemm_q6k, c, L["down"], self.y_sw, n, self.out["down"])
-        m.mmq_cache_clear(c)
+            self.run_layer(L)
+        self.mmq.mmq_cache_clear(self.ctx)
+
+    def run_layer(self, L):
+        """One layer's eleven calls, in chain order, on the current stream."""
+        m, c, n = self.mmq, self.ctx, TOKENS
+        self._run("quant_rms", m.mmq_quant_rms, c, L["x_attn"], L["norm_attn"], self.y_attn, n,
+                  HIDDEN, 1e-6, 0)
+        self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["q"], self.y_attn, n, self.out["q"])
+        self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["k"], self.y_attn, n, self.out["k"])
+        self._run("gemm_q6k", m.mmq_gemm_q6k, c, L["v"], self.y_attn, n, self.out["v"])
+        self._run("quant_f32", m.mmq_quant_f32, c, L["attn_out"], n, HIDDEN)
+        self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["o"], L["attn_out"], n, self.out["o"])
+        self._run("quant_rms", m.mmq_quant_rms, c, L["x_ffn"], L["norm_ffn"], self.y_ffn, n,
+                  HIDDEN, 1e-6, 0)
+        self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["gate"], self.y_ffn, n, self.out["gate"])
+        self._run("gemm_q4k", m.mmq_gemm_q4k, c, L["up"], self.y_ffn, n, self.out["up"])
+        self._run("quant_swiglu", m.mmq_quant_swiglu, c, self.out["gate"], self.out["up"],
+                  self.y_sw, n, FFN, 0)
+        self._run("gemm_q6k", m.mmq_gemm_q6k, c, L["down"], self.y_sw, n, self.out["down"])
+
+    def close(self):
+        for L in self.layers:
+            for name, _, _, _, _ in LAYER_GEMMS:
+                self.mmq.mmq_weight_free(L[name])
+        self.mmq.mmq_destroy(self.ctx)
 
     def class_times_ms(self):
         return {k: sum(a.elapsed_time(b) for a, b in v) for k, v in self.events.items()}, \
@@ -400,11 +416,51 @@ def _oracle_decode_full():
     return byts / dt / 1e9, dt
 
 
+def _oracle_tiny_full():
+    """The CPU oracle on the tiny workload in full: RMSNorm of 32 x 256, its
+    plane, and the q4_K 512 x 256 matmul; returns (TOPS, seconds)."""
+    import oracle
+    import synth
+    x = synth.activations(synth.rng_for("tiny", 0, "x"), 32, 256)
+    wn = synth.rms_weight(synth.rng_for("tiny", 0, "norm"), 256)
+    raw = synth.q4k_weights(synth.rng_for("tiny", 0, "w"), 512, 256)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.gemm("q4_K", *oracle.quantize(oracle.rmsnorm(x, wn, 1e-6)), raw, 512, 256)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt > 0.5:
+            break
+    return 2 * 32 * 512 * 256 * reps / dt / 1e12, dt / reps
+
+
+def _oracle_producers_full():
+    """The CPU oracle's producers on the 7B chain's full shapes (RMSNorm then
+    quantise of 3314 x 3584, standalone quantise of 3314 x 3584, SwiGLU then
+    quantise of 3314 x 18944); returns {name: (GB/s of algorithmic bytes, s)}."""
+    import oracle
+    _, x, a, _, n1, _ = _layer0_inputs()
+    import synth
+    g = synth.activations(synth.rng_for("chain7b", 0, "gate_cpu"), TOKENS, FFN)
+    u = synth.activations(synth.rng_for("chain7b", 0, "up_cpu"), TOKENS, FFN)
+    res = {}
+    for name, fn, nbytes in (
+            ("quant_rms", lambda: oracle.quantize(oracle.rmsnorm(x, n1, 1e-6)), TOKENS * HIDDEN * 5.25),
+            ("quant_f32", lambda: oracle.quantize(a), TOKENS * HIDDEN * 5.25),
+            ("quant_swiglu", lambda: oracle.quantize(oracle.swiglu(g, u)), TOKENS * FFN * 9.25)):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        res[name] = {"GB_s": round(nbytes / dt / 1e9, 3), "seconds": round(dt, 3)}
+    return res
+
+
 def cpu_baseline(seconds: float):
     """The CPU oracle (as it is) on a bounded sample of one layer of the chain,
     reported in the chain's unit (TOPS) on all the threads it uses; beside it,
-    the same sample on one thread (a shorter one) and the 14B decode GEMV step
-    in full (GB/s)."""
+    the same sample on one thread (a shorter one), the tiny workload, the
+    producers at the 7B shapes and the 14B decode GEMV step, each in full."""
     import oracle
     tops, tok_done, t_used = _oracle_layer_sample(seconds)
     n_all = oracle.threads()
@@ -414,7 +470,10 @@ def cpu_baseline(seconds: float):
     finally:
         oracle.set_threads(n_all)
     dec_gbs, dec_s = _oracle_decode_full()
+    tiny_tops, tiny_s = _oracle_tiny_full()
+    prod = _oracle_producers_full()
     return {"value": round(tops, 6), "unit": "TOPS", "cores": n_all,
+            "host_cpus_available": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"layer 0 of the chain (both RMSNorm producers, the standalone quantise, "
                       f"SwiGLU and all 7 matmuls) for {tok_done} of {TOKENS} tokens, "
@@ -424,7 +483,10 @@ def cpu_baseline(seconds: float):
                            "seconds": round(t1, 2)},
             "decode_gemv_full": {"value": round(dec_gbs, 3), "unit": "GB/s", "seconds": round(dec_s, 2),
                                  "sample": "14B decode step in full: RMSNorm 5120 and SwiGLU 13824 "
-                                           "producers, attn_v, ffn_down and lm_head q6_K GEMVs"}}
+                                           "producers, attn_v, ffn_down and lm_head q6_K GEMVs"},
+            "tiny_full": {"value": round(tiny_tops, 6), "unit": "TOPS", "seconds_per_pass": round(tiny_s, 6),
+                          "sample": "32 x 256 RMSNorm -> plane -> q4_K 512 x 256 matmul, in full"},
+            "producers_full": prod}
 
 
 def measured_peaks(torch):
@@ -492,6 +554,7 @@ def measured_peaks(torch):
                          "int8_mfma_with_rescale_ms": round(t_i8, 4),
                          "int8_mfma_with_rescale_TOPs": round(mix_ops / (t_i8 * 1e-3) / 1e12, 1)}
     del mout
+    res["overlap_probes"] = overlap_probes(torch, lib, n_cu, stream)
     lib.mmq_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                   ctypes.c_void_p]
     lib.mmq_peak_read.restype = ctypes.c_int
@@ -524,6 +587,59 @@ def measured_peaks(torch):
     res["hbm_copy_GB_s"] = round(5 * 2 * nel * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del src, dst, out
     return res
+
+
+def overlap_probes(torch, lib, n_cu, stream, iters=4096):
+    """How far the matrix pipe and the VALU overlap, by variant (libmmq_peak's
+    probe table): per 32-block and wave, 2 f16 32x32x16 MFMAs and 16 rescale
+    FMAs per output tile, one workgroup per CU with 1, 2 or 4 waves per SIMD;
+    the FMAs reading the previous block's MFMA results (the matmul's flow) or
+    registers no MFMA writes (independent); both from one wave, or split so
+    that one wave of each SIMD pair issues only MFMAs and the other only FMAs.
+    hidden_frac = (t_mfma_only + t_fma_only - t_both) / min(t_mfma_only,
+    t_fma_only): 0 when the two run one after the other, 1 when the shorter
+    one is hidden completely.  A split variant is set against half of the
+    one-pipe times of its own wave count (half the waves issue each kind)."""
+    import ctypes
+    lib.mmq_peak_probe_count.restype = ctypes.c_int
+    lib.mmq_peak_probe_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_int)]
+    lib.mmq_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.mmq_peak_probe.restype = ctypes.c_int
+    out = torch.empty(n_cu * 1024, dtype=torch.float32, device="cuda")
+    times, info = {}, {}
+    for i in range(lib.mmq_peak_probe_count()):
+        nm, th, ti, mw = ctypes.c_char_p(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        if lib.mmq_peak_probe_info(i, ctypes.byref(nm), ctypes.byref(th), ctypes.byref(ti),
+                                   ctypes.byref(mw)) != 0:
+            raise RuntimeError("probe info")
+        name = nm.value.decode()
+        if lib.mmq_peak_probe(i, out.data_ptr(), n_cu, iters, stream.cuda_stream) != 0:
+            raise RuntimeError(f"probe {name}: launch failed")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            lib.mmq_peak_probe(i, out.data_ptr(), n_cu, iters, stream.cuda_stream)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        ops = n_cu * mw.value * iters * 2 * ti.value * 2 * (2 * 32 * 32 * 16)
+        times[name] = ms
+        info[name] = {"ms": round(ms, 4), "threads": th.value,
+                      "mfma_TFLOPs": round(ops / (ms * 1e-3) / 1e12, 1) if ops else None}
+    del out
+    for name, rec in info.items():
+        pre = name.split("_both")[0].split("_split")[0]
+        tm, tv = times.get(pre + "_mfma_only"), times.get(pre + "_fma_only")
+        if tm is None or tv is None or name.endswith("_only"):
+            continue
+        if "_split" in name:
+            tm, tv = tm / 2, tv / 2
+        rec["hidden_frac"] = round((tm + tv - times[name]) / min(tm, tv), 3)
+    return info
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -628,6 +744,18 @@ def main():
     cls_ms, cls_n = chain.class_times_ms()
     chain.events = None
     st1 = mmq.mmq_stats(chain.ctx)
+    # device memory both ways: what the library holds (registered tiles,
+    # planes and split-K scratch) against the raw superblocks it was given
+    raw_bytes = args.layers * sum(od * id_ // 256 * (144 if wt == "q4_K" else 210)
+                                  for _, wt, od, id_, _ in LAYER_GEMMS)
+    memory = {"raw_superblock_bytes": raw_bytes, "registered_weight_bytes": st1["weight_bytes"],
+              "registered_over_raw": round(st1["weight_bytes"] / raw_bytes, 3),
+              "plane_and_scratch_bytes": st1["plane_bytes"],
+              "activation_and_output_bytes": sum(
+                  t.numel() * 4 for L in chain.layers for k, t in L.items()
+                  if k in ("x_attn", "attn_out", "x_ffn", "norm_attn", "norm_ffn")) +
+                  sum(t.numel() * 4 for t in (chain.y_attn, chain.y_ffn, chain.y_sw)) +
+                  sum(t.numel() * 4 for t in chain.out.values())}
     ops = chain_ops(TOKENS, args.layers)
     tops = ops / (ms_step * 1e-3) / 1e12
     log(f"{ms_step:.2f} ms/step ({wall / args.steps * 1e3:.2f} ms wall), {tops:.1f} TOPS")
@@ -705,6 +833,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
+        "mfma_instruction": "v_mfma_f32_32x32x16_f16 on exact integer operands (int8 codes, "
+                            "integer weight values); integer block dots, f32 rescale",
         "data": "synthetic",
         "config": {"workload": "7B prefill matmul chain: 28 layers x (RMSNorm->q8 plane->q,k,v; "
                                "quantise->o; RMSNorm->gate,up; SwiGLU->down), skip-write planes",
@@ -715,7 +845,7 @@ def main():
         "instrumented_ms_per_step": round(ms_step_instr, 3),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "unit": "TOPS", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "kernel": "k_gemm_da<true> (q4_K)",
                      "ops_per_launch": q4_ops_launch,
@@ -728,6 +858,7 @@ def main():
         "kernels": kernels,
         "graph": graph_rec,
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
+        "memory": memory,
         "decode_gemv": decode,
         "small_n_us": small,
         "decode_crossover_us": crossover,

@@ -50,6 +50,25 @@ int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t stream);
  * code of the launch. */
 int mmq_peak_mix(float* out, int blocks, int iters, int mode, hipStream_t stream);
 
+/* Overlap probes: variants of the per-block mix above that show what lets the
+ * matrix pipe and the VALU run at the same time.  Each probe is one kernel;
+ * per 32-block every wave issues, per output tile, 2 f16 32x32x16 MFMAs and
+ * 16 rescale FMAs, or only one of the two kinds, or (split probes) one wave
+ * of each SIMD pair issues only the MFMAs and the other only the FMAs; the
+ * FMAs read the previous block's MFMA results or registers no MFMA writes.
+ * mmq_peak_probe_count() gives the number of probes; mmq_peak_probe_info(i,
+ * ...) its name, threads per workgroup, output tiles per wave and MFMA-issuing
+ * waves per workgroup (0..count-1, else -1); mmq_peak_probe(i, out, blocks,
+ * iters, stream) launches probe i with `blocks` workgroups (one per CU gives
+ * threads/256 waves per SIMD) running `iters` rounds of 2 blocks, writing
+ * blocks * threads floats to the caller's device buffer `out`.  A launch
+ * performs blocks * mfma_waves * iters * 2 * tiles * 2 * (2*32*32*16) f16
+ * operations.  Returns 0, -1 for an invalid argument (nothing launched), or
+ * the HIP error code of the launch. */
+int mmq_peak_probe_count(void);
+int mmq_peak_probe_info(int i, const char** name, int* threads, int* tiles, int* mfma_waves);
+int mmq_peak_probe(int i, float* out, int blocks, int iters, hipStream_t stream);
+
 /* Read-only HBM stream: reads `bytes` (a multiple of 16, > 0) of the device
  * buffer `src` once with 16-byte non-temporal loads, `blocks` workgroups of
  * 256 threads walking it grid-stride, and writes one folded value per thread

@@ -175,6 +175,116 @@ __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int i
     out[(int64_t)blockIdx.x * blockDim.x + t] = v;
 }
 
+// Overlap probes: what lets the matrix pipe and the VALU run at the same time.
+// Per 32-block each wave issues, for each of its TILES output tiles, two
+// v_mfma_f32_32x32x16_f16 (the block's two K-steps) and 16 FMAs (the tile's
+// rescale, acc += s * X).  Variants:
+//   MODE 0: MFMAs only; 1: FMAs only; 2: both from the same wave, the block's
+//   MFMAs then the previous block's FMAs (the matmul's order); 3: split
+//   waves -- in every SIMD one wave issues only the MFMAs and the other only
+//   the FMAs (waves w and w + 4 of a 512-thread workgroup share a SIMD).
+//   SRC 0: the FMAs read the previous block's MFMA results (the matmul's data
+//   flow); 1: they read registers no MFMA writes, and no VALU reads an MFMA
+//   result (the two pipes share nothing but the issue port and the register
+//   file).
+//   ZERO 1: each block's first K-step starts from zero (as the matmul does);
+//   0: it accumulates onto the buffer's old contents.
+// BS threads per workgroup and one workgroup per CU give BS / 256 waves per
+// SIMD.  Work per launch: blocks * (BS / 64) * iters * 2 blocks * TILES * 2
+// MFMAs of 2*32*32*16 operations (MODE 3: half the waves issue them).
+template <int BS, int TILES, int MODE, int SRC, int ZERO>
+__global__ __launch_bounds__(BS) void k_mix_probe(float* __restrict__ out, int iters, float s) {
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    // MODE 3: the first wave of each SIMD pair issues MFMAs, the second FMAs
+    const bool do_m = MODE == 0 || MODE == 2 || (MODE == 3 && ((wave >> 2) & 1) == 0);
+    const bool do_v = MODE == 1 || MODE == 2 || (MODE == 3 && ((wave >> 2) & 1) == 1);
+    half8 a0, b0, a1, b1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a0[i] = (_Float16)((t + i) & 7);
+        b0[i] = (_Float16)((t * 3 + i) & 7);
+        a1[i] = (_Float16)((t + 2 * i) & 7);
+        b1[i] = (_Float16)((t * 5 + i) & 7);
+    }
+    f32x16 XA[TILES], XB[TILES], acc[TILES], Y[TILES];
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            XA[i][r] = (float)(r + i);
+            XB[i][r] = (float)(r - i);
+            Y[i][r] = (float)(r * 3 - i);
+            acc[i][r] = 0.0f;
+        }
+    auto block = [&](f32x16* Xw, const f32x16* Xr) {
+        if (do_m) {
+            // operands opaque to the compiler, so a zero-started MFMA is not hoisted
+            asm volatile("" : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1));
+#pragma unroll
+            for (int i = 0; i < TILES; ++i) {
+                const f32x16 zero = {};
+                Xw[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i ? a1 : a0, i ? b1 : b0,
+                                                               ZERO ? zero : Xw[i], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < TILES; ++i)
+                Xw[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i ? b1 : b0, i ? a1 : a0, Xw[i], 0, 0, 0);
+        }
+        if (do_v) {
+#pragma unroll
+            for (int i = 0; i < TILES; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(s, SRC ? Y[i][r] : Xr[i][r], acc[i][r]);
+        }
+        if (MODE == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * TILES, 0);   // the block's MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x002, 16 * TILES, 0);  // then the rescale FMAs
+        }
+    };
+    for (int it = 0; it < iters; ++it) {
+        block(XA, XB);
+        block(XB, XA);
+        if (do_v && (SRC || !do_m)) {   // the FMAs' inputs change every round
+            if (SRC) { Y[0][0] += 1.0f; Y[TILES - 1][1] -= 1.0f; }
+            else { XA[0][0] += 1.0f; XB[TILES - 1][0] -= 1.0f; }
+        }
+    }
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TILES; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v += XA[i][r] + XB[i][r] + acc[i][r] + Y[i][r];
+    out[(int64_t)blockIdx.x * blockDim.x + t] = v;
+}
+
+struct ProbeInfo {
+    const char* name;
+    int bs, tiles, mode, src, zero;
+    void (*fn)(float*, int, float);
+};
+
+#define PROBE(BS, T, M, S, Z, NAME) {NAME, BS, T, M, S, Z, k_mix_probe<BS, T, M, S, Z>}
+const ProbeInfo kProbes[] = {
+    PROBE(512, 2, 0, 0, 1, "w2_t2_mfma_only"),
+    PROBE(512, 2, 1, 0, 1, "w2_t2_fma_only"),
+    PROBE(512, 2, 2, 0, 1, "w2_t2_both_matmul_flow"),
+    PROBE(512, 2, 2, 0, 0, "w2_t2_both_matmul_flow_accumulating"),
+    PROBE(512, 2, 2, 1, 1, "w2_t2_both_independent"),
+    PROBE(512, 2, 3, 1, 1, "w2_t2_split_waves"),
+    PROBE(256, 2, 0, 0, 1, "w1_t2_mfma_only"),
+    PROBE(256, 2, 1, 0, 1, "w1_t2_fma_only"),
+    PROBE(256, 2, 2, 0, 1, "w1_t2_both_matmul_flow"),
+    PROBE(256, 2, 2, 1, 1, "w1_t2_both_independent"),
+    PROBE(1024, 1, 0, 0, 1, "w4_t1_mfma_only"),
+    PROBE(1024, 1, 1, 0, 1, "w4_t1_fma_only"),
+    PROBE(1024, 1, 2, 0, 1, "w4_t1_both_matmul_flow"),
+    PROBE(1024, 1, 2, 1, 1, "w4_t1_both_independent"),
+    PROBE(1024, 1, 3, 1, 1, "w4_t1_split_waves"),
+};
+#undef PROBE
+constexpr int kNumProbes = sizeof(kProbes) / sizeof(kProbes[0]);
+
 // Read-only stream: each thread walks the buffer grid-stride in 16 B
 // non-temporal loads (4 in flight) and writes one folded value at the end.
 __global__ __launch_bounds__(256) void k_peak_read(const uint4* __restrict__ src, int64_t n16,
@@ -231,6 +341,31 @@ int mmq_peak_mix(float* out, int blocks, int iters, int mode, hipStream_t s) {
     else if (mode == 1) hipLaunchKernelGGL(k_peak_mix<1>, g, b, 0, s, out, iters, 0.999f);
     else if (mode == 2) hipLaunchKernelGGL(k_peak_mix<2>, g, b, 0, s, out, iters, 0.999f);
     else hipLaunchKernelGGL(k_peak_mix<3>, g, b, 0, s, out, iters, 0.999f);
+    return (int)hipGetLastError();
+}
+
+int mmq_peak_probe_count(void) { return kNumProbes; }
+
+// Description of probe i: name, threads per workgroup, tiles per wave, and the
+// number of waves per workgroup that issue MFMAs (for the operation count).
+// Returns 0, or -1 for an index out of range.
+int mmq_peak_probe_info(int i, const char** name, int* threads, int* tiles, int* mfma_waves) {
+    if (i < 0 || i >= kNumProbes || !name || !threads || !tiles || !mfma_waves) return -1;
+    const ProbeInfo& p = kProbes[i];
+    *name = p.name;
+    *threads = p.bs;
+    *tiles = p.tiles;
+    *mfma_waves = p.mode == 1 ? 0 : (p.mode == 3 ? p.bs / 128 : p.bs / 64);
+    return 0;
+}
+
+// out: device buffer of blocks * (threads of probe i) floats; blocks >= 1,
+// 1 <= iters <= 1 << 20.  Returns 0, -1 for bad arguments, or the HIP error.
+int mmq_peak_probe(int i, float* out, int blocks, int iters, hipStream_t s) {
+    if (i < 0 || i >= kNumProbes || out == nullptr || blocks < 1 || iters < 1 || iters > (1 << 20))
+        return -1;
+    hipLaunchKernelGGL(kProbes[i].fn, dim3((unsigned)blocks), dim3((unsigned)kProbes[i].bs), 0, s,
+                       out, iters, 0.999f);
     return (int)hipGetLastError();
 }
 

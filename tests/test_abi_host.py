@@ -45,6 +45,7 @@ def test_peak_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mmq_peak.h")).read(), flags=re.S)
     declared = sorted(set(re.findall(r"\b(mmq\w+)\s*\(", text)))
     assert declared == ["mmq_peak_chains", "mmq_peak_mfma_f16", "mmq_peak_mfma_i8", "mmq_peak_mix",
+                        "mmq_peak_probe", "mmq_peak_probe_count", "mmq_peak_probe_info",
                         "mmq_peak_read"]
     out = subprocess.run(["nm", "-D", "--defined-only", _b.LIB_PEAK], capture_output=True,
                          text=True, check=True).stdout
@@ -66,6 +67,27 @@ def test_peak_library_exports_its_header():
     assert mix(ctypes.c_void_p(0x1000), 1, (1 << 20) + 1, 0, None) == -1
     assert mix(ctypes.c_void_p(0x1000), 1, 1, 4, None) == -1
     assert mix(ctypes.c_void_p(0x1000), 1, 1, -1, None) == -1
+    count = lib.mmq_peak_probe_count()
+    assert count >= 10
+    info = lib.mmq_peak_probe_info
+    info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int),
+                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    names = set()
+    for i in range(count):
+        nm, th, ti, mw = ctypes.c_char_p(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        assert info(i, ctypes.byref(nm), ctypes.byref(th), ctypes.byref(ti), ctypes.byref(mw)) == 0
+        assert th.value in (256, 512, 1024) and ti.value in (1, 2) and 0 <= mw.value <= th.value // 64
+        names.add(nm.value.decode())
+    assert len(names) == count
+    nm, th, ti, mw = ctypes.c_char_p(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert info(count, ctypes.byref(nm), ctypes.byref(th), ctypes.byref(ti), ctypes.byref(mw)) == -1
+    probe = lib.mmq_peak_probe
+    probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert probe(-1, ctypes.c_void_p(0x1000), 1, 1, None) == -1
+    assert probe(count, ctypes.c_void_p(0x1000), 1, 1, None) == -1
+    assert probe(0, None, 1, 1, None) == -1
+    assert probe(0, ctypes.c_void_p(0x1000), 0, 1, None) == -1
+    assert probe(0, ctypes.c_void_p(0x1000), 1, (1 << 20) + 1, None) == -1
     rd = lib.mmq_peak_read
     rd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     assert rd(None, 16, ctypes.c_void_p(0x1000), 1, None) == -1
