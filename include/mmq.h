@@ -218,6 +218,25 @@ int mmq_gemm_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,
 int mmvq_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
              void* stream);
 
+/* ---- allocation-free one-token q6_K GEMV --------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  mmvq_q6k
+ * without any allocation: a plane recorded under (a, 1, cols) serves as in
+ * mmvq_q6k (a hit); on a miss, a (f32 [cols], written -- a dead key is refused
+ * with MMQ_E_DEAD_WRITE) is quantised into a one-token plane held in a device
+ * array of the library -- one copy per GPU, resolved when a context is
+ * created on that GPU and kept until the process ends -- and nothing is
+ * recorded in the cache.  cols <= MMQ_NOALLOC_MAX_COLS, else MMQ_E_SHAPE
+ * before any launch.  The call never allocates or frees device memory.
+ * Every call on one GPU shares that one array: calls in flight at the same
+ * time on one GPU (on different streams, contexts or threads) race on it;
+ * calls on one stream are ordered and never do.  The plane row is rewritten
+ * whole by every miss, so nothing needs clearing between calls.
+ * w, a, out and the other errors as for mmvq_q6k. */
+#define MMQ_NOALLOC_MAX_COLS 32768
+int mmvq_q6k_noalloc(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
+                     void* stream);
+
 /* One-token q4_K GEMV, the sibling decode arm of the same routing
  * [d37 Excerpt B: each K-quant type has its own one-token arm].  Per
  * 32-block: D * (d*sc_j * sum(q_w * q) - dmin*m_j * S).  w must be

@@ -39,13 +39,14 @@ MMQ_PLANE_ROWS = 32
 MMQ_WRITE_AUTO = -1
 MMQ_FOREIGN_F32 = 1
 MMQ_FOREIGN_QUANT = 2
+MMQ_NOALLOC_MAX_COLS = 32768
 
 # Every symbol include/mmq.h declares (checked by the CPU tests).
 EXPORTS = [
     "mmq_create", "mmq_destroy", "mmq_last_error", "mmq_set_scratch_cap", "mmq_plane_rows",
     "mmq_register_weight", "mmq_weight_free", "mmq_weight_bytes",
     "mmq_quant_rms", "mmq_quant_swiglu", "mmq_quant_f32",
-    "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k",
+    "mmq_gemm_q4k", "mmq_gemm_q6k", "mmvq_q6k", "mmvq_q6k_noalloc", "mmvq_q4k", "mmvq_q5k",
     "mmq_gemv_q6k_f32", "mmq_decode_q6k",
     "mmq_register_foreign_consumer", "mmq_plane_only",
     "mmq_cache_clear", "mmq_cache_invalidate", "mmq_plane_export", "mmq_stats",
@@ -101,6 +102,7 @@ def _load():
         "mmq_gemm_q4k": (I, [P, P, P, I64, P, P]),
         "mmq_gemm_q6k": (I, [P, P, P, I64, P, P]),
         "mmvq_q6k": (I, [P, P, P, P, P]),
+        "mmvq_q6k_noalloc": (I, [P, P, P, P, P]),
         "mmvq_q4k": (I, [P, P, P, P, P]),
         "mmvq_q5k": (I, [P, P, P, P, P]),
         "mmq_gemv_q6k_f32": (I, [P, P, P, P, P]),
@@ -243,6 +245,11 @@ def mmq_gemm_q6k(ctx, w, a, n: int, out, stream=None):
 def mmvq_q6k(ctx, w, a, out, stream=None):
     f = _f32() if not isinstance(a, int) else None
     return _check(lib.mmvq_q6k(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
+
+
+def mmvq_q6k_noalloc(ctx, w, a, out, stream=None):
+    f = _f32() if not isinstance(a, int) else None
+    return _check(lib.mmvq_q6k_noalloc(ctx, w, _ptr(a, f), _ptr(out, f), _stream(stream)))
 
 
 def mmvq_q4k(ctx, w, a, out, stream=None):

@@ -25,6 +25,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -32,6 +34,15 @@
 #include "mmq_internal.h"
 
 using namespace mmq;
+
+// The one-token plane of the allocation-free decode call (mmvq_q6k_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends.
+// Layout as a plane of one row: codes [kStaticMaxCols], then the (D, S) pairs
+// at byte kStaticMaxCols.  Host code never uses the array's name as an
+// address: the per-device address comes from hipGetSymbolAddress.
+constexpr int64_t kStaticMaxCols = MMQ_NOALLOC_MAX_COLS;
+constexpr int64_t kStaticPlaneBytes = kStaticMaxCols + kStaticMaxCols / kBlock * 8;
+static __device__ __align__(256) unsigned char scratch[kStaticPlaneBytes];
 
 namespace {
 
@@ -79,6 +90,28 @@ int64_t plane_bytes_for(int64_t n, int64_t d, int64_t* off_ds) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;   // device -> address of `scratch` there
+
+// Address of `scratch` on `device`, which must be current; resolved once per
+// device.
+int scratch_address(int device, void** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_ptr.find(device);
+    if (it == g_scratch_ptr.end()) {
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return fail(MMQ_E_HIP, "hipGetSymbolAddress(scratch) on device %d: HIP error %d (%s)",
+                        device, (int)e, hipGetErrorString(e));
+        }
+        it = g_scratch_ptr.emplace(device, ptr).first;
+    }
+    *out = it->second;
+    return MMQ_OK;
+}
+
 }  // namespace
 
 struct mmq_ctx {
@@ -106,6 +139,7 @@ struct mmq_ctx {
     int n_cu = 256;              // compute units (K-split heuristic)
     void* part = nullptr;        // K-split partial outputs, grow-only
     int64_t part_cap = 0;
+    void* static_plane = nullptr;  // this device's copy of `scratch`
 };
 
 struct mmq_weight {
@@ -435,6 +469,10 @@ int mmq_create(int device, unsigned flags, mmq_ctx** out) {
             delete c;
             return fail(MMQ_E_DEVICE, "mmq_create: hipSetDevice(%d) failed", device);
         }
+        if (int rc = scratch_address(device, &c->static_plane)) {
+            delete c;
+            return rc;
+        }
         c->device = device;
         if (prop.multiProcessorCount > 0) c->n_cu = prop.multiProcessorCount;
     }
@@ -703,6 +741,48 @@ int mmvq_q6k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* 
     if (c->dry) return MMQ_OK;
     hipStream_t s = (hipStream_t)stream;
     return after_launch(c, launch_mmvq_q6k(w->w, pl, out, s), s, who);
+}
+
+int mmvq_q6k_noalloc(mmq_ctx* c, const mmq_weight* w, const float* a, float* out,
+                     void* stream) {
+    const char* who = "mmvq_q6k_noalloc";
+    int rc = consume_check(c, w, a, 1, out, MMQ_Q6_K, MMQ_USE_GEMV, who);
+    if (rc) return rc;
+    const int64_t cols = w->w.cols;
+    if (cols > kStaticMaxCols)
+        return fail(MMQ_E_SHAPE, "%s: cols=%lld exceeds %lld, the one-token plane this call "
+                    "holds without allocating", who, (long long)cols, (long long)kStaticMaxCols);
+    if ((rc = use_device(c))) return rc;
+    if (capturing(c, (hipStream_t)stream)) c->captured = true;
+    // a recorded plane serves as in mmvq_q6k; a miss quantises into the static
+    // plane and records nothing (no slot is acquired, so nothing can grow)
+    PlaneView pl{};
+    bool quantise = false;
+    const int idx = find_entry(c, a, 1, cols);
+    if (idx >= 0) {
+        c->st.cache_hits++;
+        c->entries[idx].last = ++c->tick;
+        if (!c->dry) pl = view_of(c, idx);
+    } else {
+        if (overlaps_dead(c, a, cols * 4)) return refuse_dead(c, who, a);
+        c->st.cache_misses++;
+        c->st.launches_quant_f32++;
+        quantise = true;
+        if (!c->dry) {
+            pl.q = (int8_t*)c->static_plane;
+            pl.ds = (uint2*)((char*)c->static_plane + kStaticMaxCols);
+            pl.rows = 1;   // the GEMV reads row 0 only: no padded rows
+            pl.d = cols;
+        }
+    }
+    written(c, out, w->w.rows * 4);
+    c->st.launches_mmvq_q6k++;
+    if (c->dry) return MMQ_OK;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (quantise) e = launch_producer(kProdF32, a, nullptr, nullptr, 1, cols, 0.0f, false, pl, s);
+    if (e == hipSuccess) e = launch_mmvq_q6k(w->w, pl, out, s);
+    return after_launch(c, e, s, who);
 }
 
 int mmvq_q4k(mmq_ctx* c, const mmq_weight* w, const float* a, float* out, void* stream) {

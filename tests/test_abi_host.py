@@ -199,7 +199,7 @@ def test_q5k_is_a_decode_only_type(ctx):
 def test_binding_constants_match_the_header():
     text = open(HEADER).read()
     for name in ("MMQ_Q4_K", "MMQ_Q5_K", "MMQ_Q6_K", "MMQ_USE_GEMM", "MMQ_USE_GEMV",
-                 "MMQ_DECODE_F32_GATE", "MMQ_PLANE_ROWS"):
+                 "MMQ_DECODE_F32_GATE", "MMQ_PLANE_ROWS", "MMQ_NOALLOC_MAX_COLS"):
         m = re.search(rf"#define {name}\s+\(?(-?\d+)", text)
         assert m, name
         assert int(m.group(1)) == getattr(mmq, name), name
@@ -408,6 +408,35 @@ def test_invalidate_drops_every_piece_of_the_dead_range(ctx):
     assert _status(mmq.mmq_quant_f32, ctx, Y, 4, d) == mmq.MMQ_OK
     assert _status(mmq.mmq_quant_f32, ctx, Y + 12288, 4, d) == mmq.MMQ_OK
     assert _status(mmq.mmq_quant_f32, ctx, V, 4, d) == mmq.MMQ_E_DEAD_WRITE
+
+
+def test_noalloc_decode_host_logic(ctx):
+    """The allocation-free GEMV: a hit on a recorded plane, a miss that records
+    nothing, dead-key refusal and the column limit, all before any launch."""
+    d = 512
+    w = _w(ctx, mmq.MMQ_Q6_K, 128, d)
+    X = 0x1000000
+    before = mmq.mmq_stats(ctx)
+    mmq.mmvq_q6k_noalloc(ctx, w, X, 0x9000000)                      # miss: nothing recorded
+    st = mmq.mmq_stats(ctx)
+    assert (st["cache_misses"], st["launches_quant_f32"], st["launches_mmvq_q6k"],
+            st["cache_entries"], st["plane_bytes"]) == (
+        before["cache_misses"] + 1, before["launches_quant_f32"] + 1,
+        before["launches_mmvq_q6k"] + 1, before["cache_entries"], before["plane_bytes"])
+    mmq.mmq_quant_f32(ctx, X, 1, d)                                  # now a recorded plane
+    h0 = mmq.mmq_stats(ctx)["cache_hits"]
+    mmq.mmvq_q6k_noalloc(ctx, w, X, 0x9000000)                      # hit
+    assert mmq.mmq_stats(ctx)["cache_hits"] == h0 + 1
+    Y = 0x2000000
+    mmq.mmq_quant_rms(ctx, 0x10000, 0x20000, Y, 4, d, 1e-6, 0)      # dead [Y, Y + 8 KiB)
+    assert _status(mmq.mmvq_q6k_noalloc, ctx, w, Y + 4096, 0x9000000) == mmq.MMQ_E_DEAD_WRITE
+    wide = _w(ctx, mmq.MMQ_Q6_K, 4, mmq.MMQ_NOALLOC_MAX_COLS + 256)
+    before = mmq.mmq_stats(ctx)
+    assert _status(mmq.mmvq_q6k_noalloc, ctx, wide, X, 0x9000000) == mmq.MMQ_E_SHAPE
+    assert "exceeds" in mmq.last_error()
+    assert mmq.mmq_stats(ctx) == before
+    assert _status(mmq.mmvq_q6k_noalloc, ctx, _w(ctx, mmq.MMQ_Q6_K, 4, 256, mmq.MMQ_USE_GEMM),
+                   X, 0x9000000) == mmq.MMQ_E_TYPE                  # no GEMV tiles
 
 
 def test_scratch_cap(ctx):
