@@ -17,19 +17,19 @@
 // Design for CDNA4.  The kernel is bound by streaming the packed weights from
 // HBM, so the weights are read exactly once, with non-temporal loads, in
 // 1 KiB-per-wave coalesced pieces, and the integer work runs on
-// v_dot4_i32_i8 (4 int8 products per instruction).  Each wave keeps its slice
-// of the activation plane in registers for its whole lifetime -- lane l owns
-// 32-blocks l, l+64, ... -- and walks output rows grid-stride; per row and
-// block the lane reads the block's packed codes (16 B of 4-bit codes, plus
-// 8 B of high bit pairs for q6_K) and its scales (the registration layout of
-// repack.hip), rebuilds packed bytes with masks and shifts and dots them with
-// its codes.  For q6_K the "- 32" of the code is applied through the
-// activation: the dot accumulator starts at -32 * sum(q) of the half,
-// computed once per lane.  One f32 expression per block adds the block's
-// term; a wave-wide sum per row finishes the output.  For rows of up to 256
-// blocks the plane slice stays in registers and the weights of the wave's
-// next row are in flight while a row is reduced; longer rows re-read the
-// slice (from L2) once per pair of rows.
+// v_dot4_i32_i8 (4 int8 products per instruction).  A wave takes one output
+// row at a time -- lane l owns 32-blocks l, l+64, ... -- and issues all of the
+// row's weight loads before it computes; per block the lane reads the block's
+// packed codes (16 B of 4-bit codes, plus 8 B of high bit pairs for q6_K) and
+// its scales (the registration layout of repack.hip), rebuilds packed bytes
+// with masks and shifts and dots them with the plane's codes.  For q6_K the
+// "- 32" of the code is applied through the activation: the dot accumulator
+// starts at -32 * sum(q) of the half.  One f32 expression per block adds the
+// block's term; a wave-wide sum per row finishes the output.  For rows of up
+// to 512 blocks the plane is staged once per workgroup of 4 waves in LDS
+// (40 B per block, the half sums included), while the waves' first rows are
+// already streaming in; longer rows re-read the plane (from L2) once per pair
+// of rows.
 #include <algorithm>
 
 #include "mmq_internal.h"
@@ -226,14 +226,11 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// MAXR > 0: the lane's activation blocks stay in registers (nb <= 64 * MAXR),
-// and the weights of the wave's next row are loaded block by block as soon as
-// the current row's registers for that block are consumed, so a row's loads
-// are in flight while the previous row is reduced.
-// MAXR == 0: blocks are re-read from the plane for every pair of rows (any
-// length).
-template <class F, int MAXR>
-__global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
+// Rows longer than 512 blocks: each wave walks pairs of rows grid-stride and
+// re-reads its blocks of the plane (from L2) once per pair, so each read
+// serves both rows.
+template <class F>
+__global__ __launch_bounds__(256) void k_mmvq_long(const MvArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * 4;
@@ -241,73 +238,42 @@ __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
     const int nb = id / kBlock;
     const int nsb = id / kSuper;
     const int rounds = (nb + 63) / 64;
-
-    if constexpr (MAXR > 0) {
-        typename F::Act act[MAXR];
-        typename F::W w[MAXR];
-#pragma unroll
-        for (int r = 0; r < MAXR; ++r)
-            if (r < rounds && 64 * r + lane < nb) act[r] = F::act(g, 64 * r + lane);
-        int o = wave;
-        if (o < od) {
-#pragma unroll
-            for (int r = 0; r < MAXR; ++r)
-                if (r < rounds && 64 * r + lane < nb) w[r] = F::load(g, o, 64 * r + lane, nb, nsb);
+    for (int o = wave; o < od; o += 2 * nwaves) {
+        const int o2 = o + nwaves;
+        float acc = 0.0f, acc2 = 0.0f;
+        for (int r = 0; r < rounds; ++r) {
+            const int b = 64 * r + lane;
+            if (b < nb) {
+                const typename F::Act a = F::act(g, b);
+                acc += F::term(a, F::load(g, o, b, nb, nsb));
+                if (o2 < od) acc2 += F::term(a, F::load(g, o2, b, nb, nsb));
+            }
         }
-        for (; o < od; o += nwaves) {
-            const int on = o + nwaves;
-            float acc = 0.0f;
-#pragma unroll
-            for (int r = 0; r < MAXR; ++r) {
-                if (r < rounds && 64 * r + lane < nb) {
-                    acc += F::term(act[r], w[r]);
-                    if (on < od) w[r] = F::load(g, on, 64 * r + lane, nb, nsb);
-                }
-            }
-            acc = wave_sum(acc);
-            if (lane == 0) g.out[o] = acc;
-        }
-    } else {
-        // two rows per pass (o and o + nwaves): each plane block read serves both
-        for (int o = wave; o < od; o += 2 * nwaves) {
-            const int o2 = o + nwaves;
-            float acc = 0.0f, acc2 = 0.0f;
-            for (int r = 0; r < rounds; ++r) {
-                const int b = 64 * r + lane;
-                if (b < nb) {
-                    const typename F::Act a = F::act(g, b);
-                    acc += F::term(a, F::load(g, o, b, nb, nsb));
-                    if (o2 < od) acc2 += F::term(a, F::load(g, o2, b, nb, nsb));
-                }
-            }
-            acc = wave_sum(acc);
-            acc2 = wave_sum(acc2);
-            if (lane == 0) {
-                g.out[o] = acc;
-                if (o2 < od) g.out[o2] = acc2;
-            }
+        acc = wave_sum(acc);
+        acc2 = wave_sum(acc2);
+        if (lane == 0) {
+            g.out[o] = acc;
+            if (o2 < od) g.out[o2] = acc2;
         }
     }
 }
 
-// Workgroups of one launch: every row (MAXR == 0: every pair of rows) gets a
-// wave when they fit in two rounds of resident waves; larger matrices get
-// exactly the resident waves (each then walks rows grid-stride).
-template <class F, int MAXR>
-int64_t mmvq_grid(int64_t rows) {
+// Workgroups of the long-row form: a wave per pair of rows while they fit in
+// two rounds of resident waves, else exactly the resident waves.
+template <class F>
+int64_t mmvq_long_grid(int64_t rows) {
     static int per_cu = -1, n_cu = 0;
     if (per_cu < 0) {
         int dev = 0, blk = 0;
         (void)hipGetDevice(&dev);
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq<F, MAXR>, 256, 0) !=
-            hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq_long<F>, 256, 0) != hipSuccess)
             blk = 1;
         per_cu = blk > 0 ? blk : 1;
         if (n_cu <= 0) n_cu = 256;
     }
     const int64_t resident = (int64_t)per_cu * n_cu;
-    const int64_t want = MAXR == 0 ? (rows + 7) / 8 : (rows + 3) / 4;
+    const int64_t want = (rows + 7) / 8;
     return want <= 2 * resident ? want : resident;
 }
 
@@ -435,9 +401,81 @@ __global__ __launch_bounds__(512) void k_mmvqn(const MvArgs g, int n, int t0) {
     }
 }
 
-template <class F, int MAXR>
+__device__ __forceinline__ Q4::Act to_act(const ActRec& r, Q5*) { return to_act(r, (Q4*)nullptr); }
+
+// One token, rows of up to RM * 64 blocks: the plane is staged once per
+// workgroup of 4 waves in LDS as 40-byte records (for q6_K with the two half
+// sums); each wave takes one row at a time grid-stride and issues all of the
+// row's weight loads before it reads the plane -- the first row's before the
+// staging, so they stream in meanwhile.  Per lane the block terms are added
+// in round order, then the wave sum.
+template <class F, int RM>
+__global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    const int id = g.id, od = g.od;
+    const int nb = id / kBlock, nsb = id / kSuper;
+    uint4* lds_q = reinterpret_cast<uint4*>(lds_raw);                 // [nb][2]
+    int2* lds_m = reinterpret_cast<int2*>(lds_raw + (size_t)nb * 32);  // [nb]
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * 4;
+    const int rounds = (nb + 63) / 64;
+    typename F::W w[RM];
+    auto load_row = [&](int o) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const int b = 64 * r + lane;
+            if (r < rounds && b < nb) w[r] = F::load(g, o, b, nb, nsb);
+        }
+    };
+    if (wave < od) load_row(wave);
+    for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+        const uint4* p = reinterpret_cast<const uint4*>(g.Q + (int64_t)b * kBlock);
+        const uint4 q0 = p[0], q1 = p[1];
+        const uint2 v = g.ds[b];
+        int aux;
+        if constexpr (__is_same(F, Q6)) {
+            const uint32_t ones = 0x01010101u;
+            int s0 = dot4(q0.x, ones, 0); s0 = dot4(q0.y, ones, s0);
+            s0 = dot4(q0.z, ones, s0);    s0 = dot4(q0.w, ones, s0);
+            int s1 = dot4(q1.x, ones, 0); s1 = dot4(q1.y, ones, s1);
+            s1 = dot4(q1.z, ones, s1);    s1 = dot4(q1.w, ones, s1);
+            aux = (int)((uint32_t)(s0 & 0xFFFF) | ((uint32_t)s1 << 16));
+        } else {
+            aux = (int)v.y;
+        }
+        lds_q[2 * b] = q0;
+        lds_q[2 * b + 1] = q1;
+        lds_m[b] = make_int2((int)v.x, aux);
+    }
+    __syncthreads();
+    for (int o = wave; o < od; o += nwaves) {
+        if (o != wave) load_row(o);
+        float acc = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const int b = 64 * r + lane;
+            if (r < rounds && b < nb) {
+                ActRec rr;
+                rr.q0 = lds_q[2 * b];
+                rr.q1 = lds_q[2 * b + 1];
+                const int2 m = lds_m[b];
+                rr.D = __int_as_float(m.x);
+                rr.aux = m.y;
+                acc += F::term(to_act(rr, (F*)nullptr), w[r]);
+            }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) g.out[o] = acc;
+    }
+}
+
+template <class F, int RM>
 void launch_rows(const MvArgs& g, int64_t rows, hipStream_t s) {
-    hipLaunchKernelGGL((k_mmvq<F, MAXR>), dim3((unsigned)mmvq_grid<F, MAXR>(rows)), dim3(256), 0, s, g);
+    const int64_t want = (rows + 3) / 4;
+    const size_t lds = (size_t)(g.id / kBlock) * kRecBytes;
+    hipLaunchKernelGGL((k_mmvq<F, RM>), dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 16384))),
+                       dim3(256), lds, s, g);
 }
 
 template <class F>
@@ -453,18 +491,21 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     g.id = (int)w.cols;
     g.od = (int)w.rows;
     g.out = out;
-    // up to 4 blocks per lane and row: register arrays sized to exactly that
-    // many (fewer registers, more resident waves); longer rows re-read the
-    // plane per pair of rows, which leaves room for 8 waves per SIMD (one
-    // row per wave measured 4% slower on 5120 x 13824, four rows per wave
-    // 50% slower: too few waves in flight)
+    // the row's weight registers sized to its rounds of 64 blocks (up to 8:
+    // 512 blocks, 16384 columns, 20 KiB of plane records in LDS); longer rows
+    // take the re-reading form
     const int64_t nb = w.cols / kBlock;
     switch ((nb + 63) / 64) {
     case 1: launch_rows<F, 1>(g, w.rows, s); break;
     case 2: launch_rows<F, 2>(g, w.rows, s); break;
     case 3: launch_rows<F, 3>(g, w.rows, s); break;
     case 4: launch_rows<F, 4>(g, w.rows, s); break;
-    default: launch_rows<F, 0>(g, w.rows, s);
+    case 5: launch_rows<F, 5>(g, w.rows, s); break;
+    case 6: launch_rows<F, 6>(g, w.rows, s); break;
+    case 7: launch_rows<F, 7>(g, w.rows, s); break;
+    case 8: launch_rows<F, 8>(g, w.rows, s); break;
+    default:
+        hipLaunchKernelGGL((k_mmvq_long<F>), dim3((unsigned)mmvq_long_grid<F>(w.rows)), dim3(256), 0, s, g);
     }
     return hipGetLastError();
 }
