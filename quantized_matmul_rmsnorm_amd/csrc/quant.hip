@@ -29,8 +29,9 @@
 // f64): per lane, then across the wave, then the four wave sums in a fixed
 // order through LDS; the scale is rounded once from f64, which makes it
 // independent of the summation order to within one f64 rounding.  While a
-// wave's share of the row fits (d <= 4*256*MAXR) its x stays in registers
-// between the two passes; longer rows are re-read.
+// wave's share of the row fits (d <= 4*256*MAXR) its x, and the matching
+// rounds of the weight vector (loaded with x, before the row sum), stay in
+// registers between the two passes; longer rows are re-read.
 //
 // Rows n .. rows-1 of the plane (the padding to a multiple of 32 rows) are
 // written as zeros, so a plane's content never depends on what its slot held
@@ -50,6 +51,7 @@ __device__ __forceinline__ int dpp(int v) {
 constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7-i in each 8
+constexpr int kRowMirror = 0x140;   // row_mirror: lane i <- lane 15-i in each 16
 
 __device__ __forceinline__ float max8(float v) {
     v = fmaxf(v, __int_as_float(dpp<kQuadXor1>(__float_as_int(v))));
@@ -65,9 +67,22 @@ __device__ __forceinline__ int sum8(int v) {
     return v;
 }
 
+// Sum over the 64 lanes as a pairwise tree: lane pairs at distance 1, 2, 4
+// and 8 by DPP on the two 32-bit halves (quad xor-1, quad xor-2, then the
+// half-row and row mirrors, which pair the same groups as xor-4 and xor-8),
+// then the 16- and 32-lane swaps.  Every lane ends with the same sum.
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    auto step = [](double x, auto shuffle) {
+        const long long b = __double_as_longlong(x);
+        const int lo = shuffle((int)(b & 0xFFFFFFFFLL)), hi = shuffle((int)(b >> 32));
+        return x + __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+    };
+    v = step(v, [](int t) { return dpp<kQuadXor1>(t); });
+    v = step(v, [](int t) { return dpp<kQuadXor2>(t); });
+    v = step(v, [](int t) { return dpp<kHalfMirror>(t); });
+    v = step(v, [](int t) { return dpp<kRowMirror>(t); });
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
     return v;
 }
 
@@ -150,6 +165,7 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
 
     float scale = 0.0f;
     float4 xr[MAXR > 0 ? MAXR : 1];
+    float4 wr[MAXR > 0 ? MAXR : 1];   // RMSNorm register form: the weight rounds
     if constexpr (KIND == kProdRms) {
         double ss = 0.0;
         auto acc4 = [&](const float4& v) {
@@ -159,9 +175,14 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
             ss += (double)v.w * (double)v.w;
         };
         if constexpr (MAXR > 0) {
+            // x and the weight rounds are loaded together, so the weight
+            // loads are in flight across the row sum and its barrier
 #pragma unroll
             for (int k = 0; k < MAXR; ++k)
                 if (k < my) xr[k] = a4[64 * (wave + W * k) + lane];
+#pragma unroll
+            for (int k = 0; k < MAXR; ++k)
+                if (k < my) wr[k] = b4[64 * (wave + W * k) + lane];
 #pragma unroll
             for (int k = 0; k < MAXR; ++k)
                 if (k < my) acc4(xr[k]);
@@ -209,7 +230,8 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
                 float4 tb[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    if (k0 + u < my) tb[u] = b4[64 * (wave + W * (k0 + u)) + lane];
+                    if (k0 + u < my)
+                        tb[u] = KIND == kProdRms ? wr[k0 + u] : b4[64 * (wave + W * (k0 + u)) + lane];
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     if (k0 + u < my) finish(wave + W * (k0 + u), xr[k0 + u], tb[u]);
