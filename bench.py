@@ -853,7 +853,9 @@ def main():
                      "frac_of_f16_mfma_peak": round(achieved / PEAK_F16_TOPS, 4),
                      "frac_of_measured_f16_mfma": round(achieved / peaks["mfma_f16_32x32x16_TFLOPs"], 4),
                      "frac_of_measured_i8_mfma": round(achieved / peaks["mfma_i8_32x32x32_TOPs"], 4),
-                     "frac_of_measured_matmul_mix": round(achieved / peaks["matmul_mix"]["both_TFLOPs"], 4)},
+                     "frac_of_measured_matmul_mix": round(achieved / peaks["matmul_mix"]["both_TFLOPs"], 4),
+                     "frac_of_measured_matmul_flow": round(
+                         achieved / peaks["overlap_probes"]["w2_t2_both_matmul_flow"]["mfma_TFLOPs"], 4)},
         "measured_peaks": peaks,
         "kernels": kernels,
         "graph": graph_rec,

@@ -117,7 +117,8 @@ typedef struct mmq_stats_t {
     int64_t launches_gemv_f32;      /* q6_K GEMVs on an f32 activation (no plane) */
 } mmq_stats_t;
 
-/* ---- context ----------------------------------------------------------- */
+/* ---- context (library infrastructure: no passage of the pages defines
+ * these calls; they own the device, the plane slots and the error text) --- */
 
 /* Create a context on HIP device `device` (must be gfx950; the device
  * becomes current on the calling thread).  flags: MMQ_CTX_*.  With
@@ -156,10 +157,12 @@ int64_t mmq_plane_rows(int64_t n);
 int mmq_register_weight(mmq_ctx* ctx, int type, int64_t rows, int64_t cols,
                         const void* raw_host, unsigned uses, mmq_weight** out);
 
-/* Release a weight's device tiles (NULL ignored; synchronises the device). */
+/* Release a weight's device tiles (NULL ignored; synchronises the device).
+ * Library infrastructure; no passage defines it. */
 void mmq_weight_free(mmq_weight* w);
 
-/* Device bytes held by a registered weight. */
+/* Device bytes held by a registered weight (library infrastructure; the
+ * pages count memory both ways [r60 4], this is the registered side). */
 int64_t mmq_weight_bytes(const mmq_weight* w);
 
 /* ---- producers [r52 2.2, 3.2; d37 Excerpt C] ----------------------------
@@ -300,13 +303,15 @@ void mmq_cache_clear(mmq_ctx* ctx);
 
 /* Drop the entries recorded under `key` and the dead range a skip-write
  * producer recorded for `key` (all of it that no later write revived), for a
- * buffer about to be reused with new contents inside a window.  Writes to
+ * buffer about to be reused with new contents inside a window (library
+ * infrastructure: the pages only clear the whole cache [d37 D]).  Writes to
  * caller memory that the caller makes itself are invisible to the library:
  * call this before re-using a key buffer.  MMQ_OK even if absent. */
 int mmq_cache_invalidate(mmq_ctx* ctx, const void* key);
 
-/* Copy the plane recorded under (key, n, d) into caller device buffers in
- * the canonical row-major layout: q int8 [r][d], dq f32 [r][d/32],
+/* Test hook (library infrastructure; no passage defines it).  Copy the
+ * plane recorded under (key, n, d) into caller device buffers in the
+ * canonical row-major layout: q int8 [r][d], dq f32 [r][d/32],
  * s int32 [r][d/32], with r = n, or mmq_plane_rows(n) if include_pad.
  * dq and s must be 4-byte aligned.
  * Errors: MMQ_E_ARG (no such plane, null or misaligned buffer), MMQ_E_HIP,
@@ -315,7 +320,8 @@ int mmq_plane_export(mmq_ctx* ctx, const void* key, int64_t n, int64_t d,
                      int include_pad, int8_t* q, float* dq, int32_t* s,
                      void* stream);
 
-/* Fill *st with counters since creation. */
+/* Fill *st with counters since creation (library infrastructure: the
+ * launch, hit and refusal counts the pages' checks count [r52 3.2]). */
 int mmq_stats(mmq_ctx* ctx, mmq_stats_t* st);
 
 #ifdef __cplusplus

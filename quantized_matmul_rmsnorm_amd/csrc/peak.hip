@@ -80,7 +80,10 @@ __global__ __launch_bounds__(256) void k_peak_i8(int* __restrict__ out, int iter
 // (acc += s * X, the per-block rescale) reading the X buffer of the previous
 // block; the buffers alternate.  The first K-step accumulates onto the
 // buffer's old contents (the matmul starts each block from zero; a zero start
-// with fixed operands would be hoisted out of the loop).  MODE 0: MFMAs only;
+// with fixed operands would be hoisted out of the loop).  That ties each
+// block's MFMAs to the FMAs that last read their buffer, so this mix overlaps
+// the two pipes less than the matmul's own flow can; k_mix_probe below
+// measures the zero start with varying operands.  MODE 0: MFMAs only;
 // 1: FMAs only; 2: both, in the matmul's order (the MFMAs of a block, then
 // the FMAs of the one before).  MODE 3 is the same per-block work on int8
 // MFMA: one v_mfma_i32_32x32x32_i8 per output tile and block (the whole
