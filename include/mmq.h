@@ -278,7 +278,7 @@ int mmq_gemv_q6k_f32(mmq_ctx* ctx, const mmq_weight* w, const float* x, float* o
  * activation feeds further quantised consumers can call mmvq_q6k directly so
  * that the plane is recorded and shared.  Counted under launches_gemv_f32 or
  * launches_mmvq_q6k. */
-#define MMQ_DECODE_F32_GATE 20000000LL
+#define MMQ_DECODE_F32_GATE 16000000LL
 int mmq_decode_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* x, float* out,
                    void* stream);
 

@@ -267,7 +267,7 @@ def mmq_decode_q6k(ctx, w, x, out, stream=None):
     return _check(lib.mmq_decode_q6k(ctx, w, _ptr(x, f), _ptr(out, f), _stream(stream)))
 
 
-MMQ_DECODE_F32_GATE = 20_000_000
+MMQ_DECODE_F32_GATE = 16_000_000
 
 
 def mmvq_q5k(ctx, w, a, out, stream=None):

@@ -26,7 +26,7 @@
 // "- 32" of the code is applied through the activation: the dot accumulator
 // starts at -32 * sum(q) of the half.  One f32 expression per block adds the
 // block's term; a wave-wide sum per row finishes the output.  For rows of up
-// to 512 blocks the plane is staged once per workgroup of 4 waves in LDS
+// to 768 blocks the plane is staged once per workgroup of 4 waves in LDS
 // (40 B per block, the half sums included), while the waves' first rows are
 // already streaming in; longer rows re-read the plane (from L2) once per pair
 // of rows.
@@ -226,7 +226,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Rows longer than 512 blocks: each wave walks pairs of rows grid-stride and
+// Rows longer than 768 blocks: each wave walks pairs of rows grid-stride and
 // re-reads its blocks of the plane (from L2) once per pair, so each read
 // serves both rows.
 template <class F>
@@ -491,8 +491,10 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     g.id = (int)w.cols;
     g.od = (int)w.rows;
     g.out = out;
-    // the row's weight registers sized to its rounds of 64 blocks (up to 8:
-    // 512 blocks, 16384 columns, 20 KiB of plane records in LDS); longer rows
+    // the row's weight registers sized to its rounds of 64 blocks (up to 12:
+    // 768 blocks, 24576 columns, 30 KiB of plane records in LDS, about 160
+    // VGPRs and 3 waves per SIMD; at 14 rounds, 2 waves per SIMD, it measured
+    // slower than the re-reading form); longer rows
     // take the re-reading form
     const int64_t nb = w.cols / kBlock;
     switch ((nb + 63) / 64) {
@@ -504,6 +506,10 @@ hipError_t launch_mmvq(const WeightDev& w, const PlaneView& pl, float* out, hipS
     case 6: launch_rows<F, 6>(g, w.rows, s); break;
     case 7: launch_rows<F, 7>(g, w.rows, s); break;
     case 8: launch_rows<F, 8>(g, w.rows, s); break;
+    case 9: launch_rows<F, 9>(g, w.rows, s); break;
+    case 10: launch_rows<F, 10>(g, w.rows, s); break;
+    case 11: launch_rows<F, 11>(g, w.rows, s); break;
+    case 12: launch_rows<F, 12>(g, w.rows, s); break;
     default:
         hipLaunchKernelGGL((k_mmvq_long<F>), dim3((unsigned)mmvq_long_grid<F>(w.rows)), dim3(256), 0, s, g);
     }

@@ -288,11 +288,12 @@ def test_gemm_full_size_sampled(ctx, wtype, od, id_):
 
 
 # ------------------------------------------------------------------ one-token GEMV
-# one shape per register-array size (rounds of 64 blocks per row 1..8, the
-# plane staged in LDS), then the re-reading form for longer rows (9 and 10
+# one shape per register-array size (rounds of 64 blocks per row 1..12, the
+# plane staged in LDS), then the re-reading form for longer rows (13 and 16
 # rounds); 20000 rows make waves walk several rows with the next row in flight
 GEMV_SHAPES = [(64, 256), (4100, 4096), (1000, 5120), (1024, 5120), (20000, 5120), (777, 8192),
-               (9000, 10240), (130, 12288), (300, 13824), (65, 16384), (50, 18432), (33, 20480)]
+               (9000, 10240), (130, 12288), (300, 13824), (65, 16384), (50, 18432), (33, 20480),
+               (40, 22528), (70, 24576), (33, 26624), (20, 32768)]
 
 
 @pytest.mark.parametrize("od,id_", GEMV_SHAPES)
