@@ -556,22 +556,33 @@ def measured_peaks(torch):
     del mout
     res["overlap_probes"] = overlap_probes(torch, lib, n_cu, stream)
     lib.mmq_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                  ctypes.c_void_p]
+                                  ctypes.c_int, ctypes.c_void_p]
     lib.mmq_peak_read.restype = ctypes.c_int
-    rbytes = 2 << 30
+    # the best of a few launch shapes over 4 GiB (well past the 256 MB MALL)
+    rbytes = 4 << 30
     rbuf = torch.ones(rbytes // 4, dtype=torch.float32, device="cuda")
-    rblocks = 8 * n_cu
-    rout = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
-    for rep in range(6):    # one warm-up, five timed
-        if rep == 1:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-        if lib.mmq_peak_read(rbuf.data_ptr(), rbytes, rout.data_ptr(), rblocks, stream.cuda_stream) != 0:
-            raise RuntimeError("read stream: launch failed")
-    e1 = torch.cuda.Event(enable_timing=True)
-    e1.record()
-    torch.cuda.synchronize()
-    res["hbm_read_GB_s"] = round(5 * rbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    rout = torch.empty(32 * n_cu * 256, dtype=torch.int32, device="cuda")
+    best, shapes = None, {}
+    for per_cu in (8, 16, 32):
+        for unroll in (4, 8, 16):
+            blocks = per_cu * n_cu
+            for rep in range(4):    # one warm-up, three timed
+                if rep == 1:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                if lib.mmq_peak_read(rbuf.data_ptr(), rbytes, rout.data_ptr(), blocks, unroll,
+                                     stream.cuda_stream) != 0:
+                    raise RuntimeError("read stream: launch failed")
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = round(3 * rbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+            shapes[f"{per_cu}x{unroll}"] = gbs
+            if best is None or gbs > best[0]:
+                best = (gbs, per_cu, unroll)
+    res["hbm_read_GB_s"] = best[0]
+    res["hbm_read_shape"] = {"workgroups_per_cu": best[1], "loads_in_flight": best[2],
+                             "GB_s_by_wg_per_cu_x_loads": shapes}
     del rbuf, rout
     nel = (1 << 30) // 4
     src = torch.ones(nel, dtype=torch.float32, device="cuda")

@@ -71,11 +71,14 @@ int mmq_peak_probe(int i, float* out, int blocks, int iters, hipStream_t stream)
 
 /* Read-only HBM stream: reads `bytes` (a multiple of 16, > 0) of the device
  * buffer `src` once with 16-byte non-temporal loads, `blocks` workgroups of
- * 256 threads walking it grid-stride, and writes one folded value per thread
- * to `out` (blocks * 256 uint32, caller-owned).  Time it with events on
- * `stream`.  Returns 0, -1 for an invalid argument (nothing launched), or the
+ * 256 threads walking it grid-stride with `unroll` (4, 8 or 16) loads in
+ * flight per thread, and writes one folded value per thread to `out`
+ * (blocks * 256 uint32, caller-owned).  Time it with events on `stream`;
+ * the best of a few (blocks, unroll) shapes is the chip's practical read
+ * rate.  Returns 0, -1 for an invalid argument (nothing launched), or the
  * HIP error code of the launch. */
-int mmq_peak_read(const void* src, int64_t bytes, unsigned* out, int blocks, hipStream_t stream);
+int mmq_peak_read(const void* src, int64_t bytes, unsigned* out, int blocks, int unroll,
+                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -290,6 +290,7 @@ constexpr int kNumProbes = sizeof(kProbes) / sizeof(kProbes[0]);
 
 // Read-only stream: each thread walks the buffer grid-stride in 16 B
 // non-temporal loads (4 in flight) and writes one folded value at the end.
+template <int U>
 __global__ __launch_bounds__(256) void k_peak_read(const uint4* __restrict__ src, int64_t n16,
                                                    uint32_t* __restrict__ out) {
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
@@ -297,13 +298,13 @@ __global__ __launch_bounds__(256) void k_peak_read(const uint4* __restrict__ src
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     uint32_t acc = 0;
     int64_t i = tid;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        u4v v[4];
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u4v v[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u)
             v[u] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(src + i + u * stride));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (; i < n16; i += stride) {
         const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(src + i));
@@ -375,10 +376,17 @@ int mmq_peak_probe(int i, float* out, int blocks, int iters, hipStream_t s) {
 // src: device buffer of `bytes` bytes (bytes % 16 == 0), read once; out:
 // device buffer of blocks * 256 uint32.  Returns 0, -1 for bad arguments, or
 // the HIP error.
-int mmq_peak_read(const void* src, int64_t bytes, unsigned* out, int blocks, hipStream_t s) {
+int mmq_peak_read(const void* src, int64_t bytes, unsigned* out, int blocks, int unroll,
+                  hipStream_t s) {
     if (src == nullptr || out == nullptr || bytes <= 0 || bytes % 16 != 0 || blocks < 1) return -1;
-    hipLaunchKernelGGL(k_peak_read, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const uint4*>(src), (int64_t)(bytes / 16), out);
+    const uint4* p = static_cast<const uint4*>(src);
+    const int64_t n16 = bytes / 16;
+    switch (unroll) {
+    case 4: hipLaunchKernelGGL(k_peak_read<4>, dim3((unsigned)blocks), dim3(256), 0, s, p, n16, out); break;
+    case 8: hipLaunchKernelGGL(k_peak_read<8>, dim3((unsigned)blocks), dim3(256), 0, s, p, n16, out); break;
+    case 16: hipLaunchKernelGGL(k_peak_read<16>, dim3((unsigned)blocks), dim3(256), 0, s, p, n16, out); break;
+    default: return -1;
+    }
     return (int)hipGetLastError();
 }
 

@@ -89,12 +89,14 @@ def test_peak_library_exports_its_header():
     assert probe(0, ctypes.c_void_p(0x1000), 0, 1, None) == -1
     assert probe(0, ctypes.c_void_p(0x1000), 1, (1 << 20) + 1, None) == -1
     rd = lib.mmq_peak_read
-    rd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    assert rd(None, 16, ctypes.c_void_p(0x1000), 1, None) == -1
-    assert rd(ctypes.c_void_p(0x1000), 24, ctypes.c_void_p(0x1000), 1, None) == -1
-    assert rd(ctypes.c_void_p(0x1000), 0, ctypes.c_void_p(0x1000), 1, None) == -1
-    assert rd(ctypes.c_void_p(0x1000), 16, None, 1, None) == -1
-    assert rd(ctypes.c_void_p(0x1000), 16, ctypes.c_void_p(0x1000), 0, None) == -1
+    rd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p]
+    assert rd(None, 16, ctypes.c_void_p(0x1000), 1, 8, None) == -1
+    assert rd(ctypes.c_void_p(0x1000), 24, ctypes.c_void_p(0x1000), 1, 8, None) == -1
+    assert rd(ctypes.c_void_p(0x1000), 0, ctypes.c_void_p(0x1000), 1, 8, None) == -1
+    assert rd(ctypes.c_void_p(0x1000), 16, None, 1, 8, None) == -1
+    assert rd(ctypes.c_void_p(0x1000), 16, ctypes.c_void_p(0x1000), 0, 8, None) == -1
+    assert rd(ctypes.c_void_p(0x1000), 16, ctypes.c_void_p(0x1000), 1, 5, None) == -1
 
 
 def test_no_device_is_reported():
