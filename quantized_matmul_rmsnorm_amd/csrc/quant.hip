@@ -25,6 +25,10 @@
 // y is stored, so write_y = 0, write_y = 1 and a standalone quantise of the
 // stored y give byte-identical planes.
 //
+// SwiGLU's gate and up rows and the standalone quantise's input are read
+// exactly once, with non-temporal loads; RMSNorm's x and weight vector are
+// read with ordinary loads (the weight vector serves every row).
+//
 // RMSNorm accumulates sum(x^2) in f64 (products of f32 values are exact in
 // f64): per lane, then across the wave, then the four wave sums in a fixed
 // order through LDS; the scale is rounded once from f64, which makes it
@@ -118,6 +122,13 @@ __device__ __forceinline__ void quant4(float4 v, int lane, uint32_t* qdst, uint2
     if ((lane & 7) == 0) *dsdst = make_uint2(__float_as_uint(dsc), (uint32_t)s);
 }
 
+// A non-temporal 16-byte load, for inputs each workgroup reads exactly once.
+__device__ __forceinline__ float4 stream_load(const float4* p) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
     const float den = 1.0f + expf(-g);
     return (g / den) * u;
@@ -134,7 +145,10 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
                                                   uint2* __restrict__ ds, int rows,
                                                   int rps) {
     constexpr int W = 4;   // waves per row segment
-    constexpr int U = 8;   // rounds of one wave whose loads are in flight together
+    // rounds of one wave whose loads are in flight together (SwiGLU: its
+    // segments give a wave at most 3 rounds, and the smaller buffer keeps
+    // 8 waves per SIMD resident)
+    constexpr int U = KIND == kProdSwiglu ? 4 : 8;
     __shared__ double s_ss[W];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -244,8 +258,13 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
             for (int u = 0; u < U; ++u) {
                 const int r = wave + W * (k0 + u);
                 if (k0 + u < my) {
-                    ta[u] = a4[64 * r + lane];
-                    if constexpr (KIND != kProdF32) tb[u] = b4[64 * r + lane];
+                    if constexpr (KIND == kProdRms) {   // x re-read, w shared by every row
+                        ta[u] = a4[64 * r + lane];
+                        tb[u] = b4[64 * r + lane];
+                    } else {                            // read exactly once: streamed
+                        ta[u] = stream_load(a4 + 64 * r + lane);
+                        if constexpr (KIND == kProdSwiglu) tb[u] = stream_load(b4 + 64 * r + lane);
+                    }
                 }
             }
 #pragma unroll
