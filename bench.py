@@ -246,9 +246,10 @@ def decode_gemv(mmq, torch, synth):
 
 def small_n_sweep(mmq, torch, synth):
     """The small-n band: matmul-call time for n = 1..128 tokens at the 7B/14B
-    shapes, weights registered for both paths (n <= 8 takes the GEMV path when
-    one pass holds the tokens, larger n the matmul tiles with a K split).  Each
-    point is a captured-graph replay over rotated weight copies."""
+    shapes, weights registered for both paths (few tokens take the GEMV path in
+    one or two passes, as the library routes them; larger n the matmul tiles
+    with a K split).  Each point is a captured-graph replay over rotated
+    weight copies."""
     ctx = mmq.mmq_create(0, 0)
     res = {}
     try:

@@ -203,12 +203,14 @@ int mmq_quant_f32(mmq_ctx* ctx, const float* x, int64_t n, int64_t d, void* stre
  * row-major [n][rows] f32, caller-owned; w is the dequantised weight.
  * Writing out drops cached planes keyed in its bytes and revives dead bytes
  * there (the same holds for every consumer below).
- * The small-n band [r60 3.2: the matmul is tuned for n >= 16; d37 2]: for
- * n <= 8 on a weight also registered with MMQ_USE_GEMV the call runs on the
- * dot4 GEMV path (one launch per pass of up to 8 tokens); otherwise the
- * matmul tiles, with K split across workgroups when the output tiles alone
- * do not fill the device (partials held in the context's scratch, summed in
- * a fixed order).
+ * The small-n band [r60 3.2: the matmul is tuned for n >= 16; d37 2]: on a
+ * weight also registered with MMQ_USE_GEMV, the call runs on the dot4 GEMV
+ * path (one launch per pass of up to 8 tokens, as many as the LDS holds at
+ * this width) when one pass holds the n tokens, or when two passes do and
+ * n <= 8 or rows * cols <= 16M (measured against the matmul on MI355X; n is
+ * at most 16 either way); otherwise the matmul tiles, with K split across
+ * workgroups when the output tiles alone do not fill the device (partials
+ * held in the context's scratch, summed in a fixed order).
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE, MMQ_E_DEAD_WRITE, MMQ_E_OOM,
  * MMQ_E_HIP. */
 int mmq_gemm_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,

@@ -673,7 +673,21 @@ static int acquire_part(mmq_ctx* c, int64_t bytes, bool in_capture, const char* 
     return MMQ_OK;
 }
 
-constexpr int64_t kSmallN = 8;
+// The small-n band: the few-token GEMV serves n <= kSmallN when it needs
+// one pass; a second pass (the weights streamed twice) still beats the split
+// matmul for n <= 8 (rows too wide for 8 tokens in the LDS: q6_K 3584 x 18944
+// at n = 8, 34 against 41 us) and for small weights up to n = 16 (q4_K
+// 3584 x 3584 at n = 12-16, 13.7 against 19.2 us), but not for the large FFN
+// weights at n = 12-16 (44-64 against 35-40 us).
+constexpr int64_t kSmallN = 16;
+constexpr int64_t kTwoPassMaxWeights = 16000000;   // rows * cols
+
+static bool small_n_gemv(const WeightDev& w, int64_t n) {
+    if (n > kSmallN || !(w.uses & MMQ_USE_GEMV)) return false;
+    const int passes = mmvqn_passes(w.cols, n);
+    if (passes == 1) return true;
+    return passes == 2 && (n <= 8 || w.rows * w.cols <= kTwoPassMaxWeights);
+}
 
 static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t n, float* out,
                        void* stream, int type, const char* who) {
@@ -684,10 +698,10 @@ static int gemm_common(mmq_ctx* c, const mmq_weight* w, const float* a, int64_t 
         return fail(MMQ_E_SHAPE, "%s: plane of %lld x %lld codes exceeds 2 GiB; split the tokens",
                     who, (long long)n, (long long)w->w.cols);
     if ((rc = use_device(c))) return rc;
-    // The small-n band: with GEMV tiles registered, up to kSmallN tokens run
-    // on the dot4 GEMV path (one launch streams the packed weights once for
-    // a pass of up to 8 tokens) instead of the 128-token matmul tiles.
-    const bool small = n <= kSmallN && (w->w.uses & MMQ_USE_GEMV) && mmvqn_supported(w->w.cols, n);
+    // The small-n band: with GEMV tiles registered, few tokens run on the
+    // dot4 GEMV path (one launch streams the packed weights once for a pass
+    // of up to 8 tokens) instead of the 128-token matmul tiles.
+    const bool small = small_n_gemv(w->w, n);
     if (small) {
         PlaneView pl;
         if ((rc = plane_for(c, who, a, n, w->w.cols, stream, &pl))) return rc;

@@ -88,7 +88,9 @@ constexpr int64_t kGemvF32MaxCols = 16384;   // x is staged whole in 64 KiB of L
 hipError_t launch_gemv_f32_q6k(const WeightDev& w, const float* x, float* out, hipStream_t s);
 // A few tokens at once over the GEMV tiles (out [n][rows]); used when the n
 // tokens' plane fits the LDS in one pass.
-int mmvqn_supported(int64_t cols, int64_t n);
+// Launches (passes of up to 8 tokens) the few-token GEMV takes for n tokens
+// of width cols; 0 if not even 2 tokens fit the LDS.
+int mmvqn_passes(int64_t cols, int64_t n);
 hipError_t launch_mmvqn_q6k(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
                             int n_cu, hipStream_t s);
 hipError_t launch_mmvqn_q4k(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,

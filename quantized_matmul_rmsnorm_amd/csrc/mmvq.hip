@@ -277,7 +277,7 @@ int64_t mmvq_long_grid(int64_t rows) {
     return want <= 2 * resident ? want : resident;
 }
 
-// ---- a few tokens at once (2 <= n <= 8) ----
+// ---- a few tokens at once (2 <= n <= 16, in passes of up to 8) ----
 // One 32-block of one token, as staged in LDS (40 bytes, two arrays): the
 // codes, then D and a sum word (q6_K: the two 16-value half sums as int16;
 // q4_K: the block's code sum S).
@@ -301,18 +301,19 @@ __device__ __forceinline__ Q4::Act to_act(const ActRec& r, Q4*) {
     return a;
 }
 
-// Workgroups of 8 waves share the NT tokens' plane (tokens t0 .. t0+NT-1,
-// missing tokens as zeros) staged once in LDS; each wave walks groups of R
-// rows grid-stride, loads a block of the R rows per round (the next round's
-// loads in flight) and applies it to all NT tokens.  out is [n][od].
+// Workgroups of 8 or 16 waves share the NT tokens' plane (tokens t0 ..
+// t0+NT-1, missing tokens as zeros) staged once in LDS; each wave walks groups
+// of R rows grid-stride, loads a block of the R rows per round (the next
+// round's loads in flight) and applies it to all NT tokens.  out is [n][od].
 template <class F, int NT, int R>
-__global__ __launch_bounds__(512) void k_mmvqn(const MvArgs g, int n, int t0) {
+__global__ __launch_bounds__(1024) void k_mmvqn(const MvArgs g, int n, int t0) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     uint4* lds_q = reinterpret_cast<uint4*>(lds_raw);                      // [NT*nb][2]
     int2* lds_m = reinterpret_cast<int2*>(lds_raw + (size_t)NT * (g.id / kBlock) * 32);  // [NT*nb]
     const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * 8 + (threadIdx.x >> 6);
-    const int nwaves = gridDim.x * 8;
+    const int wpb = blockDim.x >> 6;
+    const int wave = blockIdx.x * wpb + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * wpb;
     const int id = g.id, od = g.od;
     const int nb = id / kBlock;
     const int nsb = id / kSuper;
@@ -526,7 +527,12 @@ int mmvqn_tokens(int64_t cols, int64_t n) {
 
 template <class F, int NT>
 hipError_t launch_nt(const MvArgs& g, int64_t n, int64_t t0, int n_cu, hipStream_t s) {
-    constexpr int R = 4;
+    // One row per group: the register arrays stay small (57-94 VGPRs), so
+    // several workgroups fit on a CU where the LDS allows; a plane of more
+    // than 80 KiB (one workgroup per CU) is shared by 16 waves instead of 8.
+    // Against 4 rows per group on 8-wave workgroups, one per CU: n = 2 is
+    // 1.3-1.8x faster, n = 4 1.2-1.9x, n = 8 1.1-1.8x at the 7B and 14B shapes.
+    constexpr int R = 1;
     const size_t lds = (size_t)NT * (g.id / kBlock) * kRecBytes;
     static bool attr = false;
     if (!attr) {
@@ -534,10 +540,11 @@ hipError_t launch_nt(const MvArgs& g, int64_t n, int64_t t0, int n_cu, hipStream
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr = true;
     }
+    const int threads = lds > 80 * 1024 ? 1024 : 512;
     const int64_t groups = (g.od + R - 1) / R;
-    const int64_t want = (groups + 7) / 8;
-    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, n_cu)));
-    hipLaunchKernelGGL((k_mmvqn<F, NT, R>), grid, dim3(512), lds, s, g, (int)n, (int)t0);
+    const int64_t want = (groups + threads / 64 - 1) / (threads / 64);
+    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 4 * (int64_t)n_cu)));
+    hipLaunchKernelGGL((k_mmvqn<F, NT, R>), grid, dim3(threads), lds, s, g, (int)n, (int)t0);
     return hipGetLastError();
 }
 
@@ -624,7 +631,10 @@ __global__ __launch_bounds__(256) void k_gemv_f32_q6(const MvArgs g, const float
 // The GEMV path pays off while one pass holds all n tokens (each further
 // pass streams the weights again); the crossover against the split-K matmul
 // was measured at the 7B/14B shapes for n = 1..8.
-int mmvqn_supported(int64_t cols, int64_t n) { return n >= 1 && mmvqn_tokens(cols, n) >= n; }
+int mmvqn_passes(int64_t cols, int64_t n) {
+    const int nt = n >= 1 ? mmvqn_tokens(cols, n) : 0;
+    return nt > 0 ? (int)((n + nt - 1) / nt) : 0;
+}
 
 hipError_t launch_mmvqn_q6k(const WeightDev& w, const PlaneView& pl, int64_t n, float* out,
                             int n_cu, hipStream_t s) {

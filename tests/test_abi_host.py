@@ -538,16 +538,24 @@ def test_split_k_scratch_is_checked_before_any_launch(ctx):
 
 
 def test_small_n_routing(ctx):
-    """n <= 8 on a weight registered for both paths takes the GEMV path when
-    one pass holds the tokens; otherwise the matmul tiles."""
+    """On a weight registered for both paths the GEMV path serves the call
+    when one pass of the LDS holds the tokens (8 at width 5120, 4 at 18944),
+    or when two passes do and n <= 8 or rows * cols <= 16M; otherwise (and
+    always beyond 16 tokens) the matmul tiles."""
     both = mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV
-    w = _w(ctx, mmq.MMQ_Q4_K, 256, 5120, both)
+    w = _w(ctx, mmq.MMQ_Q4_K, 256, 5120, both)            # 1.3M weights
     wg = _w(ctx, mmq.MMQ_Q4_K, 256, 5120, mmq.MMQ_USE_GEMM)
-    wd = _w(ctx, mmq.MMQ_Q6_K, 256, 18944, both)
+    wd = _w(ctx, mmq.MMQ_Q6_K, 256, 18944, both)           # 4.8M weights, 4 tokens per pass
+    wb = _w(ctx, mmq.MMQ_Q4_K, 3328, 5120, both)           # 17.0M weights
+    wl = _w(ctx, mmq.MMQ_Q6_K, 1024, 18944, both)          # 19.4M weights, 4 tokens per pass
     A, O = 0x100000, 0x4000000
     for n, weight, fn, routed in [(1, w, mmq.mmq_gemm_q4k, 1), (8, w, mmq.mmq_gemm_q4k, 1),
-                                  (9, w, mmq.mmq_gemm_q4k, 0), (4, wg, mmq.mmq_gemm_q4k, 0),
-                                  (4, wd, mmq.mmq_gemm_q6k, 1), (5, wd, mmq.mmq_gemm_q6k, 0)]:
+                                  (9, w, mmq.mmq_gemm_q4k, 1), (16, w, mmq.mmq_gemm_q4k, 1),
+                                  (17, w, mmq.mmq_gemm_q4k, 0), (4, wg, mmq.mmq_gemm_q4k, 0),
+                                  (8, wb, mmq.mmq_gemm_q4k, 1), (9, wb, mmq.mmq_gemm_q4k, 0),
+                                  (4, wd, mmq.mmq_gemm_q6k, 1), (5, wd, mmq.mmq_gemm_q6k, 1),
+                                  (8, wd, mmq.mmq_gemm_q6k, 1), (9, wd, mmq.mmq_gemm_q6k, 0),
+                                  (8, wl, mmq.mmq_gemm_q6k, 1), (9, wl, mmq.mmq_gemm_q6k, 0)]:
         before = mmq.mmq_stats(ctx)["small_n_gemv"]
         fn(ctx, weight, A + n * 0x10000000, n, O)
         assert mmq.mmq_stats(ctx)["small_n_gemv"] - before == routed, (n, routed)

@@ -218,12 +218,15 @@ def test_gemm_degenerate_activation_rows(ctx, wtype):
                                             ("q4_K", 5, 13824, 5120), ("q6_K", 8, 3584, 18944),
                                             ("q6_K", 4, 3584, 18944),
                                             ("q6_K", 6, 64, 256), ("q4_K", 1, 700, 2048),
-                                            ("q4_K", 7, 33, 20480)])
+                                            ("q4_K", 7, 33, 20480), ("q4_K", 12, 3584, 3584),
+                                            ("q6_K", 16, 512, 3584), ("q4_K", 11, 600, 13824),
+                                            ("q4_K", 9, 4096, 5120)])
 def test_gemm_small_n_gemv_path(ctx, wtype, n, od, id_):
-    """n <= 8 on a weight registered for both paths runs on the dot4 GEMV
-    kernels when one pass of the LDS holds the n tokens (the 18944-wide plane
-    holds 4, so n = 8 there takes the matmul tiles instead; so does n = 7 at
-    width 20480)."""
+    """A weight registered for both paths runs on the dot4 GEMV kernels when
+    one pass of the LDS holds the n tokens, or two passes do and n <= 8 or
+    od * id <= 16M (the 18944-wide plane holds 4 tokens, so n = 8 there takes
+    two passes; n = 9 on 4096 x 5120 takes the matmul tiles); the outputs of
+    either path meet the matmul bar."""
     rng = synth.rng_for("test", n * 7 + od, f"smalln{wtype}{id_}")
     raw = synth.weights(wtype, rng, od, id_)
     w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw, mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMV)
@@ -233,8 +236,10 @@ def test_gemm_small_n_gemv_path(ctx, wtype, n, od, id_):
     (mmq.mmq_gemm_q4k if wtype == "q4_K" else mmq.mmq_gemm_q6k)(ctx, w, a, n, out)
     torch.cuda.synchronize()
     rec = id_ // 32 * 40                     # LDS bytes per token: 40 B per 32-block
-    one_pass = n <= max([t for t in (2, 4, 8) if t * rec <= 160 * 1024], default=0)
-    assert mmq.mmq_stats(ctx)["small_n_gemv"] == before + (1 if one_pass else 0)
+    per_pass = max([t for t in (2, 4, 8) if t * rec <= 160 * 1024], default=0)
+    passes = -(-n // per_pass) if per_pass else 0
+    gemv = n <= 16 and (passes == 1 or (passes == 2 and (n <= 8 or od * id_ <= 16_000_000)))
+    assert mmq.mmq_stats(ctx)["small_n_gemv"] == before + (1 if gemv else 0)
     q, D, S = export_plane(ctx, a, n, id_)
     ref = gemm_ref(wtype, q, D, S, raw, od, id_)
     assert_gemm_close(out.cpu().numpy(), ref, f"small-n {wtype} n={n} {od}x{id_}")
