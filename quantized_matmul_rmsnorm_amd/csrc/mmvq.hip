@@ -31,11 +31,25 @@
 // already streaming in; longer rows re-read the plane (from L2) once per pair
 // of rows.
 #include <algorithm>
+#include <atomic>
 
 #include "mmq_internal.h"
 
 namespace mmq {
 namespace {
+
+// Raise a kernel's dynamic-LDS limit once on each device that launches it
+// (the attribute is set with the device current; `done` holds one bit per
+// device index).
+template <class K>
+void lds_limit_once(K kernel, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return;
+    (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    done.fetch_or(bit);
+}
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
@@ -534,12 +548,8 @@ hipError_t launch_nt(const MvArgs& g, int64_t n, int64_t t0, int n_cu, hipStream
     // 1.3-1.8x faster, n = 4 1.2-1.9x, n = 8 1.1-1.8x at the 7B and 14B shapes.
     constexpr int R = 1;
     const size_t lds = (size_t)NT * (g.id / kBlock) * kRecBytes;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void*)k_mmvqn<F, NT, R>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr = true;
-    }
+    static std::atomic<uint64_t> attr{0};
+    lds_limit_once(k_mmvqn<F, NT, R>, 160 * 1024, attr);
     const int threads = lds > 80 * 1024 ? 1024 : 512;
     const int64_t groups = (g.od + R - 1) / R;
     const int64_t want = (groups + threads / 64 - 1) / (threads / 64);
@@ -676,12 +686,11 @@ hipError_t launch_gemv_f32_q6k(const WeightDev& w, const float* x, float* out, h
     g.od = (int)w.rows;
     g.out = out;
     const size_t lds = (size_t)w.cols * 4;
+    static std::atomic<uint64_t> attr{0};
+    lds_limit_once(k_gemv_f32_q6, (int)(kGemvF32MaxCols * 4), attr);
     static int per_cu = -1, n_cu = 0;
     if (per_cu < 0) {
         int dev = 0, blk = 0;
-        (void)hipFuncSetAttribute((const void*)k_gemv_f32_q6,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(kGemvF32MaxCols * 4));
         (void)hipGetDevice(&dev);
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_gemv_f32_q6, 256,
