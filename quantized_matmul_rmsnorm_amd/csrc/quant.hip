@@ -11,12 +11,12 @@
 // subnormals with amax <= 63 * 2^-149, where amax / 127 rounds to zero) has
 // q = 0 and S = 0.
 //
-// Geometry.  One workgroup of 4 waves per row (per row segment for SwiGLU and
-// the standalone quantise, whose rows need no row-wide reduction); the row is
-// swept in rounds of 256 values, round r belonging to
-// wave r % 4: in round r lane l owns the
-// float4 at 256*r + 4*l, so each wave access is one
-// contiguous 1 KiB (the pages' rule that a full-width coalesced access must
+// Geometry.  One workgroup of W = 4 waves per row (per row segment for SwiGLU
+// and the standalone quantise, whose rows need no row-wide reduction; W = 8
+// for an RMSNorm of at most 4 rows); the row is swept in rounds of 256
+// values, round r belonging to wave r % W: in round r lane l owns the float4
+// at 256*r + 4*l, so each wave access is one contiguous 1 KiB (the pages'
+// rule that a full-width coalesced access must
 // never be broken), and the 8 consecutive lanes 8g..8g+7 hold exactly one
 // 32-block.  amax and the code sum are reduced inside those 8 lanes with DPP
 // (quad_perm xor-1, xor-2, then row_half_mirror).  Max and integer sums are
@@ -30,10 +30,10 @@
 // read with ordinary loads (the weight vector serves every row).
 //
 // RMSNorm accumulates sum(x^2) in f64 (products of f32 values are exact in
-// f64): per lane, then across the wave, then the four wave sums in a fixed
+// f64): per lane, then across the wave, then the W wave sums in a fixed
 // order through LDS; the scale is rounded once from f64, which makes it
 // independent of the summation order to within one f64 rounding.  While a
-// wave's share of the row fits (d <= 4*256*MAXR) its x, and the matching
+// wave's share of the row fits (d <= W*256*MAXR) its x, and the matching
 // rounds of the weight vector (loaded with x, before the row sum), stay in
 // registers between the two passes; longer rows are re-read.
 //
@@ -137,14 +137,14 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // One workgroup (4 waves) per row; round r of the row belongs to wave r % 4.
 // MAXR > 0: a wave's rounds (at most MAXR) stay in registers between the
 // RMSNorm passes.
-template <int KIND, bool WRITE_Y, int MAXR, bool QUANT = true>
-__global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
+template <int KIND, bool WRITE_Y, int MAXR, bool QUANT = true, int WV = 4>
+__global__ __launch_bounds__(64 * WV) void k_producer(const float* __restrict__ a,
                                                   const float* __restrict__ b,
                                                   float* __restrict__ y, int n, int d,
                                                   float eps, int8_t* __restrict__ q,
                                                   uint2* __restrict__ ds, int rows,
                                                   int rps) {
-    constexpr int W = 4;   // waves per row segment
+    constexpr int W = WV;   // waves per row segment
     // rounds of one wave whose loads are in flight together (SwiGLU: its
     // segments give a wave at most 3 rounds, and the smaller buffer keeps
     // 8 waves per SIMD resident)
@@ -214,7 +214,14 @@ __global__ __launch_bounds__(256) void k_producer(const float* __restrict__ a,
         ss = wave_sum_f64(ss);
         if (lane == 0) s_ss[wave] = ss;
         __syncthreads();
-        const double tot = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+        double tot;
+        if constexpr (W == 4) {
+            tot = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+        } else {
+            tot = s_ss[0];
+#pragma unroll
+            for (int i = 1; i < W; ++i) tot += s_ss[i];
+        }
         scale = (float)(1.0 / sqrt(tot / (double)d + (double)eps));
     }
 
@@ -295,6 +302,14 @@ hipError_t dispatch_maxr(const float* a, const float* b, float* y, int64_t n, in
     const int rps = (rounds + segs - 1) / segs;
     segs = (rounds + rps - 1) / rps;
     const dim3 grid((unsigned)rows, (unsigned)segs), block(256);
+    // A few rows (decode): 8 waves per row, each with at most 8 rounds of it,
+    // so the row's loads, sum and quantise finish sooner (1 x 5120: 3.9 ->
+    // 3.3 us; the "wide block" of the decode RMSNorm).
+    if (KIND == kProdRms && n <= 4 && rounds <= 64) {
+        hipLaunchKernelGGL((k_producer<KIND, WY, 8, QUANT, 8>), grid, dim3(512), 0, s, a, b, y, (int)n,
+                           (int)d, eps, pl.q, pl.ds, (int)rows, rps);
+        return hipGetLastError();
+    }
     if (KIND == kProdRms && per_wave <= 4) {
         hipLaunchKernelGGL((k_producer<KIND, WY, 4, QUANT>), grid, block, 0, s, a, b, y, (int)n,
                            (int)d, eps, pl.q, pl.ds, (int)rows, rps);
