@@ -75,10 +75,13 @@ def test_quant_f32_special_values(ctx):
     assert_plane_equal(export_plane(ctx, x, n, d), oracle.quantize(y), "special values")
 
 
-# d 8192 and 16384 fill the 8- and 16-round register forms; 16640 and 18944
+# up to 4 rows take the 8-wave form (d up to 16384, its 64 rounds at 3 x 16384;
+# 4 rows at 4096, and 5 rows at 4096 take the 4-wave form); d 8192 and 16384
+# fill the 8- and 16-round register forms of the 4-wave form; 16640 and 18944
 # re-read x for the second pass
 @pytest.mark.parametrize("n,d", [(37, 512), (128, 3584), (1, 5120), (3314, 3584), (2, 8192),
-                                 (3, 16384), (2, 16640), (2, 18944)])
+                                 (3, 16384), (2, 16640), (2, 18944), (4, 4096), (5, 4096),
+                                 (9, 16384)])
 def test_quant_rms_fused_and_cross_mode(ctx, n, d):
     rng = synth.rng_for("test", n, f"rms{d}")
     xh = synth.activations(rng, n, d)
