@@ -218,8 +218,14 @@ int mmq_gemm_q4k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,
 int mmq_gemm_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, int64_t n,
                  float* out, void* stream);
 
-/* One-token q6_K GEMV (n == 1): out[o] = sum_k D[k/32] q[k] * w[o][k].
- * w must be registered with MMQ_USE_GEMV. */
+/* One-token q6_K GEMV (n == 1): out[o] = sum_k D[k/32] q[k] * w[o][k] for
+ * o < rows, with (q, D) the plane of a.  a: f32 [cols] device pointer, the
+ * plane key (a hit uses the recorded plane; a miss quantises a standalone
+ * and records it, unless a overlaps a dead key); out: f32 [rows] device
+ * pointer, caller-owned.  w must be a q6_K weight registered with
+ * MMQ_USE_GEMV.  Errors: MMQ_E_ARG (null, misaligned or foreign pointer),
+ * MMQ_E_TYPE (wrong type or not registered for the GEMV), MMQ_E_SHAPE,
+ * MMQ_E_DEAD_WRITE, MMQ_E_OOM (no plane memory on a miss), MMQ_E_HIP. */
 int mmvq_q6k(mmq_ctx* ctx, const mmq_weight* w, const float* a, float* out,
              void* stream);
 
