@@ -51,6 +51,22 @@ void lds_limit_once(K kernel, int bytes, std::atomic<uint64_t>& done) {
     done.fetch_or(bit);
 }
 
+// Workgroups of `kernel` resident on the current device at once (per CU
+// times CUs); a failed query counts one per CU and leaves no error behind.
+// Call sites keep the result in a function-local static, whose
+// initialisation C++ makes thread-safe.
+template <class K>
+int64_t resident_workgroups(K kernel, int threads, size_t lds) {
+    int dev = 0, n_cu = 0, blk = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, kernel, threads, lds) != hipSuccess) {
+        (void)hipGetLastError();
+        blk = 1;
+    }
+    return (int64_t)(blk > 0 ? blk : 1) * (n_cu > 0 ? n_cu : 256);
+}
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
@@ -276,17 +292,7 @@ __global__ __launch_bounds__(256) void k_mmvq_long(const MvArgs g) {
 // two rounds of resident waves, else exactly the resident waves.
 template <class F>
 int64_t mmvq_long_grid(int64_t rows) {
-    static int per_cu = -1, n_cu = 0;
-    if (per_cu < 0) {
-        int dev = 0, blk = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_mmvq_long<F>, 256, 0) != hipSuccess)
-            blk = 1;
-        per_cu = blk > 0 ? blk : 1;
-        if (n_cu <= 0) n_cu = 256;
-    }
-    const int64_t resident = (int64_t)per_cu * n_cu;
+    static const int64_t resident = resident_workgroups(k_mmvq_long<F>, 256, 0);
     const int64_t want = (rows + 7) / 8;
     return want <= 2 * resident ? want : resident;
 }
@@ -688,18 +694,9 @@ hipError_t launch_gemv_f32_q6k(const WeightDev& w, const float* x, float* out, h
     const size_t lds = (size_t)w.cols * 4;
     static std::atomic<uint64_t> attr{0};
     lds_limit_once(k_gemv_f32_q6, (int)(kGemvF32MaxCols * 4), attr);
-    static int per_cu = -1, n_cu = 0;
-    if (per_cu < 0) {
-        int dev = 0, blk = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blk, k_gemv_f32_q6, 256,
-                                                         (size_t)kGemvF32MaxCols * 4) != hipSuccess)
-            blk = 1;
-        per_cu = blk > 0 ? blk : 1;
-        if (n_cu <= 0) n_cu = 256;
-    }
-    const int64_t resident = (int64_t)per_cu * n_cu;
+    // counted at the largest staged x, so the grid never exceeds what fits
+    static const int64_t resident =
+        resident_workgroups(k_gemv_f32_q6, 256, (size_t)kGemvF32MaxCols * 4);
     const int64_t want = (w.rows + 3) / 4;
     const int64_t grid = want <= 2 * resident ? want : resident;
     hipLaunchKernelGGL(k_gemv_f32_q6, dim3((unsigned)grid), dim3(256), lds, s, g, x);
