@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--small-n", action="store_true", help="add the small-n band sweep (us per call)")
+    p.add_argument("--power", action="store_true",
+                   help="add socket power and clocks (amd-smi) under the matmuls, probes and read stream")
     p.add_argument("--decode-crossover", action="store_true",
                    help="add the q6_K decode arm's path sweep over od x id (us per call)")
     p.add_argument("--f16-reference", action="store_true",
@@ -490,15 +492,116 @@ def cpu_baseline(seconds: float):
             "producers_full": prod}
 
 
+def _smi_sample():
+    """One amd-smi reading: socket power (W) and the per-XCD shader clocks
+    (MHz), or None where the tool is missing or prints neither."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["amd-smi", "metric", "--power", "--clock"], capture_output=True,
+                             text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+    clk = []
+    for blk in re.split(r"\n\s*GFX_\d+:", txt)[1:]:
+        m = re.search(r"CLK:\s*([0-9.]+)\s*MHz", blk)
+        if m:
+            clk.append(float(m.group(1)))
+    if pw is None and not clk:
+        return None
+    return {"socket_W": float(pw.group(1)) if pw else None, "gfx_clk_MHz": clk}
+
+
+def power_sweep(mmq, torch, synth, seconds=10.0):
+    """Socket power and shader clocks while one kernel runs back to back:
+    the q4_K gate and q6_K down matmuls at 3314 tokens, the matmul's MFMA +
+    rescale probes without memory traffic (MFMAs alone, FMAs alone, both in
+    the matmul's flow) and the read stream.  Each runs for `seconds`; amd-smi
+    is sampled once, after the first third."""
+    import ctypes
+    import time
+    from quantized_matmul_rmsnorm_amd import build as _b
+    peak = ctypes.CDLL(_b.LIB_PEAK)
+    peak.mmq_peak_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    peak.mmq_peak_probe.restype = ctypes.c_int
+    peak.mmq_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p]
+    peak.mmq_peak_read.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    ctx = mmq.mmq_create(0, 0)
+    res, work, weights = {}, {}, []
+    try:
+        for name, wt, od, id_ in (("gate_q4k_18944x3584", "q4_K", 18944, 3584),
+                                  ("down_q6k_3584x18944", "q6_K", 3584, 18944)):
+            raw = synth.weights(wt, synth.rng_for("power", 0, name), od, id_)
+            code = mmq.MMQ_Q4_K if wt == "q4_K" else mmq.MMQ_Q6_K
+            w = mmq.mmq_register_weight(ctx, code, od, id_, raw, mmq.MMQ_USE_GEMM)
+            weights.append(w)
+            a = torch.from_numpy(synth.activations(synth.rng_for("power", 0, name + "a"), TOKENS, id_)).cuda()
+            o = torch.empty((TOKENS, od), dtype=torch.float32, device="cuda")
+            mmq.mmq_quant_f32(ctx, a, TOKENS, id_)
+            g = mmq.mmq_gemm_q4k if wt == "q4_K" else mmq.mmq_gemm_q6k
+            work[name] = lambda g=g, w=w, a=a, o=o: g(ctx, w, a, TOKENS, o)
+        pout = torch.empty(n_cu * 1024, dtype=torch.float32, device="cuda")
+        peak.mmq_peak_probe_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                             ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                             ctypes.POINTER(ctypes.c_int)]
+        probe_index = {}
+        for i in range(peak.mmq_peak_probe_count()):
+            nm, th, ti, mw = ctypes.c_char_p(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+            peak.mmq_peak_probe_info(i, ctypes.byref(nm), ctypes.byref(th), ctypes.byref(ti),
+                                     ctypes.byref(mw))
+            probe_index[nm.value.decode()] = i
+        for pname in ("w2_t2_mfma_only", "w2_t2_fma_only", "w2_t2_both_matmul_flow"):
+            i = probe_index[pname]
+            work["probe_" + pname] = lambda i=i: peak.mmq_peak_probe(i, pout.data_ptr(), n_cu, 4096,
+                                                                    stream.cuda_stream)
+        rbytes = 4 << 30
+        rbuf = torch.ones(rbytes // 4, dtype=torch.float32, device="cuda")
+        rout = torch.empty(32 * n_cu * 256, dtype=torch.int32, device="cuda")
+        work["read_stream_4GiB"] = lambda: peak.mmq_peak_read(rbuf.data_ptr(), rbytes, rout.data_ptr(),
+                                                             32 * n_cu, 16, stream.cuda_stream)
+        for name, fn in work.items():
+            torch.cuda.synchronize()
+            t0 = time.time()
+            sample, calls = None, 0
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            while time.time() - t0 < seconds:
+                e0.record()
+                for _ in range(10):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                calls += 10
+                if sample is None and time.time() - t0 > seconds / 3:
+                    sample = _smi_sample() or {}
+            rec = {"us_per_call": round(e0.elapsed_time(e1) * 100.0, 2), "calls": calls}
+            rec.update(sample or {})
+            res[name] = rec
+            log(f"power {name}: {rec}")
+        del rbuf, rout, pout
+    finally:
+        work.clear()
+        for w in weights:
+            mmq.mmq_weight_free(w)
+        mmq.mmq_destroy(ctx)
+    return res
+
+
 def measured_peaks(torch):
     """Ceilings measured on this device, beside the published peaks: the
     matrix pipe's rate for the f16 and int8 32x32 MFMA instructions (a
     benchmark kernel of independent MFMA chains, libmmq_peak.so); the
     matmul's per-block MFMA + rescale-FMA mix with no memory traffic (MFMAs
     alone, FMAs alone and both; hidden_frac is the share of the shorter of
-    the two that running both together hides); a read-only stream over 2 GiB
-    (the same library) and the device-to-device copy rate of a 1 GiB buffer
-    (read + write bytes)."""
+    the two that running both together hides); the overlap probes; a
+    read-only stream over 4 GiB, the best of nine launch shapes (the same
+    library); and the device-to-device copy rate of a 1 GiB buffer (read +
+    write bytes)."""
     import ctypes
     from quantized_matmul_rmsnorm_amd import build as _b
     lib = ctypes.CDLL(_b.LIB_PEAK)
@@ -829,6 +932,7 @@ def main():
         decode["aggregate_frac_measured_copy"] = round(decode["aggregate_GB_s"] / peaks["hbm_copy_GB_s"], 4)
         decode["aggregate_frac_measured_read"] = round(decode["aggregate_GB_s"] / peaks["hbm_read_GB_s"], 4)
     small = small_n_sweep(mmq, torch, synth) if args.small_n else None
+    power = power_sweep(mmq, torch, synth) if args.power else None
     crossover = decode_crossover_sweep(mmq, torch, synth) if args.decode_crossover else None
     f16ref = f16_reference(torch) if args.f16_reference else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
@@ -875,6 +979,7 @@ def main():
         "memory": memory,
         "decode_gemv": decode,
         "small_n_us": small,
+        "power": power,
         "decode_crossover_us": crossover,
         "f16_gemm_reference": f16ref,
         "cpu_baseline": cpu,
