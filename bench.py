@@ -517,8 +517,9 @@ def power_sweep(mmq, torch, synth, seconds=10.0):
     """Socket power and shader clocks while one kernel runs back to back:
     the q4_K gate and q6_K down matmuls at 3314 tokens, the matmul's MFMA +
     rescale probes without memory traffic (MFMAs alone, FMAs alone, both in
-    the matmul's flow) and the read stream.  Each runs for `seconds`; amd-smi
-    is sampled once, after the first third."""
+    the matmul's flow; on small constant operands, w2_, and on random ones
+    that change every block, r2_) and the read stream.  Each runs for
+    `seconds`; amd-smi is sampled once, after the first third."""
     import ctypes
     import time
     from quantized_matmul_rmsnorm_amd import build as _b
@@ -555,7 +556,8 @@ def power_sweep(mmq, torch, synth, seconds=10.0):
             peak.mmq_peak_probe_info(i, ctypes.byref(nm), ctypes.byref(th), ctypes.byref(ti),
                                      ctypes.byref(mw))
             probe_index[nm.value.decode()] = i
-        for pname in ("w2_t2_mfma_only", "w2_t2_fma_only", "w2_t2_both_matmul_flow"):
+        for pname in ("w2_t2_mfma_only", "w2_t2_fma_only", "w2_t2_both_matmul_flow",
+                      "r2_t2_mfma_only", "r2_t2_fma_only", "r2_t2_both_matmul_flow"):
             i = probe_index[pname]
             work["probe_" + pname] = lambda i=i: peak.mmq_peak_probe(i, pout.data_ptr(), n_cu, 4096,
                                                                     stream.cuda_stream)
@@ -714,7 +716,10 @@ def overlap_probes(torch, lib, n_cu, stream, iters=4096):
     hidden_frac = (t_mfma_only + t_fma_only - t_both) / min(t_mfma_only,
     t_fma_only): 0 when the two run one after the other, 1 when the shorter
     one is hidden completely.  A split variant is set against half of the
-    one-pipe times of its own wave count (half the waves issue each kind)."""
+    one-pipe times of its own wave count (half the waves issue each kind).
+    The r2_ probes repeat the 2-waves-per-SIMD ones on random operands that
+    change from block to block: the matrix datapath then switches as on real
+    data, which pulls the shader clock down."""
     import ctypes
     lib.mmq_peak_probe_count.restype = ctypes.c_int
     lib.mmq_peak_probe_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -731,16 +736,20 @@ def overlap_probes(torch, lib, n_cu, stream, iters=4096):
                                    ctypes.byref(mw)) != 0:
             raise RuntimeError("probe info")
         name = nm.value.decode()
-        if lib.mmq_peak_probe(i, out.data_ptr(), n_cu, iters, stream.cuda_stream) != 0:
-            raise RuntimeError(f"probe {name}: launch failed")
+        # random-operand probes pull the clock down as a matmul on real data
+        # does, so they run long enough (about 0.2 s) for the clock to settle
+        warm, reps = (64, 64) if name.startswith("r2_") else (1, 3)
+        for _ in range(warm):
+            if lib.mmq_peak_probe(i, out.data_ptr(), n_cu, iters, stream.cuda_stream) != 0:
+                raise RuntimeError(f"probe {name}: launch failed")
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(3):
+        for _ in range(reps):
             lib.mmq_peak_probe(i, out.data_ptr(), n_cu, iters, stream.cuda_stream)
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 3
+        ms = e0.elapsed_time(e1) / reps
         ops = n_cu * mw.value * iters * 2 * ti.value * 2 * (2 * 32 * 32 * 16)
         times[name] = ms
         info[name] = {"ms": round(ms, 4), "threads": th.value,
@@ -971,7 +980,9 @@ def main():
                      "frac_of_measured_i8_mfma": round(achieved / peaks["mfma_i8_32x32x32_TOPs"], 4),
                      "frac_of_measured_matmul_mix": round(achieved / peaks["matmul_mix"]["both_TFLOPs"], 4),
                      "frac_of_measured_matmul_flow": round(
-                         achieved / peaks["overlap_probes"]["w2_t2_both_matmul_flow"]["mfma_TFLOPs"], 4)},
+                         achieved / peaks["overlap_probes"]["w2_t2_both_matmul_flow"]["mfma_TFLOPs"], 4),
+                     "frac_of_measured_matmul_flow_random": round(
+                         achieved / peaks["overlap_probes"]["r2_t2_both_matmul_flow"]["mfma_TFLOPs"], 4)},
         "measured_peaks": peaks,
         "kernels": kernels,
         "graph": graph_rec,

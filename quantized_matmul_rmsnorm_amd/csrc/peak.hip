@@ -91,8 +91,11 @@ __global__ __launch_bounds__(256) void k_peak_i8(int* __restrict__ out, int iter
 // int32 block dot needs (convert, times the row's weight scale, FMA with the
 // token scale).
 template <int MODE>
-__global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int iters, float s) {
+__global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int iters, float s_arg) {
     const int t = threadIdx.x;
+    // a per-lane factor, as the matmul's token scale is: the rescale then
+    // reads only VGPRs (an SGPR operand halves the VALU issue rate)
+    const float s = s_arg * (1.0f + 0x1p-20f * (float)(t & 63));
     half8 a0, b0, a1, b1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -164,9 +167,11 @@ __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int i
         }
         block(XA, XB);
         block(XB, XA);
-        if constexpr (MODE == 1) {   // the FMAs' inputs change every round
-            XA[0][0] += 1.0f;
-            XB[1][0] -= 1.0f;
+        if constexpr (MODE == 1) {   // the FMAs' inputs: registers the compiler cannot fold
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(XA[i][r]), "+v"(XB[i][r]));
         }
     }
     float v = 0.0f;
@@ -195,20 +200,47 @@ __global__ __launch_bounds__(512) void k_peak_mix(float* __restrict__ out, int i
 // BS threads per workgroup and one workgroup per CU give BS / 256 waves per
 // SIMD.  Work per launch: blocks * (BS / 64) * iters * 2 blocks * TILES * 2
 // MFMAs of 2*32*32*16 operations (MODE 3: half the waves issue them).
-template <int BS, int TILES, int MODE, int SRC, int ZERO>
+// RND 1: the operands are random values in [-2, 2) (a hash of thread and
+// index) in four sets that successive blocks rotate through, and each block's
+// rescale factor differs, so the datapaths switch as they do on real data
+// (iters rounded up to even); RND 0: small constant operands, the same every
+// block.  The hash is Wellons' "lowbias32" integer mixer (hash-prospector).
+__device__ __forceinline__ _Float16 probe_rand(uint32_t x) {
+    x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+    return (_Float16)((float)(x & 0xFFFFu) * (1.0f / 16384.0f) - 2.0f);
+}
+
+template <int BS, int TILES, int MODE, int SRC, int ZERO, int RND = 0>
 __global__ __launch_bounds__(BS) void k_mix_probe(float* __restrict__ out, int iters, float s) {
     const int t = threadIdx.x;
     const int wave = t >> 6;
     // MODE 3: the first wave of each SIMD pair issues MFMAs, the second FMAs
     const bool do_m = MODE == 0 || MODE == 2 || (MODE == 3 && ((wave >> 2) & 1) == 0);
     const bool do_v = MODE == 1 || MODE == 2 || (MODE == 3 && ((wave >> 2) & 1) == 1);
-    half8 a0, b0, a1, b1;
+    constexpr int NSET = RND ? 4 : 1;
+    half8 a0[NSET], b0[NSET], a1[NSET], b1[NSET];
+    float sv[NSET];
+    const uint32_t seed = ((uint32_t)blockIdx.x * BS + (uint32_t)t) * 256u;
+    // the rescale factor differs per lane, as the matmul's token scale does, so
+    // the FMAs read three VGPRs (an SGPR operand would halve their issue rate)
+    const float lane_s = s * (1.0f + 0x1p-20f * (float)(t & 63));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        a0[i] = (_Float16)((t + i) & 7);
-        b0[i] = (_Float16)((t * 3 + i) & 7);
-        a1[i] = (_Float16)((t + 2 * i) & 7);
-        b1[i] = (_Float16)((t * 5 + i) & 7);
+    for (int k = 0; k < NSET; ++k) {
+        sv[k] = lane_s * (1.0f + 0.0078125f * (float)k);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (RND) {
+                a0[k][i] = probe_rand(seed + 64u * k + i);
+                b0[k][i] = probe_rand(seed + 64u * k + 8 + i);
+                a1[k][i] = probe_rand(seed + 64u * k + 16 + i);
+                b1[k][i] = probe_rand(seed + 64u * k + 24 + i);
+            } else {
+                a0[k][i] = (_Float16)((t + i) & 7);
+                b0[k][i] = (_Float16)((t * 3 + i) & 7);
+                a1[k][i] = (_Float16)((t + 2 * i) & 7);
+                b1[k][i] = (_Float16)((t * 5 + i) & 7);
+            }
+        }
     }
     f32x16 XA[TILES], XB[TILES], acc[TILES], Y[TILES];
 #pragma unroll
@@ -220,37 +252,55 @@ __global__ __launch_bounds__(BS) void k_mix_probe(float* __restrict__ out, int i
             Y[i][r] = (float)(r * 3 - i);
             acc[i][r] = 0.0f;
         }
-    auto block = [&](f32x16* Xw, const f32x16* Xr) {
+    auto block = [&](f32x16* Xw, const f32x16* Xr, int k) {
         if (do_m) {
             // operands opaque to the compiler, so a zero-started MFMA is not hoisted
-            asm volatile("" : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1));
+            asm volatile("" : "+v"(a0[k]), "+v"(b0[k]), "+v"(a1[k]), "+v"(b1[k]));
 #pragma unroll
             for (int i = 0; i < TILES; ++i) {
                 const f32x16 zero = {};
-                Xw[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i ? a1 : a0, i ? b1 : b0,
+                Xw[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i ? a1[k] : a0[k], i ? b1[k] : b0[k],
                                                                ZERO ? zero : Xw[i], 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < TILES; ++i)
-                Xw[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i ? b1 : b0, i ? a1 : a0, Xw[i], 0, 0, 0);
+                Xw[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i ? b1[k] : b0[k], i ? a1[k] : a0[k], Xw[i],
+                                                               0, 0, 0);
+            // the unrolled RND loop overwrites a buffer two blocks later without
+            // reading it: mark each block's results used so none is dropped
+            if (RND) {
+#pragma unroll
+                for (int i = 0; i < TILES; ++i) asm volatile("" : : "v"(Xw[i]));
+            }
         }
         if (do_v) {
 #pragma unroll
             for (int i = 0; i < TILES; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(s, SRC ? Y[i][r] : Xr[i][r], acc[i][r]);
+                for (int r = 0; r < 16; ++r) acc[i][r] = fmaf(sv[k], SRC ? Y[i][r] : Xr[i][r], acc[i][r]);
         }
         if (MODE == 2) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2 * TILES, 0);   // the block's MFMAs
             __builtin_amdgcn_sched_group_barrier(0x002, 16 * TILES, 0);  // then the rescale FMAs
         }
     };
-    for (int it = 0; it < iters; ++it) {
-        block(XA, XB);
-        block(XB, XA);
-        if (do_v && (SRC || !do_m)) {   // the FMAs' inputs change every round
-            if (SRC) { Y[0][0] += 1.0f; Y[TILES - 1][1] -= 1.0f; }
-            else { XA[0][0] += 1.0f; XB[TILES - 1][0] -= 1.0f; }
+    // two blocks per iteration; with RND the loop is unrolled by two so that
+    // four blocks walk the four operand sets with static register indices
+    for (int it = 0; it < iters; it += RND ? 2 : 1) {
+        block(XA, XB, 0);
+        block(XB, XA, RND ? 1 : 0);
+        if (RND) {
+            block(XA, XB, RND ? 2 : 0);
+            block(XB, XA, RND ? 3 : 0);
+        }
+        if (do_v && (SRC || !do_m)) {   // the FMAs' inputs: registers the compiler cannot fold
+#pragma unroll
+            for (int i = 0; i < TILES; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {   // element by element: no tuple copies
+                    if (SRC) asm volatile("" : "+v"(Y[i][r]));
+                    else asm volatile("" : "+v"(XA[i][r]), "+v"(XB[i][r]));
+                }
         }
     }
     float v = 0.0f;
@@ -268,6 +318,7 @@ struct ProbeInfo {
 };
 
 #define PROBE(BS, T, M, S, Z, NAME) {NAME, BS, T, M, S, Z, k_mix_probe<BS, T, M, S, Z>}
+#define PROBE_RND(BS, T, M, S, Z, NAME) {NAME, BS, T, M, S, Z, k_mix_probe<BS, T, M, S, Z, 1>}
 const ProbeInfo kProbes[] = {
     PROBE(512, 2, 0, 0, 1, "w2_t2_mfma_only"),
     PROBE(512, 2, 1, 0, 1, "w2_t2_fma_only"),
@@ -284,8 +335,12 @@ const ProbeInfo kProbes[] = {
     PROBE(1024, 1, 2, 0, 1, "w4_t1_both_matmul_flow"),
     PROBE(1024, 1, 2, 1, 1, "w4_t1_both_independent"),
     PROBE(1024, 1, 3, 1, 1, "w4_t1_split_waves"),
+    PROBE_RND(512, 2, 0, 0, 1, "r2_t2_mfma_only"),
+    PROBE_RND(512, 2, 1, 0, 1, "r2_t2_fma_only"),
+    PROBE_RND(512, 2, 2, 0, 1, "r2_t2_both_matmul_flow"),
 };
 #undef PROBE
+#undef PROBE_RND
 constexpr int kNumProbes = sizeof(kProbes) / sizeof(kProbes[0]);
 
 // Read-only stream: each thread walks the buffer grid-stride in 16 B
