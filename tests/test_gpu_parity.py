@@ -179,6 +179,40 @@ def test_gemm_parity(ctx, wtype, n, od, id_):
     mmq.mmq_weight_free(w)
 
 
+def test_tiny_chain_rms_plane_q4k(ctx):
+    """The tiny workload end to end: 32 tokens x hidden 256, the RMSNorm
+    producer (weight in [0.5, 1.5), eps 1e-6) into a skip-write plane, then the
+    q4_K 512 x 256 matmul, which finds that plane in the cache.  The plane
+    equals the one written with y and meets the fused bar against the oracle;
+    the matmul meets the element-wise bar on it."""
+    cfg = synth.CONFIGS["tiny"]
+    n, d, od = cfg["n"], cfg["hidden"], cfg["od"]
+    rng = synth.rng_for("test", n, "tinychain")
+    xh = synth.activations(rng, n, d)
+    wh = synth.rms_weight(rng, d)
+    raw = synth.q4k_weights(rng, od, d)
+    y_ref = oracle.rmsnorm(xh, wh, EPS)
+    w = mmq.mmq_register_weight(ctx, mmq.MMQ_Q4_K, od, d, raw, mmq.MMQ_USE_GEMM)
+    x, g = dev_tensor(xh), dev_tensor(wh)
+    y0 = torch.empty((n, d), dtype=torch.float32, device="cuda")   # never written
+    y1 = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    out = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmq_quant_rms(ctx, x, g, y0, n, d, EPS, 0)
+    hits, misses = mmq.mmq_stats(ctx)["cache_hits"], mmq.mmq_stats(ctx)["cache_misses"]
+    mmq.mmq_gemm_q4k(ctx, w, y0, n, out)
+    st = mmq.mmq_stats(ctx)
+    assert (st["cache_hits"], st["cache_misses"]) == (hits + 1, misses)
+    p0 = export_plane(ctx, y0, n, d)
+    mmq.mmq_quant_rms(ctx, x, g, y1, n, d, EPS, 1)
+    p1 = export_plane(ctx, y1, n, d)
+    torch.cuda.synchronize()
+    assert_plane_equal(p0, p1, "tiny: skip-write vs written plane")
+    assert_fused_close(p1, oracle.quantize(y_ref), y1.cpu().numpy(), y_ref, "tiny rms")
+    ref = gemm_ref("q4_K", *p0, raw, od, d)
+    assert_gemm_close(out.cpu().numpy(), ref, "tiny q4_K 512x256")
+    mmq.mmq_weight_free(w)
+
+
 @pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
 def test_gemm_degenerate_activation_rows(ctx, wtype):
     """Rows the plane encodes at its edges: all zero (D = 0, S = 0), one
