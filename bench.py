@@ -717,9 +717,9 @@ def overlap_probes(torch, lib, n_cu, stream, iters=4096):
     t_fma_only): 0 when the two run one after the other, 1 when the shorter
     one is hidden completely.  A split variant is set against half of the
     one-pipe times of its own wave count (half the waves issue each kind).
-    The r2_ probes repeat the 2-waves-per-SIMD ones on random operands that
-    change from block to block: the matrix datapath then switches as on real
-    data, which pulls the shader clock down."""
+    The r2_ and r4_ probes repeat the 2- and 4-waves-per-SIMD ones on random
+    operands that change from block to block: the matrix datapath then
+    switches as on real data, which pulls the shader clock down."""
     import ctypes
     lib.mmq_peak_probe_count.restype = ctypes.c_int
     lib.mmq_peak_probe_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -738,7 +738,7 @@ def overlap_probes(torch, lib, n_cu, stream, iters=4096):
         name = nm.value.decode()
         # random-operand probes pull the clock down as a matmul on real data
         # does, so they run long enough (about 0.2 s) for the clock to settle
-        warm, reps = (64, 64) if name.startswith("r2_") else (1, 3)
+        warm, reps = (64, 64) if name.startswith(("r2_", "r4_")) else (1, 3)
         for _ in range(warm):
             if lib.mmq_peak_probe(i, out.data_ptr(), n_cu, iters, stream.cuda_stream) != 0:
                 raise RuntimeError(f"probe {name}: launch failed")

@@ -338,6 +338,9 @@ const ProbeInfo kProbes[] = {
     PROBE_RND(512, 2, 0, 0, 1, "r2_t2_mfma_only"),
     PROBE_RND(512, 2, 1, 0, 1, "r2_t2_fma_only"),
     PROBE_RND(512, 2, 2, 0, 1, "r2_t2_both_matmul_flow"),
+    PROBE_RND(1024, 1, 0, 0, 1, "r4_t1_mfma_only"),
+    PROBE_RND(1024, 1, 1, 0, 1, "r4_t1_fma_only"),
+    PROBE_RND(1024, 1, 2, 0, 1, "r4_t1_both_matmul_flow"),
 };
 #undef PROBE
 #undef PROBE_RND
