@@ -515,7 +515,8 @@ def _smi_sample():
 
 def power_sweep(mmq, torch, synth, seconds=10.0):
     """Socket power and shader clocks while one kernel runs back to back:
-    the q4_K gate and q6_K down matmuls at 3314 tokens, the matmul's MFMA +
+    the q4_K gate and q6_K down matmuls at 3314 tokens (also on all-zero
+    activations), the matmul's MFMA +
     rescale probes without memory traffic (MFMAs alone, FMAs alone, both in
     the matmul's flow; on small constant operands, w2_, and on random ones
     that change every block, r2_) and the read stream.  Each runs for
@@ -546,6 +547,11 @@ def power_sweep(mmq, torch, synth, seconds=10.0):
             mmq.mmq_quant_f32(ctx, a, TOKENS, id_)
             g = mmq.mmq_gemm_q4k if wt == "q4_K" else mmq.mmq_gemm_q6k
             work[name] = lambda g=g, w=w, a=a, o=o: g(ctx, w, a, TOKENS, o)
+            # the same call on all-zero activations: the same instructions with
+            # the matrix datapath's operands still
+            z = torch.zeros((TOKENS, id_), dtype=torch.float32, device="cuda")
+            mmq.mmq_quant_f32(ctx, z, TOKENS, id_)
+            work[name + "_zero_activations"] = lambda g=g, w=w, z=z, o=o: g(ctx, w, z, TOKENS, o)
         pout = torch.empty(n_cu * 1024, dtype=torch.float32, device="cuda")
         peak.mmq_peak_probe_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                              ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
