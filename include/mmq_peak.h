@@ -38,7 +38,8 @@ int mmq_peak_mfma_i8(int* out, int blocks, int iters, hipStream_t stream);
 /* The matmul's per-block instruction mix with no memory traffic, in its
  * launch shape (workgroups of 512 threads, 2 waves per SIMD): per 32-block
  * each wave issues 4 f16 32x32x16 MFMAs (two output tiles, two K-steps) and
- * the 32 FMAs of the previous block's rescale.  mode 0 issues the MFMAs only,
+ * the 32 FMAs of the previous block's rescale (a per-lane factor, so each
+ * FMA reads three VGPRs).  mode 0 issues the MFMAs only,
  * 1 the FMAs only, 2 both in the matmul's order; comparing the three times
  * shows how far the matrix pipe and the VALU overlap on this device.  mode 3
  * runs the same per-block work on int8 MFMA: 2 v_mfma_i32_32x32x32_i8 per
@@ -56,6 +57,10 @@ int mmq_peak_mix(float* out, int blocks, int iters, int mode, hipStream_t stream
  * 16 rescale FMAs, or only one of the two kinds, or (split probes) one wave
  * of each SIMD pair issues only the MFMAs and the other only the FMAs; the
  * FMAs read the previous block's MFMA results or registers no MFMA writes.
+ * Each FMA reads three VGPRs (the rescale factor differs per lane, as the
+ * matmul's token scale does).  Probes named r... run on random f16 operands
+ * that change from block to block, as real data does (iters rounded up to
+ * even); the others on small constant operands.
  * mmq_peak_probe_count() gives the number of probes; mmq_peak_probe_info(i,
  * ...) its name, threads per workgroup, output tiles per wave and MFMA-issuing
  * waves per workgroup (0..count-1, else -1); mmq_peak_probe(i, out, blocks,
