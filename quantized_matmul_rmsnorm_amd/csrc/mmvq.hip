@@ -427,9 +427,9 @@ __device__ __forceinline__ Q4::Act to_act(const ActRec& r, Q5*) { return to_act(
 // One token, rows of up to RM * 64 blocks: the plane is staged once per
 // workgroup of 4 waves in LDS as 40-byte records (for q6_K with the two half
 // sums); each wave takes one row at a time grid-stride and issues all of the
-// row's weight loads before it reads the plane -- the first row's before the
-// staging, so they stream in meanwhile.  Per lane the block terms are added
-// in round order, then the wave sum.
+// row's weight loads before it reads the plane -- the first row's right after
+// the plane's own loads, so they stream in during the staging.  Per lane the
+// block terms are added in round order, then the wave sum.
 template <class F, int RM>
 __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
@@ -449,11 +449,30 @@ __global__ __launch_bounds__(256) void k_mmvq(const MvArgs g) {
             if (r < rounds && b < nb) w[r] = F::load(g, o, b, nb, nsb);
         }
     };
+    // The plane's loads are issued before the first row's weight loads:
+    // loads complete in issue order, so the staging (and the barrier after
+    // it) waits only for the plane, and each round of the row is then summed
+    // as its weights arrive instead of after the whole row has.
+    constexpr int SB = (RM * 64 + 255) / 256;   // plane blocks per thread (nb <= RM * 64)
+    uint4 sq0[SB], sq1[SB];
+    uint2 sv[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+        const int b = threadIdx.x + 256 * k;
+        if (b < nb) {
+            const uint4* p = reinterpret_cast<const uint4*>(g.Q + (int64_t)b * kBlock);
+            sq0[k] = p[0];
+            sq1[k] = p[1];
+            sv[k] = g.ds[b];
+        }
+    }
     if (wave < od) load_row(wave);
-    for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-        const uint4* p = reinterpret_cast<const uint4*>(g.Q + (int64_t)b * kBlock);
-        const uint4 q0 = p[0], q1 = p[1];
-        const uint2 v = g.ds[b];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+        const int b = threadIdx.x + 256 * k;
+        if (b >= nb) continue;
+        const uint4 q0 = sq0[k], q1 = sq1[k];
+        const uint2 v = sv[k];
         int aux;
         if constexpr (__is_same(F, Q6)) {
             const uint32_t ones = 0x01010101u;
