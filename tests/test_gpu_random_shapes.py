@@ -24,7 +24,7 @@ WT = {"q4_K": mmq.MMQ_Q4_K, "q6_K": mmq.MMQ_Q6_K}
 NS = [1, 2, 3, 5, 8, 9, 12, 16, 17, 31, 33, 100, 129, 257]
 
 
-def _gemm_cases(count=24, budget=400_000_000):
+def _gemm_cases(count=48, budget=400_000_000):
     """(wtype, n, od, id, registered for the GEMV too); n * od * id within the
     oracle's budget, a third of the cases with n >= 100 (several 128-token
     tiles and a ragged tail)."""
@@ -41,7 +41,7 @@ def _gemm_cases(count=24, budget=400_000_000):
     return cases
 
 
-def _producer_cases(count=12):
+def _producer_cases(count=24):
     rng = np.random.default_rng(31337)
     kinds = ("rms", "swiglu", "f32")
     return [(kinds[i % 3], int(rng.integers(1, 71)), 256 * int(rng.integers(1, 81)))
