@@ -13,7 +13,8 @@
  *
  * Sources (titles of the engineering-log pages this follows):
  *   [r52]  "55 · r52 — skip-write mode 2", sections 2.2 and 3.2
- *   [r60]  "64 · r60 — flipping the verified gate set to default-on", 3.2
+ *   [r60]  "64 · r60 — the coronation: flipping the verified gate set to
+ *          default-on", section 3.2
  *   [d37]  "72 · D3-7 — attn_v-q6K MMVQ routing ...", Excerpts A, A2, C
  * The K-quant superblock layouts are not on those pages; they follow the
  * public GGUF q4_K / q5_K / q6_K definitions (256 weights per superblock).
