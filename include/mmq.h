@@ -87,6 +87,10 @@ extern "C" {
 /* ---- registration uses ------------------------------------------------ */
 #define MMQ_USE_GEMM 1u       /* prefill matmul (any n)                      */
 #define MMQ_USE_GEMV 2u       /* one-token GEMV (and the few-token band)      */
+#define MMQ_USE_GEMM_PACKED 4u /* with MMQ_USE_GEMM, q4_K only: the matmul
+                                 tiles keep the 4-bit codes (0.72 B per weight
+                                 instead of 2.16) and the matmul expands them
+                                 in registers; same results, bit for bit     */
 
 #define MMQ_PLANE_ROWS 32       /* plane rows are padded to this multiple     */
 #define MMQ_WRITE_AUTO (-1)     /* write_y: skip when allowed, degrade otherwise */
@@ -152,6 +156,12 @@ int64_t mmq_plane_rows(int64_t n);
  * The default uses: q4_K MMQ_USE_GEMM, q6_K MMQ_USE_GEMM | MMQ_USE_GEMV,
  * q5_K MMQ_USE_GEMV (q5_K has a decode arm only; MMQ_USE_GEMM with q5_K is
  * MMQ_E_TYPE).
+ * MMQ_USE_GEMM_PACKED keeps a q4_K weight's matmul tiles as 4-bit codes
+ * that the matmul expands in registers [r60 5, the "uint4 B-expand" step of
+ * the campaign; r60 6 lesson 4 weighs an f16 weight cache against packed
+ * weights, memory both ways].  The matmul returns the same bits as from the
+ * default f16 tiles, in more time.  It needs MMQ_USE_GEMM (MMQ_E_ARG
+ * otherwise) and a q4_K weight (MMQ_E_TYPE otherwise).
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE (unknown type), MMQ_E_OOM,
  * MMQ_E_HIP. */
 int mmq_register_weight(mmq_ctx* ctx, int type, int64_t rows, int64_t cols,

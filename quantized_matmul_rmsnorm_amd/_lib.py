@@ -34,6 +34,7 @@ MMQ_Q6_K = 14
 MMQ_CTX_SYNC_CHECK = 1
 MMQ_CTX_DRYRUN = 2
 MMQ_USE_GEMM = 1
+MMQ_USE_GEMM_PACKED = 4
 MMQ_USE_GEMV = 2
 MMQ_PLANE_ROWS = 32
 MMQ_WRITE_AUTO = -1

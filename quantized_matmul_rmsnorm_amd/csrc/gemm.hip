@@ -44,7 +44,14 @@
 // one basic block the scheduler can interleave; each wave raises its priority
 // while it issues a block's MFMAs, so the other wave on the SIMD runs its
 // rescale FMAs in the gaps.  Outputs are stored
-// only for t < n and o < rows.  Workgroups are mapped so that each XCD works
+// only for t < n and o < rows.
+//
+// Packed q4_K tiles (k_gemm_da_packed).  A weight registered with its 4-bit
+// codes streams 8 B per lane and block instead of 32 and the wave rebuilds
+// the same f16 operand in registers: a mask and an OR put two codes under
+// the f16 exponent of 1024 (1024 + q, exact), and one packed fma with
+// (sc_j, -1024*sc_j) gives sc_j*q exactly (at most 945).  The MFMAs then see
+// the operand the f16 tiles hold, so both forms return the same bits.  Workgroups are mapped so that each XCD works
 // on a contiguous group of output x token tiles (shared L2).
 #include <algorithm>
 
@@ -57,6 +64,21 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Eight 4-bit codes of one fragment half (code e at bits 4*(e/2) for even e,
+// 16 + 4*(e/2) for odd e) -> sc * code as eight exact f16, given the pairs
+// s2 = (sc, sc) and n2 = (-1024*sc, -1024*sc).
+__device__ __forceinline__ half8 expand_q4(uint32_t x, half2v s2, half2v n2) {
+    half8 h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t w = ((x >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
+        const half2v p = __builtin_elementwise_fma(__builtin_bit_cast(half2v, w), s2, n2);
+        h[2 * k] = p[0];
+        h[2 * k + 1] = p[1];
+    }
+    return h;
+}
 
 // bf16 bits of x, rounded to nearest even, and the value of such bits
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
@@ -146,9 +168,17 @@ struct GemmArgs {
     int compact;          // 1: partials go to part[split][tile][128][128]
 };
 
-// The matmul kernel (Q4K: q4_K weights, else q6_K).
-template <bool Q4K>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
+// The packed q4_K matmul's arguments: the common ones plus the sub-scales.
+struct GemmArgsPacked {
+    GemmArgs g;
+    const uint4* wsc;     // 8 f16 sub-scales per (row, superblock)
+    uint32_t wsc_bytes;
+};
+
+// The matmul (Q4K: q4_K weights, else q6_K; PACKED: q4_K from 4-bit tiles).
+template <bool Q4K, bool PACKED>
+__device__ __forceinline__ void gemm_da(const GemmArgs& g, const uint4* wsc, uint32_t wsc_bytes) {
+    static_assert(Q4K || !PACKED, "packed tiles are q4_K only");
     constexpr int CH = 4;                   // 32-blocks per staged activation chunk
     constexpr int SBCH = 8 / CH;
     constexpr int NDM = Q4K ? 2 : 1;
@@ -185,14 +215,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     const auto rDS = rsrc(g.ds, g.ds_bytes);
     const auto rM = rsrc(g.dmr, g.dmr_bytes);
     const auto rF = rsrc(g.mfrag, g.mfrag_bytes);
+    const auto rS = rsrc(wsc, wsc_bytes);
 
     // this wave's weight fragments: block b, half k16 at voffA + (2b + k16) KiB
     const uint32_t voffA = ((uint32_t)(og0 + ogl) * (uint32_t)K16) * 1024u + (uint32_t)lane * 16u;
     half8 ring[RA][2];
+    // packed: block b's 4-bit codes at voffA4 + 512 b
+    const uint32_t voffA4 = ((uint32_t)(og0 + ogl) * (uint32_t)nb) * 512u + (uint32_t)lane * 8u;
+    uint2 ring4[RA];
     auto load_a = [&](int b, int slot) {
+        if constexpr (PACKED) {
+            ring4[slot] = bload<uint2>(rA, voffA4, (uint32_t)b * 512u);
+        } else {
 #pragma unroll
-        for (int k16 = 0; k16 < 2; ++k16)
-            ring[slot][k16] = bload<half8>(rA, voffA + (uint32_t)(k16 * 1024), (uint32_t)b * 2048u);
+            for (int k16 = 0; k16 < 2; ++k16)
+                ring[slot][k16] = bload<half8>(rA, voffA + (uint32_t)(k16 * 1024), (uint32_t)b * 2048u);
+        }
     };
 
     const int tb = tid >> 2;
@@ -264,6 +302,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
         dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
         dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
     };
+    // packed q4_K: this lane's row's 8 sub-scales of superblock sbx as f16
+    // pairs (sc[2j], sc[2j+1]) in dst[0..3]
+    auto load_sc4 = [&](int sbx, uint32_t* dst) {
+        const uint32_t off = (uint32_t)((((og0 + ogl) * nsb + sbx) * 32 + (lane & 31)) * 16);
+        const uint4 a = bload<uint4>(rS, off, 0u);
+        dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+    };
     f32x16 acc[2], res[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -281,6 +326,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
     if (!Q4K) {
         load_sc(sb0, scv);
         load_sc(min(sb0 + 1, sb1 - 1), scn);
+    }
+    if (PACKED) {
+        load_sc4(sb0, scv);
+        load_sc4(min(sb0 + 1, sb1 - 1), scn);
     }
     if (Q4K) {   // the zero half of the [lo | 0] fragments, never written again
         for (int e = tid; e < 3 * 4 * 32 * 8; e += kThreads)
@@ -319,15 +368,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
             f32x16 X[2][2];
             auto mfma_block = [&](int j, int slot, half8 (*bf)[2], f32x16* Xo) {
                 if constexpr (Q4K) {
+                    half8 A[2];
+                    if constexpr (PACKED) {
+                        const uint32_t sp = scv[j >> 1];
+                        const half2v s2 = __builtin_bit_cast(
+                            half2v, __builtin_amdgcn_perm(sp, sp, (j & 1) ? 0x03020302u : 0x01000100u));
+                        const half2v m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+                        const half2v n2 = s2 * m1024;
+                        A[0] = expand_q4(ring4[slot].x, s2, n2);
+                        A[1] = expand_q4(ring4[slot].y, s2, n2);
+                    } else {
+                        A[0] = ring[slot][0];
+                        A[1] = ring[slot][1];
+                    }
 #pragma unroll
                     for (int k16 = 0; k16 < 2; ++k16) {
 #pragma unroll
                         for (int i = 0; i < 2; ++i) {
                             if (k16 == 0) {
                                 const f32x16 zero = {};
-                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][0], bf[i][0], zero, 0, 0, 0);
+                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], bf[i][0], zero, 0, 0, 0);
                             } else {
-                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[slot][1], bf[i][1], Xo[i], 0, 0, 0);
+                                Xo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[1], bf[i][1], Xo[i], 0, 0, 0);
                             }
                         }
                     }
@@ -427,6 +489,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
             for (int i = 0; i < 8; ++i) scv[i] = scn[i];
             load_sc(min(sb + 2, sb1 - 1), scn);
         }
+        if (PACKED) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) scv[i] = scn[i];
+            load_sc4(min(sb + 2, sb1 - 1), scn);
+        }
     }
 
     const int od = g.od;
@@ -461,6 +528,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
             }
         }
     }
+}
+
+template <bool Q4K>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_da(const GemmArgs g) {
+    gemm_da<Q4K, false>(g, nullptr, 0u);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_da_packed(const GemmArgsPacked p) {
+    gemm_da<true, true>(p.g, p.wsc, p.wsc_bytes);
 }
 
 // Sum of the K-split partials in split order (deterministic): out[i] =
@@ -583,7 +659,7 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.q = pl.q;
     a.ds = pl.ds;
     const int64_t nsb = w.cols / kSuper, og = w.rows_pad / 32;
-    a.wa_bytes = (uint32_t)(w.rows_pad * w.cols * 2);
+    a.wa_bytes = (uint32_t)(w.packed ? w.rows_pad * w.cols / 2 : w.rows_pad * w.cols * 2);
     a.dmr_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 64 : 32) * 4);
     a.mfrag_bytes = (uint32_t)(og * nsb * (w.type == 12 ? 512 * 2 : 32 * 16 * 2));
     a.q_bytes = (uint32_t)(pl.rows * pl.d);
@@ -596,7 +672,14 @@ hipError_t launch_gemm(const WeightDev& w, const PlaneView& pl, int64_t n, float
     a.n_otiles = (int)(w.rows_pad / 128);
     const int tiles = a.n_ttiles * a.n_otiles;
     auto go = [&](unsigned grid) {
-        if (w.type == 12)
+        if (w.type == 12 && w.packed) {
+            GemmArgsPacked ap;
+            ap.g = a;
+            ap.wsc = w.wsc;
+            ap.wsc_bytes = (uint32_t)(w.rows_pad * nsb * 16);
+            hipLaunchKernelGGL(k_gemm_da_packed, dim3(grid), dim3(kThreads), 0, s, ap);
+        }
+        else if (w.type == 12)
             hipLaunchKernelGGL((k_gemm_da<true>), dim3(grid), dim3(kThreads), 0, s, a);
         else
             hipLaunchKernelGGL((k_gemm_da<false>), dim3(grid), dim3(kThreads), 0, s, a);

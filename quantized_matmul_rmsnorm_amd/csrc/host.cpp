@@ -510,8 +510,13 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
         cols > ((int64_t)1 << 24))
         return fail(MMQ_E_SHAPE, "%s: rows=%lld cols=%lld (cols must be a multiple of 256)", who,
                     (long long)rows, (long long)cols);
-    if (uses & ~(MMQ_USE_GEMM | MMQ_USE_GEMV))
+    if (uses & ~(MMQ_USE_GEMM | MMQ_USE_GEMV | MMQ_USE_GEMM_PACKED))
         return fail(MMQ_E_ARG, "%s: unknown uses 0x%x", who, uses);
+    if ((uses & MMQ_USE_GEMM_PACKED) && !(uses & MMQ_USE_GEMM))
+        return fail(MMQ_E_ARG, "%s: MMQ_USE_GEMM_PACKED needs MMQ_USE_GEMM (uses=%u)", who, uses);
+    if ((uses & MMQ_USE_GEMM_PACKED) && type != MMQ_Q4_K)
+        return fail(MMQ_E_TYPE, "%s: packed matmul tiles are for q4_K weights only (type %d)", who,
+                    type);
     if (uses == 0)
         uses = type == MMQ_Q4_K ? MMQ_USE_GEMM
                : type == MMQ_Q5_K ? MMQ_USE_GEMV : (MMQ_USE_GEMM | MMQ_USE_GEMV);
@@ -527,13 +532,16 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     w.cols = cols;
     w.rows_pad = round_up(rows, kTileO);
     w.uses = uses;
+    w.packed = (uses & MMQ_USE_GEMM_PACKED) != 0;
     const int64_t nsb = cols / kSuper, nb = cols / kBlock, og = w.rows_pad / 32;
     const int64_t bpb = type == MMQ_Q4_K ? 144 : type == MMQ_Q5_K ? 176 : 210;
     const int64_t raw_bytes = rows * nsb * bpb;
-    // matmul tiles: one f16 per weight (q4_K sc*q, q6_K q-32), superblock
-    // scales, and per (row group, superblock) the q4_K mins or the q6_K
-    // sub-scales as f16
-    const int64_t wa_b = w.rows_pad * cols * 2;
+    // matmul tiles: one f16 per weight (q4_K sc*q, q6_K q-32; packed q4_K:
+    // half a byte per weight plus 8 f16 sub-scales per row and superblock),
+    // superblock scales, and per (row group, superblock) the q4_K mins or the
+    // q6_K sub-scales as f16
+    const int64_t wa_b = w.packed ? w.rows_pad * cols / 2 : w.rows_pad * cols * 2;
+    const int64_t ws_b = w.packed ? w.rows_pad * nsb * 16 : 0;
     const int64_t dmr_b = og * nsb * (type == MMQ_Q4_K ? 64 : 32) * 4;
     const int64_t mf_b = og * nsb * (type == MMQ_Q4_K ? 512 * 2 : 32 * 16 * 2);
     // one-token GEMV tiles: q6_K ql/qh/sc/d; q4_K nibbles (in ql), (sc, m)
@@ -550,7 +558,7 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
                     (long long)wa_b);
     }
     int64_t total = 0;
-    if (uses & MMQ_USE_GEMM) total += wa_b + dmr_b + mf_b;
+    if (uses & MMQ_USE_GEMM) total += wa_b + ws_b + dmr_b + mf_b;
     if (uses & MMQ_USE_GEMV) total += ql_b + qh_b + sc_b + dv_b;
     w.bytes = total;
     if (c->dry) {
@@ -579,15 +587,18 @@ int mmq_register_weight(mmq_ctx* c, int type, int64_t rows, int64_t cols, const 
     hipError_t e = hipMemcpy(raw_dev, raw_host, (size_t)raw_bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: copy"); }
     if (uses & MMQ_USE_GEMM) {
-        void *p1 = nullptr, *p2 = nullptr, *p3 = nullptr;
-        if (!dalloc(wa_b, &p1) || !dalloc(dmr_b, &p2) || (mf_b && !dalloc(mf_b, &p3))) {
+        void *p1 = nullptr, *p2 = nullptr, *p3 = nullptr, *p4 = nullptr;
+        if (!dalloc(wa_b, &p1) || !dalloc(dmr_b, &p2) || (mf_b && !dalloc(mf_b, &p3)) ||
+            (ws_b && !dalloc(ws_b, &p4))) {
             cleanup();
-            return fail(MMQ_E_OOM, "%s: %lld bytes of matmul tiles", who, (long long)(wa_b + dmr_b + mf_b));
+            return fail(MMQ_E_OOM, "%s: %lld bytes of matmul tiles", who,
+                        (long long)(wa_b + ws_b + dmr_b + mf_b));
         }
-        w.wa = (_Float16*)p1; w.dmr = (float*)p2; w.mfrag = (_Float16*)p3;
+        w.wa = (_Float16*)p1; w.dmr = (float*)p2; w.mfrag = (_Float16*)p3; w.wsc = (uint4*)p4;
         e = hipMemset(p1, 0, (size_t)wa_b);   // padded rows stay zero weights
         if (e == hipSuccess) e = hipMemset(p2, 0, (size_t)dmr_b);
         if (e == hipSuccess && p3) e = hipMemset(p3, 0, (size_t)mf_b);
+        if (e == hipSuccess && p4) e = hipMemset(p4, 0, (size_t)ws_b);
         if (e == hipSuccess) e = launch_repack_gemm((const uint8_t*)raw_dev, w, nullptr);
         if (e != hipSuccess) { cleanup(); return hip_fail(e, "mmq_register_weight: repack"); }
     }
@@ -618,7 +629,7 @@ void mmq_weight_free(mmq_weight* h) {
     if (!h->dry) {
         (void)hipSetDevice(h->ctx->device);
         (void)hipDeviceSynchronize();
-        void* ps[] = {h->w.wa,    h->w.dmr,   h->w.mfrag, h->w.gv_ql,
+        void* ps[] = {h->w.wa,    h->w.dmr,   h->w.mfrag, h->w.wsc,  h->w.gv_ql,
                       h->w.gv_qh, h->w.gv_h5, h->w.gv_sc, h->w.gv_d};
         for (void* p : ps)
             if (p) (void)hipFree(p);

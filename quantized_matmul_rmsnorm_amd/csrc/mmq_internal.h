@@ -32,7 +32,10 @@ struct WeightDev {
     int64_t rows = 0, cols = 0, rows_pad = 0;
     unsigned uses = 0;
     // prefill matmul tiles
-    _Float16* wa = nullptr;   // f16 integer-valued A fragments (q4_K sc*q, q6_K q-32)
+    bool packed = false;      // q4_K registered with MMQ_USE_GEMM_PACKED
+    _Float16* wa = nullptr;   // f16 integer-valued A fragments (q4_K sc*q, q6_K q-32);
+                              // packed: the 4-bit codes, 8 B per lane and block
+    uint4* wsc = nullptr;     // packed: [row group][superblock][32 rows] 8 f16 sub-scales
     float* dmr = nullptr;     // per (row group, superblock) scales, fragment order
     _Float16* mfrag = nullptr;// q4_K: 6-bit mins as f16, fragment order;
                               // q6_K: [row group][superblock][32 rows][16] f16 sub-scales

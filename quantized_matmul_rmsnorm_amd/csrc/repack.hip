@@ -27,6 +27,13 @@
 //         dmr[og][sb][{d,dmin}][half][r] f32, r/half as the MFMA output row
 //             of ol: ol = 8*(r/4) + 4*half + r%4
 //         mfrag[og][sb][lane][j] = bf16(m_j) for both lane halves (exact)
+//   q4_K packed (MMQ_USE_GEMM_PACKED): the same fragments as 4-bit codes,
+//         wa4[og][b][lane] uint2 for 32-block b: .x holds the lane's 8 codes
+//         of k16 = 2b, .y those of 2b + 1; code e sits at bits 4*(e/2) (e
+//         even) or 16 + 4*(e/2) (e odd), so that one mask and one OR put codes
+//         e and e+1 under the f16 exponent of 1024 as a pair;
+//         wsc[og][sb][ol] uint4 = f16(sc_j), j = 0..7 (exact);
+//         dmr and mfrag as above
 //   q6_K: wa[og][k16][lane][e] = f16(q - 32)     (exact; the matmul forms
 //             sc * (q - 32), 13 bits, as two exact f16 parts in registers)
 //         mfrag[og][sb][ol][i] = f16(sc_i), i = 0..15 (exact)
@@ -133,6 +140,58 @@ __global__ void k_repack_q4k_gemm(const uint8_t* __restrict__ raw, int64_t rows,
     dm[half * 16 + r] = d;
     dm[32 + half * 16 + r] = dmin;
     // mins as bf16 bits (exact: at most 6 significant bits)
+    uint16_t* mf = reinterpret_cast<uint16_t*>(mfrag) + (og * nsb + sb) * 512;
+    for (int j = 0; j < 8; ++j) {
+        const uint16_t bits = (uint16_t)(__float_as_uint((float)mn[j]) >> 16);
+        mf[ol * 8 + j] = bits;
+        mf[(ol + 32) * 8 + j] = bits;
+    }
+}
+
+// Packed q4_K tiles: one thread per (row, superblock) of the real rows.  A
+// row owns whole 32-bit words of wa4 (lanes ol and ol + 32), so no two
+// threads write one word.
+__global__ void k_repack_q4k_gemm_packed(const uint8_t* __restrict__ raw, int64_t rows,
+                                         int64_t cols, uint32_t* __restrict__ wa4,
+                                         uint4* __restrict__ wsc, float* __restrict__ dmr,
+                                         _Float16* __restrict__ mfrag) {
+    const int64_t nsb = cols / kSuper;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nsb) return;
+    const int64_t o = idx / nsb, sb = idx % nsb;
+    const uint8_t* blk = raw + idx * 144;
+    float d, dmin;
+    int sc[8], mn[8];
+    q4k_decode(blk, d, dmin, sc, mn);
+    const int64_t og = o / 32, nb = cols / kBlock;
+    const int ol = (int)(o % 32);
+    for (int j = 0; j < 8; ++j) {            // 32-block b = 8*sb + j
+        const int64_t b = sb * 8 + j;
+        for (int step = 0; step < 2; ++step) {
+            for (int hl = 0; hl < 2; ++hl) {  // lane half: k % 16 in [8*hl, 8*hl + 8)
+                uint32_t word = 0;
+                for (int e = 0; e < 8; ++e) {
+                    const int q = q4k_quant(blk, 32 * j + 16 * step + 8 * hl + e);
+                    const int bit = (e & 1) ? 16 + 4 * (e >> 1) : 4 * (e >> 1);
+                    word |= (uint32_t)q << bit;
+                }
+                const int lane = ol + 32 * hl;
+                wa4[((og * nb + b) * 64 + lane) * 2 + step] = word;
+            }
+        }
+    }
+    uint32_t sp[4];
+    for (int j = 0; j < 4; ++j) {
+        const uint16_t lo = __builtin_bit_cast(uint16_t, (_Float16)(float)sc[2 * j]);
+        const uint16_t hi = __builtin_bit_cast(uint16_t, (_Float16)(float)sc[2 * j + 1]);
+        sp[j] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    wsc[(og * nsb + sb) * 32 + ol] = make_uint4(sp[0], sp[1], sp[2], sp[3]);
+    int half;
+    const int r = out_reg(ol, half);
+    float* dm = dmr + (og * nsb + sb) * 64;
+    dm[half * 16 + r] = d;
+    dm[32 + half * 16 + r] = dmin;
     uint16_t* mf = reinterpret_cast<uint16_t*>(mfrag) + (og * nsb + sb) * 512;
     for (int j = 0; j < 8; ++j) {
         const uint16_t bits = (uint16_t)(__float_as_uint((float)mn[j]) >> 16);
@@ -272,7 +331,10 @@ __global__ void k_repack_q5k_gemv(const uint8_t* __restrict__ raw, int64_t rows,
 hipError_t launch_repack_gemm(const uint8_t* raw_dev, const WeightDev& w, hipStream_t s) {
     const int64_t total = w.rows * (w.cols / kSuper);
     const dim3 block(128), grid((unsigned)((total + 127) / 128));
-    if (w.type == 12)
+    if (w.type == 12 && w.packed)
+        hipLaunchKernelGGL(k_repack_q4k_gemm_packed, grid, block, 0, s, raw_dev, w.rows, w.cols,
+                           reinterpret_cast<uint32_t*>(w.wa), w.wsc, w.dmr, w.mfrag);
+    else if (w.type == 12)
         hipLaunchKernelGGL(k_repack_q4k_gemm, grid, block, 0, s, raw_dev, w.rows, w.cols, w.wa,
                            w.dmr, w.mfrag);
     else

@@ -149,7 +149,7 @@ def test_registration_validation(ctx):
     assert _status(mmq.mmq_register_weight, ctx, 11, 4, 256, raw) == mmq.MMQ_E_TYPE
     assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 300, raw) == mmq.MMQ_E_SHAPE
     assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 0, 256, raw) == mmq.MMQ_E_SHAPE
-    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw, 0x4) == mmq.MMQ_E_ARG
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw, 0x8) == mmq.MMQ_E_ARG
     w4 = _w(ctx, mmq.MMQ_Q4_K, 512, 256)
     # q4_K one-token GEMV layout: 16 B of codes + 2 B (sc, m) per 32 weights, (d, dmin) per 256
     w4v = _w(ctx, mmq.MMQ_Q4_K, 300, 512, mmq.MMQ_USE_GEMV)
@@ -168,6 +168,40 @@ def test_registration_validation(ctx):
     mmq.mmq_weight_free(w4)
     assert mmq.mmq_stats(ctx)["weight_bytes"] == mmq.mmq_weight_bytes(w6)
     mmq.mmq_weight_free(w6)
+
+
+def test_packed_q4k_registration(ctx):
+    """MMQ_USE_GEMM_PACKED: q4_K only, only beside MMQ_USE_GEMM, refused before
+    any allocation; the tiles take half a byte per weight plus 8 f16
+    sub-scales per row and superblock, beside the same scales and mins; the
+    matmul accepts the weight like any other."""
+    P, G = mmq.MMQ_USE_GEMM_PACKED, mmq.MMQ_USE_GEMM
+    raw4, raw5, raw6 = (np.zeros(b * 4, np.uint8) for b in (144, 176, 210))
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw4, P) == mmq.MMQ_E_ARG
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q4_K, 4, 256, raw4,
+                   P | mmq.MMQ_USE_GEMV) == mmq.MMQ_E_ARG
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q6_K, 4, 256, raw6, G | P) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmq_register_weight, ctx, mmq.MMQ_Q5_K, 4, 256, raw5, G | P) == mmq.MMQ_E_TYPE
+    assert mmq.mmq_stats(ctx)["weight_bytes"] == 0
+    w = _w(ctx, mmq.MMQ_Q4_K, 1000, 512, G | P)
+    rows_pad, nsb = 1024, 2
+    packed = rows_pad * 512 // 2 + rows_pad * nsb * 16 + (rows_pad // 32) * nsb * (64 * 4 + 512 * 2)
+    assert mmq.mmq_weight_bytes(w) == packed
+    wf = _w(ctx, mmq.MMQ_Q4_K, 1000, 512, G)
+    assert mmq.mmq_weight_bytes(wf) == rows_pad * 512 * 2 + (rows_pad // 32) * nsb * (64 * 4 + 512 * 2)
+    assert mmq.mmq_weight_bytes(wf) / mmq.mmq_weight_bytes(w) > 2.9
+    # with the GEMV layout too: both sets of tiles
+    wb = _w(ctx, mmq.MMQ_Q4_K, 1000, 512, G | P | mmq.MMQ_USE_GEMV)
+    assert mmq.mmq_weight_bytes(wb) == packed + 1000 * 16 * (16 + 2) + 1000 * 2 * 8
+    A, O = 0x100000, 0x200000
+    assert _status(mmq.mmq_gemm_q4k, ctx, w, A, 300, O) == mmq.MMQ_OK
+    assert _status(mmq.mmq_gemm_q6k, ctx, w, A, 300, O) == mmq.MMQ_E_TYPE
+    assert _status(mmq.mmvq_q4k, ctx, w, A, O) == mmq.MMQ_E_TYPE      # no GEMV tiles
+    assert _status(mmq.mmvq_q4k, ctx, wb, A, O) == mmq.MMQ_OK
+    assert mmq.mmq_stats(ctx)["launches_gemm_q4k"] == 1
+    for h in (w, wf, wb):
+        mmq.mmq_weight_free(h)
+    assert mmq.mmq_stats(ctx)["weight_bytes"] == 0
 
 
 def test_q5k_is_a_decode_only_type(ctx):
@@ -200,7 +234,7 @@ def test_q5k_is_a_decode_only_type(ctx):
 
 def test_binding_constants_match_the_header():
     text = open(HEADER).read()
-    for name in ("MMQ_Q4_K", "MMQ_Q5_K", "MMQ_Q6_K", "MMQ_USE_GEMM", "MMQ_USE_GEMV",
+    for name in ("MMQ_Q4_K", "MMQ_Q5_K", "MMQ_Q6_K", "MMQ_USE_GEMM", "MMQ_USE_GEMV", "MMQ_USE_GEMM_PACKED",
                  "MMQ_DECODE_F32_GATE", "MMQ_PLANE_ROWS", "MMQ_NOALLOC_MAX_COLS"):
         m = re.search(rf"#define {name}\s+\(?(-?\d+)", text)
         assert m, name

@@ -213,7 +213,7 @@ def test_tiny_chain_rms_plane_q4k(ctx):
     mmq.mmq_weight_free(w)
 
 
-@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K", "q4_K packed"])
 def test_gemm_degenerate_activation_rows(ctx, wtype):
     """Rows the plane encodes at its edges: all zero (D = 0, S = 0), one
     nonzero block among zero blocks, one nonzero value per block, and row
@@ -230,8 +230,11 @@ def test_gemm_degenerate_activation_rows(ctx, wtype):
     y[5] *= np.float32(1e-20)
     y[6, :512] = 0.0
     y = np.ascontiguousarray(y, np.float32)
+    packed = wtype.endswith("packed")
+    wtype = wtype.split()[0]
     raw = synth.weights(wtype, synth.rng_for("test", od, f"degenw{wtype}"), od, id_)
-    w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw, mmq.MMQ_USE_GEMM)
+    w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw,
+                                mmq.MMQ_USE_GEMM | (mmq.MMQ_USE_GEMM_PACKED if packed else 0))
     a = dev_tensor(y)
     out = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
     (mmq.mmq_gemm_q4k if wtype == "q4_K" else mmq.mmq_gemm_q6k)(ctx, w, a, n, out)
@@ -327,6 +330,41 @@ def test_gemm_full_size_sampled(ctx, wtype, od, id_):
     assert_gemm_close(got[np.ix_(tok, outs)], ref, f"{wtype} {od}x{id_} sampled")
     assert np.isfinite(got).all()
     mmq.mmq_weight_free(w)
+
+
+# ------------------------------------------------------------------ packed q4_K tiles
+PACKED_SHAPES = [(1, 128, 256), (37, 256, 512), (200, 384, 1024), (130, 1000, 768),
+                 (16, 32, 2304), (70, 512, 2560), (130, 384, 4864), (3, 18944, 3584),
+                 (3314, 512, 3584), (3314, 3584, 3584), (3314, 18944, 3584)]
+
+
+@pytest.mark.parametrize("n,od,id_", PACKED_SHAPES)
+def test_gemm_packed_q4k_bit_identical(ctx, n, od, id_):
+    """A q4_K weight registered with its 4-bit codes (MMQ_USE_GEMM_PACKED)
+    returns the same bits as from the f16 tiles on every output: ragged
+    shapes, the K split (few output tiles), full rounds, and the tail split of
+    the 18944 x 3584 gate at 3314 tokens; small shapes also meet the oracle's
+    bar on every output.  The tiles take about a third of the bytes."""
+    rng = synth.rng_for("test", n * 7 + od, f"packed{id_}")
+    raw = synth.weights("q4_K", rng, od, id_)
+    wf = mmq.mmq_register_weight(ctx, WT["q4_K"], od, id_, raw, mmq.MMQ_USE_GEMM)
+    wp = mmq.mmq_register_weight(ctx, WT["q4_K"], od, id_, raw,
+                                 mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMM_PACKED)
+    assert mmq.mmq_weight_bytes(wf) > 2.9 * mmq.mmq_weight_bytes(wp)
+    a = dev_tensor(_act("packed", n, id_))
+    of = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
+    op = torch.full((n, od), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmq_gemm_q4k(ctx, wf, a, n, of)
+    mmq.mmq_gemm_q4k(ctx, wp, a, n, op)
+    torch.cuda.synchronize()
+    assert torch.isfinite(op).all()
+    assert torch.equal(of, op), f"packed {n}x{od}x{id_}: not bit-identical to the f16 tiles"
+    if n * od * id_ <= 200_000_000:
+        q, D, S = export_plane(ctx, a, n, id_)
+        ref = gemm_ref("q4_K", q, D, S, raw, od, id_)
+        assert_gemm_close(op.cpu().numpy(), ref, f"packed q4_K n={n} {od}x{id_}")
+    mmq.mmq_weight_free(wf)
+    mmq.mmq_weight_free(wp)
 
 
 # ------------------------------------------------------------------ one-token GEMV

@@ -25,9 +25,10 @@ NS = [1, 2, 3, 5, 8, 9, 12, 16, 17, 31, 33, 100, 129, 257]
 
 
 def _gemm_cases(count=48, budget=400_000_000):
-    """(wtype, n, od, id, registered for the GEMV too); n * od * id within the
-    oracle's budget, a third of the cases with n >= 100 (several 128-token
-    tiles and a ragged tail)."""
+    """(wtype, n, od, id, registered for the GEMV too, packed q4_K tiles);
+    n * od * id within the oracle's budget, a third of the cases with
+    n >= 100 (several 128-token tiles and a ragged tail), every other q4_K
+    case on the packed 4-bit matmul tiles."""
     rng = np.random.default_rng(20261203)
     cases = []
     while len(cases) < count:
@@ -37,7 +38,8 @@ def _gemm_cases(count=48, budget=400_000_000):
         id_ = 256 * int(rng.integers(1, 25))
         both = bool(rng.integers(0, 2))
         if n * od * id_ <= budget:
-            cases.append((wtype, n, od, id_, both))
+            packed = wtype == "q4_K" and (len(cases) // 2) % 2 == 1
+            cases.append((wtype, n, od, id_, both, packed))
     return cases
 
 
@@ -61,11 +63,12 @@ def ctx(_module_ctx):
     return _module_ctx
 
 
-@pytest.mark.parametrize("wtype,n,od,id_,both", _gemm_cases())
-def test_random_matmul_shape(ctx, wtype, n, od, id_, both):
+@pytest.mark.parametrize("wtype,n,od,id_,both,packed", _gemm_cases())
+def test_random_matmul_shape(ctx, wtype, n, od, id_, both, packed):
     tag = f"rand{wtype}{n}x{od}x{id_}"
     raw = synth.weights(wtype, synth.rng_for("random", n, tag), od, id_)
-    uses = mmq.MMQ_USE_GEMM | (mmq.MMQ_USE_GEMV if both else 0)
+    uses = (mmq.MMQ_USE_GEMM | (mmq.MMQ_USE_GEMV if both else 0) |
+            (mmq.MMQ_USE_GEMM_PACKED if packed else 0))
     w = mmq.mmq_register_weight(ctx, WT[wtype], od, id_, raw, uses)
     try:
         rng = synth.rng_for("random", n, tag + "a")
