@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--layers", type=int, default=LAYERS, help=argparse.SUPPRESS)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-packed", action="store_true",
+                   help="skip the packed q4_K tiles leg (both tile forms timed per call)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--small-n", action="store_true", help="add the small-n band sweep (us per call)")
     p.add_argument("--power", action="store_true",
@@ -244,6 +246,66 @@ def decode_gemv(mmq, torch, synth):
         mmq.mmq_cache_clear(ctx)
         mmq.mmq_destroy(ctx)
     return res
+
+
+def packed_q4k(mmq, torch, synth, chain, rounds=3, reps=10):
+    """Layer 0's q4_K matmuls with their weights registered a second time as
+    packed 4-bit tiles (MMQ_USE_GEMM_PACKED): per-call time of both forms on
+    the same recorded plane (alternating rounds, best round), whether the two
+    outputs are the same bits, and the device bytes of each form."""
+    L, c, n = chain.layers[0], chain.ctx, TOKENS
+    a = L["attn_out"]
+    shapes, f16_b, packed_b = {}, 0, 0
+    for name, wt, od, id_, _ in LAYER_GEMMS:
+        if wt != "q4_K":
+            continue
+        raw = synth.weights(wt, synth.rng_for("chain7b", chain.layer_ids[0], name), od, id_)
+        wp = mmq.mmq_register_weight(c, mmq.MMQ_Q4_K, od, id_, raw,
+                                     mmq.MMQ_USE_GEMM | mmq.MMQ_USE_GEMM_PACKED)
+        del raw
+        out_f = chain.out[name]
+        out_p = torch.empty_like(out_f)
+        mmq.mmq_gemm_q4k(c, L[name], a, n, out_f)
+        mmq.mmq_gemm_q4k(c, wp, a, n, out_p)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out_f, out_p))
+        best = {"f16": float("inf"), "packed": float("inf")}
+        for _ in range(rounds):
+            for form, w, o in (("f16", L[name], out_f), ("packed", wp, out_p)):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    mmq.mmq_gemm_q4k(c, w, a, n, o)
+                e1.record()
+                torch.cuda.synchronize()
+                best[form] = min(best[form], e0.elapsed_time(e1) * 1e3 / reps)
+        bf, bp = mmq.mmq_weight_bytes(L[name]), mmq.mmq_weight_bytes(wp)
+        f16_b += bf
+        packed_b += bp
+        shapes[name] = {"od": od, "id": id_, "f16_us": round(best["f16"], 2),
+                        "packed_us": round(best["packed"], 2),
+                        "packed_over_f16": round(best["packed"] / best["f16"], 4),
+                        "bit_identical": same,
+                        "f16_bytes_per_weight": round(bf / (od * id_), 4),
+                        "packed_bytes_per_weight": round(bp / (od * id_), 4)}
+        mmq.mmq_weight_free(wp)
+    mmq.mmq_cache_clear(c)
+    mean = lambda k: sum(v[k] for v in shapes.values()) / len(shapes)
+    q6_b = sum(mmq.mmq_weight_bytes(L[name]) for name, wt, _, _, _ in LAYER_GEMMS if wt == "q6_K")
+    raw_b = sum(od * id_ // 256 * (144 if wt == "q4_K" else 210) for _, wt, od, id_, _ in LAYER_GEMMS)
+    rec = {"shapes": shapes, "tokens": n,
+           "mean_call_f16_us": round(mean("f16_us"), 2), "mean_call_packed_us": round(mean("packed_us"), 2),
+           "mean_packed_over_f16": round(mean("packed_us") / mean("f16_us"), 4),
+           "all_bit_identical": all(v["bit_identical"] for v in shapes.values()),
+           "chain_registered_bytes_f16": len(chain.layers) * (f16_b + q6_b),
+           "chain_registered_bytes_packed_q4k": len(chain.layers) * (packed_b + q6_b),
+           "chain_raw_bytes": len(chain.layers) * raw_b}
+    log(f"packed q4_K tiles: {rec['mean_call_packed_us']} us per call against "
+        f"{rec['mean_call_f16_us']} (f16 tiles), bit-identical {rec['all_bit_identical']}; "
+        f"chain weights {rec['chain_registered_bytes_packed_q4k'] / 1e9:.2f} GB against "
+        f"{rec['chain_registered_bytes_f16'] / 1e9:.2f} GB (raw {rec['chain_raw_bytes'] / 1e9:.2f})")
+    return rec
 
 
 def small_n_sweep(mmq, torch, synth):
@@ -937,6 +999,7 @@ def main():
                  "launches_per_step": sum(st_b[k] - st_a[k] for k in st_b if k.startswith("launches_"))}
     log(f"graph replay: {graph_ms:.2f} ms/step")
 
+    packed = None if args.no_packed else packed_q4k(mmq, torch, synth, chain)
     traffic = measured_traffic()
     peaks = measured_peaks(torch)
     log(f"measured: f16 MFMA {peaks['mfma_f16_32x32x16_TFLOPs']} TFLOP/s, int8 MFMA "
@@ -994,6 +1057,7 @@ def main():
         "graph": graph_rec,
         "cache": {k: st1[k] - st0[k] for k in ("cache_hits", "cache_misses", "cache_refusals")},
         "memory": memory,
+        "packed_q4k_tiles": packed,
         "decode_gemv": decode,
         "small_n_us": small,
         "power": power,
