@@ -7,8 +7,9 @@ the same chain is run eagerly; every replay must equal the eager run bit for
 bit (same kernels, same inputs), and the last replay's final layer is checked
 against the CPU oracle: the o projection on the oracle's own quantisation of
 its input, every matmul on the exported plane, and the SwiGLU plane against
-the oracle's SwiGLU of the replayed gate/up outputs.  The launch census of the
-capture comes from mmq_stats.  Capture rules tested: nothing is allocated
+the oracle's SwiGLU of the replayed gate/up outputs.  The chain runs once with
+the q4_K weights on f16 tiles and once on packed 4-bit tiles.  The launch
+census of the capture comes from mmq_stats.  Capture rules tested: nothing is allocated
 during a capture (a plane that would need a bigger slot is refused before
 anything is recorded).
 """
@@ -30,7 +31,7 @@ GEMMS = [("q", "q4_K", HID, HID), ("k", "q4_K", KV, HID), ("v", "q6_K", KV, HID)
 
 
 class Chain:
-    def __init__(self, mmq):
+    def __init__(self, mmq, packed=False):
         self.m = mmq
         self.ctx = mmq.mmq_create(0, 0)
         dev = "cuda"
@@ -40,7 +41,8 @@ class Chain:
             for name, wt, od, id_ in GEMMS:
                 raw = synth.weights(wt, synth.rng_for("graph", l, name), od, id_)
                 code = mmq.MMQ_Q4_K if wt == "q4_K" else mmq.MMQ_Q6_K
-                L[name] = mmq.mmq_register_weight(self.ctx, code, od, id_, raw, mmq.MMQ_USE_GEMM)
+                uses = mmq.MMQ_USE_GEMM | (mmq.MMQ_USE_GEMM_PACKED if packed and wt == "q4_K" else 0)
+                L[name] = mmq.mmq_register_weight(self.ctx, code, od, id_, raw, uses)
             for t in ("x_attn", "attn_out", "x_ffn"):
                 L[t] = torch.empty((N, HID), dtype=torch.float32, device=dev)
             for t in ("norm_attn", "norm_ffn"):
@@ -86,8 +88,9 @@ class Chain:
         self.m.mmq_destroy(self.ctx)
 
 
-def test_chain_graph_replays_equal_eager():
-    ch = Chain(mmq)
+@pytest.mark.parametrize("packed", [False, True], ids=["f16_tiles", "packed_q4k_tiles"])
+def test_chain_graph_replays_equal_eager(packed):
+    ch = Chain(mmq, packed)
     try:
         ch.set_inputs(0)
         ch.step()                      # eager: sizes every plane slot
