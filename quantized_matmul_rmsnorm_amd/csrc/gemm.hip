@@ -48,10 +48,14 @@
 //
 // Packed q4_K tiles (k_gemm_da_packed).  A weight registered with its 4-bit
 // codes streams 8 B per lane and block instead of 32 and the wave rebuilds
-// the same f16 operand in registers: a mask and an OR put two codes under
-// the f16 exponent of 1024 (1024 + q, exact), and one packed fma with
-// (sc_j, -1024*sc_j) gives sc_j*q exactly (at most 945).  The MFMAs then see
-// the operand the f16 tiles hold, so both forms return the same bits.  Workgroups are mapped so that each XCD works
+// the operand in registers: one mask turns two codes into the f16 subnormals
+// q * 2^-24 (exact), and one packed multiply by the stored sc_j * 2^10 gives
+// sc_j*q * 2^-14 exactly (a normal f16: sc_j*q <= 945).  The MFMAs then
+// return each block dot times 2^-14, exactly, and registration stores the
+// superblock scale d times 2^14, so every rescale rounds the same value
+// scaled by a power of two: both forms return the same bits, as long as a
+// superblock's partial sum stays above 2^-112 (it falls below only for block
+// scales under about 2e-34).  Workgroups are mapped so that each XCD works
 // on a contiguous group of output x token tiles (shared L2).
 #include <algorithm>
 
@@ -66,14 +70,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Eight 4-bit codes of one fragment half (code e at bits 4*(e/2) for even e,
-// 16 + 4*(e/2) for odd e) -> sc * code as eight exact f16, given the pairs
-// s2 = (sc, sc) and n2 = (-1024*sc, -1024*sc).
-__device__ __forceinline__ half8 expand_q4(uint32_t x, half2v s2, half2v n2) {
+// 16 + 4*(e/2) for odd e) -> sc * code * 2^-14 as eight exact f16, given the
+// pair s2 = (sc * 2^10, sc * 2^10): each masked code is the f16 subnormal
+// code * 2^-24, and the product is exact (at most 945 * 2^-14, at least 2^-14
+// when not zero).
+__device__ __forceinline__ half8 expand_q4(uint32_t x, half2v s2) {
     half8 h;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t w = ((x >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
-        const half2v p = __builtin_elementwise_fma(__builtin_bit_cast(half2v, w), s2, n2);
+        const uint32_t w = (x >> (4 * k)) & 0x000F000Fu;
+        const half2v p = __builtin_bit_cast(half2v, w) * s2;
         h[2 * k] = p[0];
         h[2 * k + 1] = p[1];
     }
@@ -302,8 +308,8 @@ __device__ __forceinline__ void gemm_da(const GemmArgs& g, const uint4* wsc, uin
         dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
         dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
     };
-    // packed q4_K: this lane's row's 8 sub-scales of superblock sbx as f16
-    // pairs (sc[2j], sc[2j+1]) in dst[0..3]
+    // packed q4_K: this lane's row's 8 sub-scales of superblock sbx, times
+    // 2^10, as f16 pairs (sc[2j], sc[2j+1]) in dst[0..3]
     auto load_sc4 = [&](int sbx, uint32_t* dst) {
         const uint32_t off = (uint32_t)((((og0 + ogl) * nsb + sbx) * 32 + (lane & 31)) * 16);
         const uint4 a = bload<uint4>(rS, off, 0u);
@@ -373,10 +379,8 @@ __device__ __forceinline__ void gemm_da(const GemmArgs& g, const uint4* wsc, uin
                         const uint32_t sp = scv[j >> 1];
                         const half2v s2 = __builtin_bit_cast(
                             half2v, __builtin_amdgcn_perm(sp, sp, (j & 1) ? 0x03020302u : 0x01000100u));
-                        const half2v m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-                        const half2v n2 = s2 * m1024;
-                        A[0] = expand_q4(ring4[slot].x, s2, n2);
-                        A[1] = expand_q4(ring4[slot].y, s2, n2);
+                        A[0] = expand_q4(ring4[slot].x, s2);
+                        A[1] = expand_q4(ring4[slot].y, s2);
                     } else {
                         A[0] = ring[slot][0];
                         A[1] = ring[slot][1];

@@ -30,10 +30,11 @@
 //   q4_K packed (MMQ_USE_GEMM_PACKED): the same fragments as 4-bit codes,
 //         wa4[og][b][lane] uint2 for 32-block b: .x holds the lane's 8 codes
 //         of k16 = 2b, .y those of 2b + 1; code e sits at bits 4*(e/2) (e
-//         even) or 16 + 4*(e/2) (e odd), so that one mask and one OR put codes
-//         e and e+1 under the f16 exponent of 1024 as a pair;
-//         wsc[og][sb][ol] uint4 = f16(sc_j), j = 0..7 (exact);
-//         dmr and mfrag as above
+//         even) or 16 + 4*(e/2) (e odd), so that one mask turns codes e and
+//         e+1 into a pair of f16 subnormals (code * 2^-24);
+//         wsc[og][sb][ol] uint4 = f16(sc_j * 2^10), j = 0..7 (exact: <= 64512),
+//         so one packed multiply gives sc_j*q * 2^-14;
+//         dmr as above with d times 2^14 (exact), mfrag as above
 //   q6_K: wa[og][k16][lane][e] = f16(q - 32)     (exact; the matmul forms
 //             sc * (q - 32), 13 bits, as two exact f16 parts in registers)
 //         mfrag[og][sb][ol][i] = f16(sc_i), i = 0..15 (exact)
@@ -182,15 +183,15 @@ __global__ void k_repack_q4k_gemm_packed(const uint8_t* __restrict__ raw, int64_
     }
     uint32_t sp[4];
     for (int j = 0; j < 4; ++j) {
-        const uint16_t lo = __builtin_bit_cast(uint16_t, (_Float16)(float)sc[2 * j]);
-        const uint16_t hi = __builtin_bit_cast(uint16_t, (_Float16)(float)sc[2 * j + 1]);
+        const uint16_t lo = __builtin_bit_cast(uint16_t, (_Float16)(float)(sc[2 * j] * 1024));
+        const uint16_t hi = __builtin_bit_cast(uint16_t, (_Float16)(float)(sc[2 * j + 1] * 1024));
         sp[j] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
     wsc[(og * nsb + sb) * 32 + ol] = make_uint4(sp[0], sp[1], sp[2], sp[3]);
     int half;
     const int r = out_reg(ol, half);
     float* dm = dmr + (og * nsb + sb) * 64;
-    dm[half * 16 + r] = d;
+    dm[half * 16 + r] = d * 16384.0f;   // the block dots come out times 2^-14
     dm[32 + half * 16 + r] = dmin;
     uint16_t* mf = reinterpret_cast<uint16_t*>(mfrag) + (og * nsb + sb) * 512;
     for (int j = 0; j < 8; ++j) {
