@@ -90,7 +90,8 @@ extern "C" {
 #define MMQ_USE_GEMM_PACKED 4u /* with MMQ_USE_GEMM, q4_K only: the matmul
                                  tiles keep the 4-bit codes (0.72 B per weight
                                  instead of 2.16) and the matmul expands them
-                                 in registers; same results, bit for bit     */
+                                 in registers; same results, bit for bit,
+                                 while partial sums stay normal f32        */
 
 #define MMQ_PLANE_ROWS 32       /* plane rows are padded to this multiple     */
 #define MMQ_WRITE_AUTO (-1)     /* write_y: skip when allowed, degrade otherwise */
@@ -160,8 +161,10 @@ int64_t mmq_plane_rows(int64_t n);
  * that the matmul expands in registers [r60 5, the "uint4 B-expand" step of
  * the campaign; r60 6 lesson 4 weighs an f16 weight cache against packed
  * weights, memory both ways].  The matmul returns the same bits as from the
- * default f16 tiles, in more time.  It needs MMQ_USE_GEMM (MMQ_E_ARG
- * otherwise) and a q4_K weight (MMQ_E_TYPE otherwise).
+ * default f16 tiles, in more time (the expanded operand carries a factor
+ * 2^-14 that the stored d takes back, so a superblock's partial sum under
+ * 2^-112 or over 2^112 may round differently).  It needs MMQ_USE_GEMM
+ * (MMQ_E_ARG otherwise) and a q4_K weight (MMQ_E_TYPE otherwise).
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_TYPE (unknown type), MMQ_E_OOM,
  * MMQ_E_HIP. */
 int mmq_register_weight(mmq_ctx* ctx, int type, int64_t rows, int64_t cols,
