@@ -73,7 +73,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // 16 + 4*(e/2) for odd e) -> sc * code * 2^-14 as eight exact f16, given the
 // pair s2 = (sc * 2^10, sc * 2^10): each masked code is the f16 subnormal
 // code * 2^-24, and the product is exact (at most 945 * 2^-14, at least 2^-14
-// when not zero).
+// when not zero).  This needs f16 denormals kept, the kernels' default mode
+// (the build passes no flush or fast-math flag).
 __device__ __forceinline__ half8 expand_q4(uint32_t x, half2v s2) {
     half8 h;
 #pragma unroll
