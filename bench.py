@@ -75,7 +75,7 @@ class Chain:
     buffers (the plane keys) and matmul outputs.  `layer_ids` picks which
     layers of the 28 are built (all of them for the timed step)."""
 
-    def __init__(self, mmq, torch, synth, layers, layer_ids=None):
+    def __init__(self, mmq, torch, synth, layers, layer_ids=None, packed_q4k=False):
         self.mmq, self.torch = mmq, torch
         self.ctx = mmq.mmq_create(0, 0)
         self.layers = []
@@ -86,7 +86,8 @@ class Chain:
             for name, wt, od, id_, _ in LAYER_GEMMS:
                 raw = synth.weights(wt, synth.rng_for("chain7b", l, name), od, id_)
                 code = mmq.MMQ_Q4_K if wt == "q4_K" else mmq.MMQ_Q6_K
-                L[name] = mmq.mmq_register_weight(self.ctx, code, od, id_, raw, mmq.MMQ_USE_GEMM)
+                uses = mmq.MMQ_USE_GEMM | (mmq.MMQ_USE_GEMM_PACKED if packed_q4k and wt == "q4_K" else 0)
+                L[name] = mmq.mmq_register_weight(self.ctx, code, od, id_, raw, uses)
                 del raw
             for t in ("x_attn", "attn_out", "x_ffn"):
                 L[t] = torch.from_numpy(synth.activations(synth.rng_for("chain7b", l, t), TOKENS,
@@ -252,7 +253,8 @@ def packed_q4k(mmq, torch, synth, chain, rounds=3, reps=10):
     """Layer 0's q4_K matmuls with their weights registered a second time as
     packed 4-bit tiles (MMQ_USE_GEMM_PACKED): per-call time of both forms on
     the same recorded plane (alternating rounds, best round), whether the two
-    outputs are the same bits, and the device bytes of each form."""
+    outputs are the same bits, and the device bytes of each form.  (main()
+    adds the whole chain on packed tiles under "chain".)"""
     L, c, n = chain.layers[0], chain.ctx, TOKENS
     a = L["attn_out"]
     shapes, f16_b, packed_b = {}, 0, 0
@@ -306,6 +308,32 @@ def packed_q4k(mmq, torch, synth, chain, rounds=3, reps=10):
         f"chain weights {rec['chain_registered_bytes_packed_q4k'] / 1e9:.2f} GB against "
         f"{rec['chain_registered_bytes_f16'] / 1e9:.2f} GB (raw {rec['chain_raw_bytes'] / 1e9:.2f})")
     return rec
+
+
+def packed_chain(mmq, torch, synth, args, ops):
+    """The same chain with every q4_K weight registered on packed 4-bit tiles
+    (q6_K as before): K steps with events only at the step boundaries, after
+    the warm-up steps, and the library's registered bytes."""
+    ch = Chain(mmq, torch, synth, args.layers, packed_q4k=True)
+    try:
+        for _ in range(args.warmup):
+            ch.step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            ch.step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        wb = mmq.mmq_stats(ch.ctx)["weight_bytes"]
+    finally:
+        ch.close()
+    log(f"chain on packed q4_K tiles: {ms:.2f} ms/step, {ops / (ms * 1e-3) / 1e12:.1f} TOPS, "
+        f"{wb / 1e9:.2f} GB of registered weights")
+    return {"ms_per_step": round(ms, 3), "tops": round(ops / (ms * 1e-3) / 1e12, 2),
+            "registered_weight_bytes": wb}
 
 
 def small_n_sweep(mmq, torch, synth):
@@ -1013,6 +1041,8 @@ def main():
     power = power_sweep(mmq, torch, synth) if args.power else None
     crossover = decode_crossover_sweep(mmq, torch, synth) if args.decode_crossover else None
     f16ref = f16_reference(torch) if args.f16_reference else None
+    if packed is not None:
+        packed["chain"] = packed_chain(mmq, torch, synth, args, ops)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     rec = {
