@@ -3,7 +3,8 @@
 Layers 0 and 27 of the 28-layer 7B sweep (3314 tokens, hidden 3584, ffn 18944,
 seeded by their layer index exactly as in the benchmark) are built and run by
 bench.py's own Chain class: the same eleven calls per layer, the same shapes,
-hence the same launch plans the benchmark times.  After each layer, checked
+hence the same launch plans the benchmark times.  Layer 27 runs a second time
+with its q4_K weights on packed 4-bit tiles, as the benchmark's packed chain.  After each layer, checked
 against the oracle:
   * the attention output's standalone plane: bit-exact (q, D, S);
   * the two RMSNorm planes and the SwiGLU plane (whose inputs are the GPU's own
@@ -51,9 +52,10 @@ def _d_close(gpu, ref, what):
     assert rel.max(initial=0.0) < 1e-5, f"{what}: D off by {rel.max()}"
 
 
-@pytest.mark.parametrize("layer", [0, 27])
-def test_timed_chain_layer_against_oracle(layer):
-    ch = bench.Chain(mmq, torch, synth, bench.LAYERS, layer_ids=[layer])
+@pytest.mark.parametrize("layer,packed", [(0, False), (27, False), (27, True)],
+                         ids=["layer0", "layer27", "layer27_packed_q4k_tiles"])
+def test_timed_chain_layer_against_oracle(layer, packed):
+    ch = bench.Chain(mmq, torch, synth, bench.LAYERS, layer_ids=[layer], packed_q4k=packed)
     try:
         L = ch.layers[0]
         before = mmq.mmq_stats(ch.ctx)
